@@ -1,0 +1,168 @@
+"""Benchmark: one Stable LatentMoE layer forward per step on one MI355X.
+
+A step is one pass of the whole layer (down-projection + router, top-k, align,
+routed MXFP4 gate/up + GLU, routed down, combine + RMSNorm, shared experts,
+up-projection) over one batch of seeded synthetic tokens with every input
+already resident in HBM. Default workload: one K3 layer at decode batch 16
+(hidden 7168, latent 3584, 896 MXFP4 experts with top-16, RMSNorm, 2 shared
+experts merged to a 6144-wide MXFP4 GLU). Four seeded token batches rotate so
+that consecutive steps touch different experts.
+
+Prints one JSON line (rank 0). Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "latent-MoE layer tokens/s; % peak HBM GB/s (decode), % MXFP4 MFMA (prefill)"
+HBM_PEAK_GBS = 8000.0
+EXPERT_GATE_UP_BYTES = None  # set from the config below
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(c, dl, x_bits, n_tokens: int):
+    """The oracle, as it stands, on the first n_tokens of one batch (host cores)."""
+    from oracle import layer as ol
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    dense = dl.host_dense
+    # pre-generate the experts the sample touches so that generation is not timed
+    r = ol.route((x_bits[:n_tokens].astype(np.uint32) << 16).view(np.float32).astype(np.float64),
+                 dense["router"], dense["select_bias"], c.topk, c.routed_scaling_factor)
+    from workload import gen
+    need = sorted(set(r["ids"].reshape(-1).tolist()))
+    cache = {e: gen.make_expert(c, 0, e) for e in need}
+    shared = gen.make_shared(c, 0)
+    t0 = time.perf_counter()
+    ol.forward(x_bits[:n_tokens], dense["down"], dense["norm"], dense["router"], dense["select_bias"],
+               lambda e: cache[e], dense["up"], shared, c.topk, inter=c.inter, shared_inter=c.shared_inter,
+               rms_eps=c.rms_eps, rsf=c.routed_scaling_factor, align_block=16)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of one batch ({len(need)} experts), float64 numpy oracle, "
+                      f"{dt:.1f} s wall; expert decode single-threaded, matmuls on {blas_threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="decode16", help="named workload (decode16, decode256, prefill8192)")
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; runs on more than one GPU are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from latent_moe_expert_amd import layer as L
+    from tests.gpu_harness import DeviceLayer, to_dev_bf16
+    from workload import gen
+
+    c = gen.named_config(args.config)
+    t0 = time.time()
+    dl = DeviceLayer(c)
+    xs_bits = gen.make_x(c, 0, T=4 * c.T)
+    xs = [to_dev_bf16(xs_bits[i * c.T:(i + 1) * c.T]) for i in range(4)]
+    log(f"inputs resident in HBM in {time.time() - t0:.1f} s")
+
+    dims = dl.dims(c.T)
+    ws = torch.empty(L.moe_latent_workspace_size(dims, c.topk), dtype=torch.uint8, device="cuda")
+    y = torch.empty((c.T, c.hidden), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L.moe_latent_forward(dims, xs[i % 4], dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales, dl.up,
+                             dl.sh_packed, dl.sh_scales, c.topk, y, ws, stream=stream)
+
+    # distinct experts touched by each batch (routing taps, untimed)
+    D = []
+    for i in range(4):
+        ids = torch.empty((c.T, c.topk), dtype=torch.int32, device="cuda")
+        L.moe_latent_forward_ex(dims, xs[i], dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales, dl.up,
+                                dl.sh_packed, dl.sh_scales, c.topk, y, ws, taps={"topk_ids": ids})
+        torch.cuda.synchronize()
+        D.append(len(np.unique(ids.cpu().numpy())))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    L.moe_latent_timing_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    L.moe_latent_timing_enable(False)
+    stages, nf = L.moe_latent_timing_read()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = c.T * args.steps / elapsed
+    stage_ms = {k: v / max(nf, 1) for k, v in stages.items()}
+
+    gu_per_expert = 2 * (c.inter * c.latent // 2 + c.inter * c.latent // 32)     # w1 + w3, packed + scales
+    dn_per_expert = c.latent * c.inter // 2 + c.latent * c.inter // 32
+    D_steps = [D[i % 4] for i in range(args.steps)]
+    D_mean = float(np.mean(D_steps))
+    pairs = c.T * c.topk
+    # algorithmic bytes of one gate/up launch: each touched expert's w1|w3 once, the gathered
+    # latent rows once per pair, and h written once per pair
+    gu_bytes = D_mean * gu_per_expert + pairs * c.latent * 2 + pairs * c.inter * 2
+    gu_ms = stage_ms["expert_gate_up"]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    sh_bytes = gen.shared_record_bytes(c) + gen.shared_scale_bytes(c) if c.shared_inter else 0
+    exp_ms = stage_ms["expert_gate_up"] + stage_ms["expert_down"] + stage_ms["shared_gate_up"] + stage_ms["shared_down"]
+    exp_bytes = D_mean * (gu_per_expert + dn_per_expert) + sh_bytes
+    record = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{c.name}: one K3 latent-MoE layer, T={c.T} tokens, hidden {c.hidden}, latent "
+                               f"{c.latent}, {c.n_experts} MXFP4 experts top-{c.topk}, intermediate {c.inter}, "
+                               f"RMSNorm={c.norm}, shared GLU {c.shared_inter}; weights MXFP4 (E2M1 + E8M0/32), "
+                               f"activations bf16, fp32 accumulation",
+                   "global_batch": c.T, "parallelism": "none (1 GPU)",
+                   "distinct_experts_per_step": D_mean},
+        "roofline": {"bound": "hbm", "kernel": "expert_gate_up (routed MXFP4 gate/up + GLU)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_bytes), "avg_launch_ms": round(gu_ms, 5)},
+        "expert_kernels_hbm_frac": round(exp_bytes / (exp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

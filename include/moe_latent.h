@@ -1,0 +1,186 @@
+/*
+ * moe_latent.h -- C ABI of the MI355X (gfx950) Stable LatentMoE layer library.
+ *
+ * The layer (WASTE "Kimi K3, as released", "What is new since Kimi-Linear",
+ * item 1, and the "Port status" row "latent MoE"; K3 report review, "Stable
+ * LatentMoE"): the hidden state x [T, H] is projected down to a latent z [T, L]
+ * (routed_expert_down_proj); a sigmoid router picks top-k of E experts per
+ * token; each selected expert is a GLU MLP on the latent whose weights are
+ * MXFP4; the expert outputs are combined with their router weights, optionally
+ * RMS-normalised (routed_expert_norm), projected back up to H
+ * (routed_expert_up_proj) and summed with the full-width shared experts.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers (HIP, one GPU) unless marked "host".
+ *   - bf16 tensors are raw 16-bit bit patterns; all matrices are row-major.
+ *   - MXFP4 matrix [N, K]: packed U8 [N, K/2], two E2M1 nibbles per byte, the
+ *     LOW nibble holds the even element; scales U8 [N, K/32], one E8M0
+ *     exponent (value 2^(e-127)) per 32 consecutive weights of a row
+ *     (WASTE page, shard-header listing and "Gate 3 repeated on real K3
+ *     experts").
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise the host. All argument checks run before
+ *     anything is enqueued: on any error return nothing has been enqueued.
+ *   - The caller owns every buffer. The library allocates no device memory in
+ *     these calls and keeps no per-call state; results are bitwise identical
+ *     from run to run for identical inputs.
+ *   - Return value: 0 on success or a negative MOE_E* code.
+ */
+#ifndef MOE_LATENT_H
+#define MOE_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_LATENT_ABI_VERSION 1
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null pointer, negative or inconsistent size */
+#define MOE_EUNSUPPORTED (-2) /* sizes outside what the kernels handle (see moe_latent_dims) */
+#define MOE_EALIAS (-3)       /* an output overlaps an input or the workspace */
+#define MOE_EWORKSPACE (-4)   /* workspace too small or misaligned */
+#define MOE_EHIP (-5)         /* a HIP launch failed; moe_latent_last_hip_error() has the code */
+#define MOE_EABI (-6)         /* struct_size does not match this library */
+
+/* Layer sizes. Limits checked by every call (else MOE_EUNSUPPORTED):
+ * hidden, latent, inter, shared_inter multiples of 128; 1 <= n_experts <= 4096;
+ * latent <= 8192; align_block 0 (library choice, 16) or a multiple of 16. */
+typedef struct moe_latent_dims {
+  uint32_t struct_size;        /* = sizeof(moe_latent_dims) */
+  int32_t T;                   /* tokens (0 is allowed: nothing is enqueued, pointers are not read) */
+  int32_t hidden;              /* H, 7168 for K3 */
+  int32_t latent;              /* L, 3584 */
+  int32_t n_experts;           /* E, 896 */
+  int32_t inter;               /* I, expert intermediate width, 3072 */
+  int32_t shared_inter;        /* merged shared GLU width (6144), 0 = no shared experts */
+  int32_t align_block;         /* B of the expert-sorted layout */
+  float rms_eps;               /* RMSNorm epsilon (1e-6) */
+  float routed_scaling_factor; /* 1.0 for K3 */
+} moe_latent_dims;
+
+/* Router (WASTE page, "Shape" router row and "Against the technical report"). */
+typedef struct moe_router {
+  const float* weight;      /* fp32 [E, H] */
+  const float* select_bias; /* fp32 [E] or NULL: added to the sigmoid scores for selection only */
+} moe_router;
+
+/* Merged shared experts, one GLU H -> Is -> H (K3 report review, parameter
+ * count, second step; MXFP4 as in SlimServe quants.md's K3 tensor table). */
+typedef struct moe_shared {
+  const uint8_t* packed; /* [gate Is x H/2 | up Is x H/2 | down H x Is/2] */
+  const uint8_t* scales; /* [gate Is x H/32 | up Is x H/32 | down H x Is/32] */
+} moe_shared;
+
+/* Optional copies of intermediates (each pointer may be NULL). */
+typedef struct moe_latent_taps {
+  uint32_t struct_size;   /* = sizeof(moe_latent_taps) */
+  uint16_t* z;            /* bf16 [T, L]  down-projection */
+  float* logits;          /* fp32 [T, E]  router logits */
+  int32_t* topk_ids;      /* [T, k]       selected experts, ascending id per token */
+  float* topk_w;          /* fp32 [T, k]  routing weights */
+  int32_t* counts;        /* [E]          pairs per expert */
+  int32_t* sorted_ids;    /* [capacity]   expert-sorted flat slot indices (see moe_align_block_size) */
+  int32_t* expert_ids;    /* [capacity/B] */
+  int32_t* num_post;      /* [1] */
+  int32_t* inv_pos;       /* [T*k]        position of slot t*k+j in sorted_ids */
+  float* c;               /* fp32 [T, L]  weighted aggregate before the norm */
+  uint16_t* c_norm;       /* bf16 [T, L]  input of the up-projection */
+  float* y_routed;        /* fp32 [T, H]  up-projection output */
+  float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none) */
+} moe_latent_taps;
+
+int moe_latent_abi_version(void);
+const char* moe_latent_strerror(int code);
+/* hipError_t of the last MOE_EHIP returned on this host thread (0 if none). */
+int moe_latent_last_hip_error(void);
+
+/* Host-only. Workspace bytes needed by moe_latent_forward for these sizes. */
+int moe_latent_workspace_size(const moe_latent_dims* d, int topk, size_t* bytes);
+
+/* Host-only. Entries of the expert-sorted layout (capacity) and the block B
+ * the library uses for these sizes:
+ * capacity = B * floor((T*k + min(E, T*k)*(B-1)) / B). */
+int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacity, int32_t* block);
+
+/*
+ * One layer forward: y = up(norm(sum_j w_tj * expert_{e_tj}(down(x_t)))) + shared(x_t).
+ *
+ *   x               bf16 [T, H]
+ *   down            bf16 [L, H]   routed_expert_down_proj
+ *   norm            bf16 [L] or NULL (no RMSNorm)
+ *   router          fp32 weight [E, H], optional fp32 select_bias [E]
+ *   experts_packed  U8 [E][w1 I x L/2 | w3 I x L/2 | w2 L x I/2]; w1 = gate, w3 = up, w2 = down
+ *   experts_scales  U8 [E][w1 I x L/32 | w3 I x L/32 | w2 L x I/32]
+ *   up              bf16 [H, L]   routed_expert_up_proj
+ *   shared          merged shared GLU or NULL
+ *   topk            experts per token, 1 <= topk <= min(E, 64)
+ *   y               bf16 [T, H] output; must not overlap x or the workspace
+ *   workspace       >= moe_latent_workspace_size bytes, 256-byte aligned
+ *
+ * Routing: s = sigmoid(x . W_r^T), key = s + select_bias; the topk largest keys
+ * win, ties to the lower expert id; weights w = s / sum(s_selected) * rsf. The
+ * expert activation is SiLU(gate) * up. Near-ties of the key at the k-th place
+ * can route differently from a float64 evaluation (fp32 here).
+ */
+int moe_latent_forward(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                       const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,
+                       const void* up, const moe_shared* shared, int topk, void* y, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/* As moe_latent_forward, also copying the intermediates requested in `taps`
+ * (device pointers, sizes as in moe_latent_taps; taps may be NULL). */
+int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                          const moe_router* router, const uint8_t* experts_packed,
+                          const uint8_t* experts_scales, const void* up, const moe_shared* shared, int topk,
+                          void* y, void* workspace, size_t ws_bytes, void* stream, const moe_latent_taps* taps);
+
+/*
+ * Routing only: logits = x . W_r^T (fp32), then the selection of
+ * moe_latent_forward. Writes topk_ids [T, topk] (ascending ids per token) and
+ * topk_w [T, topk]; logits [T, E] fp32 is required scratch/output.
+ */
+int moe_route(const moe_latent_dims* d, const void* x, const moe_router* router, int topk, int32_t* topk_ids,
+              float* topk_w, float* logits, void* stream);
+
+/* Host-only. Device scratch bytes moe_align_block_size needs. */
+int moe_align_workspace_size(int T, int topk, int n_experts, size_t* bytes);
+
+/*
+ * moe_align_block_size (SlimServe quants.md, note on the alignment fix): the
+ * expert-sorted layout of the T*topk (token, slot) pairs.
+ *   topk_ids   [T, topk], ids in [0, E), each token listing an expert at most
+ *              once (ids outside the range are dropped and get inv_pos -1)
+ *   block      B >= 1: every expert segment is padded to a multiple of B; a
+ *              consumer with tile height h | B expands expert_ids B/h times
+ *   sorted_ids [capacity]: segments in ascending expert id, each the flat
+ *              indices t*topk+j in ascending order then the sentinel T*topk;
+ *              the tail past num_post also holds the sentinel
+ *   expert_ids [capacity/B]: expert of each block, -1 past num_post
+ *   num_post   [1]: padded entry count; inv_pos [T*topk]; counts [E]
+ *   scratch    >= moe_align_workspace_size bytes
+ * capacity as in moe_latent_align_layout. Integer-only and bit-exact.
+ */
+int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts, int block, int32_t* sorted_ids,
+                         int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, int32_t* counts, void* scratch,
+                         size_t scratch_bytes, void* stream);
+
+/*
+ * Stage timing for measurement. While enabled, moe_latent_forward records HIP
+ * events around each stage on its stream (at most 4096 forwards are kept).
+ * moe_latent_timing_read synchronises on the recorded events and returns, per
+ * stage, the summed milliseconds and the number of forwards recorded; it then
+ * clears the record. Stage names: moe_latent_stage_name(i), i < stage count.
+ */
+int moe_latent_timing_enable(int on);
+int moe_latent_stage_count(void);
+const char* moe_latent_stage_name(int i);
+int moe_latent_timing_read(float* ms_per_stage /* host [stage count] */, int* n_forwards /* host */);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LATENT_H */

@@ -1,0 +1,160 @@
+// moe_align_block_size: the padded, expert-sorted layout of (token, slot) pairs
+// that the grouped expert contractions read (SlimServe quants.md, note on the
+// alignment fix: one layout whose rows are aligned to the LCM of the consumers'
+// tile widths, with an expert id per tile; expert ids above 255 must work).
+//
+// Layout produced (bit-exact, integer only):
+//   sorted_ids: for experts in ascending id order, the flat slot indices t*k+j
+//               that chose the expert, ascending, then padding with the
+//               sentinel T*k up to a multiple of B; empty experts get nothing;
+//               the tail up to capacity holds the sentinel.
+//   expert_ids: expert of each block of B entries, -1 past the end.
+//   num_post:   padded entry count; inv_pos[t*k+j] = position of that slot.
+//
+// Three kernels, no float and no order-dependent atomics:
+//   count   one block per chunk of 64 tokens builds, in LDS, a 64-bit mask per
+//           expert of the chunk tokens that chose it; writes popcounts.
+//   scan    one block: per-expert prefix over chunks, padded sizes, the
+//           exclusive scan over experts, expert_ids and all padding.
+//   scatter one block per chunk rebuilds the masks; a slot's rank inside its
+//           expert is (chunk prefix) + popcount(mask & lower tokens).
+// Each token lists an expert at most once (the router's ids are distinct), so
+// token order inside an expert equals flat-index order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 64;  // tokens per chunk (one bit each in a 64-bit mask)
+
+__device__ void build_masks(const int32_t* __restrict__ ids, int T, int k, int E, int chunk,
+                            unsigned long long* mask) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+  __syncthreads();
+  const int t0 = chunk * kChunk;
+  const int nt = min(kChunk, T - t0);
+  const int np = nt * k;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const int e = ids[(size_t)t0 * k + i];
+    if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << (i / k));
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                          int32_t* __restrict__ chunk_cnt) {
+  extern __shared__ unsigned long long mask[];
+  build_masks(ids, T, k, E, blockIdx.x, mask);
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    chunk_cnt[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
+}
+
+__global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, int B, int pairs, int cap,
+                                                          int32_t* __restrict__ chunk_cnt /* in: counts, out: prefix */,
+                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offs,
+                                                          int32_t* __restrict__ sorted_ids,
+                                                          int32_t* __restrict__ expert_ids,
+                                                          int32_t* __restrict__ num_post) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  // per-expert prefix over chunks
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_cnt[(size_t)c * E + e];
+      chunk_cnt[(size_t)c * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of padded sizes over experts: thread tid owns a contiguous run
+  const int per = (E + 1023) / 1024;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) local += (counts[e] + B - 1) / B * B;
+  part[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - local;
+  for (int e = e0; e < e1; ++e) {
+    offs[e] = run;
+    run += (counts[e] + B - 1) / B * B;
+  }
+  const int total = part[1023];
+  if (tid == 0) *num_post = total;
+  __syncthreads();
+  // expert ids per block and padding entries of each segment
+  for (int e = tid; e < E; e += 1024) {
+    const int c = counts[e];
+    const int p = (c + B - 1) / B * B;
+    const int o = offs[e];
+    for (int b = 0; b < p / B; ++b) expert_ids[o / B + b] = e;
+    for (int i = c; i < p; ++i) sorted_ids[o + i] = pairs;
+  }
+  for (int i = total + tid; i < cap; i += 1024) sorted_ids[i] = pairs;
+  for (int b = total / B + tid; b < cap / B; b += 1024) expert_ids[b] = -1;
+}
+
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                            const int32_t* __restrict__ chunk_pre,
+                                                            const int32_t* __restrict__ offs,
+                                                            int32_t* __restrict__ sorted_ids,
+                                                            int32_t* __restrict__ inv_pos) {
+  extern __shared__ unsigned long long mask[];
+  build_masks(ids, T, k, E, blockIdx.x, mask);
+  const int t0 = blockIdx.x * kChunk;
+  const int nt = min(kChunk, T - t0);
+  const int np = nt * k;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const int flat = t0 * k + i;
+    const int e = ids[flat];
+    if (e < 0 || e >= E) {
+      inv_pos[flat] = -1;
+      continue;
+    }
+    const int tl = i / k;
+    const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
+    const int pos = offs[e] + chunk_pre[(size_t)blockIdx.x * E + e] + __popcll(below);
+    sorted_ids[pos] = flat;
+    inv_pos[flat] = pos;
+  }
+}
+
+}  // namespace
+
+int align_capacity(int T, int k, int E, int B) {
+  const long long pairs = (long long)T * k;
+  const long long d = pairs < E ? pairs : E;
+  return (int)(B * ((pairs + d * (B - 1)) / B));
+}
+
+size_t align_scratch_bytes(int T, int E) {
+  const size_t nchunks = (size_t)(T + kChunk - 1) / kChunk;
+  return (nchunks * E + E) * sizeof(int32_t);  // chunk prefixes + expert offsets
+}
+
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t* counts, int32_t* sorted_ids,
+                        int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, void* scratch, hipStream_t s) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int cap = align_capacity(T, k, E, B);
+  int32_t* chunk = (int32_t*)scratch;
+  int32_t* offs = chunk + (size_t)nchunks * E;
+  const size_t lds = (size_t)E * sizeof(unsigned long long);
+  if (nchunks > 0) hipLaunchKernelGGL(align_count_kernel, dim3(nchunks), dim3(256), lds, s, ids, T, k, E, chunk);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, B, T * k, cap, chunk, counts, offs,
+                     sorted_ids, expert_ids, num_post);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(256), lds, s, ids, T, k, E, chunk, offs,
+                       sorted_ids, inv_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

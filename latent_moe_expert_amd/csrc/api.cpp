@@ -1,0 +1,443 @@
+// C ABI of the latent-MoE layer library: validation, workspace plan, launches.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/moe_latent.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return MOE_EHIP;
+}
+#define MOE_HIP(call)                         \
+  do {                                        \
+    hipError_t e_ = (call);                   \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopk = 64;
+constexpr int kMaxLatent = 8192;
+
+// ------------------------------------------------------------------ stage timing
+enum Stage { kProjRouter, kTopk, kAlign, kExpGateUp, kExpDown, kCombine, kShGateUp, kShDown, kUpProj, kNumStages };
+const char* kStageNames[kNumStages] = {"proj_router", "topk", "align", "expert_gate_up", "expert_down",
+                                       "combine_norm", "shared_gate_up", "shared_down", "up_proj"};
+constexpr int kMaxTimed = 256;
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // kMaxTimed * (kNumStages + 1)
+  int n = 0;                   // forwards recorded
+  hipEvent_t* slot() {         // events of the next forward, or null when full
+    if (n >= kMaxTimed) return nullptr;
+    const size_t need = (size_t)(n + 1) * (kNumStages + 1);
+    while (ev.size() < need) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      ev.push_back(e);
+    }
+    return &ev[(size_t)n * (kNumStages + 1)];
+  }
+} g_timing;
+
+// ------------------------------------------------------------------ plan
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Plan {
+  int T, H, L, E, I, Is, k, B, cap, pairs;
+  size_t z, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys, total;
+};
+
+int check_dims(const moe_latent_dims* d, int topk) {
+  if (!d) return MOE_EINVAL;
+  if (d->struct_size != sizeof(moe_latent_dims)) return MOE_EABI;
+  if (d->T < 0 || d->hidden <= 0 || d->latent <= 0 || d->n_experts <= 0 || d->inter <= 0 || d->shared_inter < 0 ||
+      d->align_block < 0 || topk < 1 || topk > d->n_experts)
+    return MOE_EINVAL;
+  if (!(d->rms_eps >= 0.f) || !(d->routed_scaling_factor == d->routed_scaling_factor)) return MOE_EINVAL;
+  if (d->hidden % 128 || d->latent % 128 || d->inter % 128 || d->shared_inter % 128) return MOE_EUNSUPPORTED;
+  if (d->n_experts > kMaxExperts || topk > kMaxTopk || d->latent > kMaxLatent) return MOE_EUNSUPPORTED;
+  if (d->align_block % 16) return MOE_EUNSUPPORTED;
+  if ((long long)d->T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+Plan make_plan(const moe_latent_dims* d, int topk) {
+  Plan p;
+  p.T = d->T, p.H = d->hidden, p.L = d->latent, p.E = d->n_experts, p.I = d->inter, p.Is = d->shared_inter;
+  p.k = topk;
+  p.B = d->align_block ? d->align_block : 16;
+  p.pairs = p.T * p.k;
+  p.cap = moe::align_capacity(p.T, p.k, p.E, p.B);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  p.z = take((size_t)p.T * p.L * 2);
+  p.logits = take((size_t)p.T * p.E * 4);
+  p.ids = take((size_t)p.pairs * 4);
+  p.w = take((size_t)p.pairs * 4);
+  p.counts = take((size_t)p.E * 4);
+  p.sorted = take((size_t)p.cap * 4);
+  p.expert_ids = take((size_t)(p.cap / p.B) * 4);
+  p.num_post = take(4);
+  p.inv_pos = take((size_t)p.pairs * 4);
+  p.align_scratch = take(moe::align_scratch_bytes(p.T, p.E));
+  p.h = take((size_t)p.cap * p.I * 2);
+  p.O = take((size_t)p.cap * p.L * 4);
+  p.cn = take((size_t)p.T * p.L * 2);
+  p.hs = take((size_t)p.T * p.Is * 2);
+  p.ys = take((size_t)p.T * p.H * 4);
+  p.total = o;
+  return p;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const char *x = (const char*)a, *y = (const char*)b;
+  return x < y + nb && y < x + na;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+int copy_tap(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (!dst || !bytes) return MOE_OK;
+  MOE_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_latent_abi_version(void) { return MOE_LATENT_ABI_VERSION; }
+
+const char* moe_latent_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer or bad size)";
+    case MOE_EUNSUPPORTED: return "sizes not supported by the kernels";
+    case MOE_EALIAS: return "an output overlaps an input or the workspace";
+    case MOE_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MOE_EHIP: return "HIP launch failed (see moe_latent_last_hip_error)";
+    case MOE_EABI: return "struct_size mismatch (header and library differ)";
+    default: return "unknown error";
+  }
+}
+
+int moe_latent_last_hip_error(void) { return g_last_hip; }
+
+int moe_latent_workspace_size(const moe_latent_dims* d, int topk, size_t* bytes) {
+  const int rc = check_dims(d, topk);
+  if (rc) return rc;
+  if (!bytes) return MOE_EINVAL;
+  *bytes = make_plan(d, topk).total;
+  return MOE_OK;
+}
+
+int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacity, int32_t* block) {
+  const int rc = check_dims(d, topk);
+  if (rc) return rc;
+  if (!capacity || !block) return MOE_EINVAL;
+  const Plan p = make_plan(d, topk);
+  *capacity = p.cap;
+  *block = p.B;
+  return MOE_OK;
+}
+
+int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                          const moe_router* router, const uint8_t* experts_packed,
+                          const uint8_t* experts_scales, const void* up, const moe_shared* shared, int topk,
+                          void* y, void* workspace, size_t ws_bytes, void* stream, const moe_latent_taps* taps) {
+  int rc = check_dims(d, topk);
+  if (rc) return rc;
+  if (taps && taps->struct_size != sizeof(moe_latent_taps)) return MOE_EABI;
+  if (d->T == 0) return MOE_OK;  // nothing to compute; empty tensors may have null pointers
+  if (!x || !down || !router || !router->weight || !experts_packed || !experts_scales || !up || !y)
+    return MOE_EINVAL;
+  if ((d->shared_inter > 0) != (shared != nullptr)) return MOE_EINVAL;
+  if (shared && (!shared->packed || !shared->scales)) return MOE_EINVAL;
+  const Plan p = make_plan(d, topk);
+  if (!workspace) return MOE_EWORKSPACE;
+  if (ws_bytes < p.total || ((uintptr_t)workspace & 255)) return MOE_EWORKSPACE;
+  const size_t xb = (size_t)p.T * p.H * 2, yb = (size_t)p.T * p.H * 2;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, workspace, p.total) || overlap(workspace, p.total, x, xb))
+    return MOE_EALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* z = at<uint16_t>(ws, p.z);
+  float* logits = at<float>(ws, p.logits);
+  int32_t* ids = at<int32_t>(ws, p.ids);
+  float* w = at<float>(ws, p.w);
+  int32_t* counts = at<int32_t>(ws, p.counts);
+  int32_t* sorted = at<int32_t>(ws, p.sorted);
+  int32_t* expert_ids = at<int32_t>(ws, p.expert_ids);
+  int32_t* num_post = at<int32_t>(ws, p.num_post);
+  int32_t* inv_pos = at<int32_t>(ws, p.inv_pos);
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* O = at<float>(ws, p.O);
+  uint16_t* cn = at<uint16_t>(ws, p.cn);
+  uint16_t* hs = at<uint16_t>(ws, p.hs);
+  float* ys = at<float>(ws, p.ys);
+
+  hipEvent_t* ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.on) {
+      ev = g_timing.slot();
+      if (ev) ++g_timing.n;
+    }
+  }
+  auto mark = [&](int i) -> int {
+    if (ev) MOE_HIP(hipEventRecord(ev[i], s));
+    return MOE_OK;
+  };
+#define STAGE_MARK(i)          \
+  do {                         \
+    int r_ = mark(i);          \
+    if (r_) return r_;         \
+  } while (0)
+
+  STAGE_MARK(0);
+  // a1: down-projection and router logits, one launch
+  {
+    moe::DenseArgs a{};
+    a.A = (const uint16_t*)x;
+    a.lda = p.H;
+    a.M = p.T;
+    a.K = p.H;
+    a.nseg = 2;
+    a.seg[0] = {down, p.L, 0, moe::kStoreBf16, z, p.L, nullptr, 0, nullptr, 0};
+    a.seg[1] = {router->weight, p.E, 1, moe::kStoreF32, logits, p.E, nullptr, 0, nullptr, 0};
+    MOE_HIP(moe::launch_dense(a, s));
+  }
+  STAGE_MARK(1);
+  // a2: sigmoid, bias, top-k, weights
+  MOE_HIP(moe::launch_router_topk(logits, p.E, router->select_bias, p.T, p.E, p.k, d->routed_scaling_factor, ids, w,
+                                  s));
+  STAGE_MARK(2);
+  // a3: moe_align_block_size
+  MOE_HIP(moe::launch_align(ids, p.T, p.k, p.E, p.B, counts, sorted, expert_ids, num_post, inv_pos,
+                            at<void>(ws, p.align_scratch), s));
+  STAGE_MARK(3);
+  // a4 + a5: gate/up contraction with the GLU epilogue
+  const size_t gu_bytes = (size_t)p.I * p.L / 2, gu_scales = (size_t)p.I * p.L / 32;
+  {
+    moe::MxArgs g{};
+    g.A = z;
+    g.lda = p.L;
+    g.routed = 1;
+    g.a_by_pos = 0;
+    g.sorted_ids = sorted;
+    g.expert_ids = expert_ids;
+    g.tiles_per_block = p.B / 16;
+    g.num_post = num_post;
+    g.pairs = p.pairs;
+    g.topk = p.k;
+    g.max_blocks = p.cap / 16;
+    g.W = experts_packed;
+    g.S = experts_scales;
+    g.W2 = experts_packed + gu_bytes;
+    g.S2 = experts_scales + gu_scales;
+    g.w_stride = 3 * gu_bytes;
+    g.s_stride = 3 * gu_scales;
+    g.N = p.I;
+    g.K = p.L;
+    g.out = h;
+    g.ldo = p.I;
+    MOE_HIP(moe::launch_mx_small(g, s));
+  }
+  STAGE_MARK(4);
+  // a6: down contraction
+  {
+    moe::MxArgs g{};
+    g.A = h;
+    g.lda = p.I;
+    g.routed = 1;
+    g.a_by_pos = 1;
+    g.sorted_ids = sorted;
+    g.expert_ids = expert_ids;
+    g.tiles_per_block = p.B / 16;
+    g.num_post = num_post;
+    g.pairs = p.pairs;
+    g.topk = p.k;
+    g.max_blocks = p.cap / 16;
+    g.W = experts_packed + 2 * gu_bytes;
+    g.S = experts_scales + 2 * gu_scales;
+    g.w_stride = 3 * gu_bytes;
+    g.s_stride = 3 * gu_scales;
+    g.N = p.L;
+    g.K = p.I;
+    g.out = O;
+    g.ldo = p.L;
+    MOE_HIP(moe::launch_mx_small(g, s));
+  }
+  STAGE_MARK(5);
+  // a7 + a8: weighted combine and RMSNorm
+  MOE_HIP(moe::launch_combine_norm(O, p.L, inv_pos, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
+                                   taps ? taps->c : nullptr, cn, s));
+  STAGE_MARK(6);
+  // a10: shared experts on the full hidden state
+  if (shared) {
+    const size_t sgu = (size_t)p.Is * p.H / 2, sgs = (size_t)p.Is * p.H / 32;
+    moe::MxArgs g{};
+    g.A = (const uint16_t*)x;
+    g.lda = p.H;
+    g.routed = 0;
+    g.M = p.T;
+    g.max_blocks = (p.T + 15) / 16;
+    g.W = shared->packed;
+    g.S = shared->scales;
+    g.W2 = shared->packed + sgu;
+    g.S2 = shared->scales + sgs;
+    g.N = p.Is;
+    g.K = p.H;
+    g.out = hs;
+    g.ldo = p.Is;
+    MOE_HIP(moe::launch_mx_small(g, s));
+    STAGE_MARK(7);
+    moe::MxArgs dn{};
+    dn.A = hs;
+    dn.lda = p.Is;
+    dn.routed = 0;
+    dn.M = p.T;
+    dn.max_blocks = (p.T + 15) / 16;
+    dn.W = shared->packed + 2 * sgu;
+    dn.S = shared->scales + 2 * sgs;
+    dn.N = p.H;
+    dn.K = p.Is;
+    dn.out = ys;
+    dn.ldo = p.H;
+    MOE_HIP(moe::launch_mx_small(dn, s));
+  } else {
+    STAGE_MARK(7);
+  }
+  STAGE_MARK(8);
+  // a9: up-projection, plus the shared output, rounded to bf16
+  {
+    moe::DenseArgs a{};
+    a.A = cn;
+    a.lda = p.L;
+    a.M = p.T;
+    a.K = p.L;
+    a.nseg = 1;
+    a.seg[0] = {up, p.H, 0, moe::kAddStoreBf16, y, p.H, shared ? ys : nullptr, p.H,
+                taps ? taps->y_routed : nullptr, p.H};
+    MOE_HIP(moe::launch_dense(a, s));
+  }
+  STAGE_MARK(9);
+
+  if (taps) {
+    int r;
+    if ((r = copy_tap(taps->z, z, (size_t)p.T * p.L * 2, s))) return r;
+    if ((r = copy_tap(taps->logits, logits, (size_t)p.T * p.E * 4, s))) return r;
+    if ((r = copy_tap(taps->topk_ids, ids, (size_t)p.pairs * 4, s))) return r;
+    if ((r = copy_tap(taps->topk_w, w, (size_t)p.pairs * 4, s))) return r;
+    if ((r = copy_tap(taps->counts, counts, (size_t)p.E * 4, s))) return r;
+    if ((r = copy_tap(taps->sorted_ids, sorted, (size_t)p.cap * 4, s))) return r;
+    if ((r = copy_tap(taps->expert_ids, expert_ids, (size_t)(p.cap / p.B) * 4, s))) return r;
+    if ((r = copy_tap(taps->num_post, num_post, 4, s))) return r;
+    if ((r = copy_tap(taps->inv_pos, inv_pos, (size_t)p.pairs * 4, s))) return r;
+    if ((r = copy_tap(taps->c_norm, cn, (size_t)p.T * p.L * 2, s))) return r;
+    if (taps->y_shared) {
+      if (shared) {
+        if ((r = copy_tap(taps->y_shared, ys, (size_t)p.T * p.H * 4, s))) return r;
+      } else {
+        MOE_HIP(moe::launch_fill_f32(taps->y_shared, (size_t)p.T * p.H, 0.f, s));
+      }
+    }
+  }
+  return MOE_OK;
+#undef STAGE_MARK
+}
+
+int moe_latent_forward(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                       const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,
+                       const void* up, const moe_shared* shared, int topk, void* y, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  return moe_latent_forward_ex(d, x, down, norm, router, experts_packed, experts_scales, up, shared, topk, y,
+                               workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_route(const moe_latent_dims* d, const void* x, const moe_router* router, int topk, int32_t* topk_ids,
+              float* topk_w, float* logits, void* stream) {
+  const int rc = check_dims(d, topk);
+  if (rc) return rc;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !router || !router->weight || !topk_ids || !topk_w || !logits) return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  moe::DenseArgs a{};
+  a.A = (const uint16_t*)x;
+  a.lda = d->hidden;
+  a.M = d->T;
+  a.K = d->hidden;
+  a.nseg = 1;
+  a.seg[0] = {router->weight, d->n_experts, 1, moe::kStoreF32, logits, d->n_experts, nullptr, 0, nullptr, 0};
+  MOE_HIP(moe::launch_dense(a, s));
+  MOE_HIP(moe::launch_router_topk(logits, d->n_experts, router->select_bias, d->T, d->n_experts, topk,
+                                  d->routed_scaling_factor, topk_ids, topk_w, s));
+  return MOE_OK;
+}
+
+int moe_align_workspace_size(int T, int topk, int n_experts, size_t* bytes) {
+  if (T < 0 || topk < 1 || n_experts < 1 || !bytes) return MOE_EINVAL;
+  if (n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
+  *bytes = moe::align_scratch_bytes(T, n_experts);
+  return MOE_OK;
+}
+
+int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts, int block, int32_t* sorted_ids,
+                         int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, int32_t* counts, void* scratch,
+                         size_t scratch_bytes, void* stream) {
+  if (T < 0 || topk < 1 || n_experts < 1 || block < 1) return MOE_EINVAL;
+  if (n_experts > kMaxExperts || (long long)T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
+  if (!sorted_ids || !expert_ids || !num_post || !counts || (T > 0 && (!topk_ids || !inv_pos))) return MOE_EINVAL;
+  if (scratch_bytes < moe::align_scratch_bytes(T, n_experts) || (!scratch && scratch_bytes)) return MOE_EWORKSPACE;
+  MOE_HIP(moe::launch_align(topk_ids, T, topk, n_experts, block, counts, sorted_ids, expert_ids, num_post, inv_pos,
+                            scratch, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_latent_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return MOE_OK;
+}
+
+int moe_latent_stage_count(void) { return kNumStages; }
+
+const char* moe_latent_stage_name(int i) { return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr; }
+
+int moe_latent_timing_read(float* ms_per_stage, int* n_forwards) {
+  if (!ms_per_stage || !n_forwards) return MOE_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (int i = 0; i < kNumStages; ++i) ms_per_stage[i] = 0.f;
+  for (int f = 0; f < g_timing.n; ++f) {
+    hipEvent_t* e = &g_timing.ev[(size_t)f * (kNumStages + 1)];
+    MOE_HIP(hipEventSynchronize(e[kNumStages]));
+    for (int i = 0; i < kNumStages; ++i) {
+      float ms = 0.f;
+      MOE_HIP(hipEventElapsedTime(&ms, e[i], e[i + 1]));
+      ms_per_stage[i] += ms;
+    }
+  }
+  *n_forwards = g_timing.n;
+  g_timing.n = 0;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device helpers shared by the latent-MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+#define MOE_WAVE 64
+
+// bf16 is carried as raw uint16 bit patterns outside the MFMA operands.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Eight MXFP4 elements (one 32-bit word, element 2j in the low nibble of byte j)
+// to eight bf16 values times the E8M0 scale. The conversion instruction takes the
+// scale from the exponent field of its fp32 operand, so `scale_as_f32` is the raw
+// E8M0 code shifted into that field (exact for every code, 255 gives NaN).
+// Returns 4 dwords, each two bf16 (lower element in the low half).
+__device__ __forceinline__ void fp4x8_to_bf16x8(uint32_t w, float scale_as_f32, uint32_t out[4]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale_as_f32, 0));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale_as_f32, 1));
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale_as_f32, 2));
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale_as_f32, 3));
+}
+
+__device__ __forceinline__ float e8m0_as_f32_exponent(uint32_t code) { return __uint_as_float(code << 23); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Swappable GLU activation of the experts: SiLU(gate) * up.
+__device__ __forceinline__ float glu_act(float gate, float up) {
+  return gate / (1.0f + __expf(-gate)) * up;
+}
+
+__device__ __forceinline__ float sigmoidf_dev(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// wave-level sum (wave64)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Streaming 16-byte load that bypasses nothing but marks the data as read-once.
+__device__ __forceinline__ u32x4_t load_nt_u32x4(const void* p) {
+  return __builtin_nontemporal_load((const u32x4_t*)p);
+}
+__device__ __forceinline__ u32x4_t load_u32x4(const void* p) { return *(const u32x4_t*)p; }

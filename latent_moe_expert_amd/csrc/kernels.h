@@ -1,0 +1,84 @@
+// Internal launchers of the latent-MoE HIP kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- dense projections
+// out[m][n] = sum_k A[m][k] * W[n][k] for one or two weight segments sharing A.
+enum DenseOut : int {
+  kStoreBf16 = 0,       // out bf16 [M, ldo]
+  kStoreF32 = 1,        // out f32  [M, ldo]
+  kAddStoreBf16 = 2,    // out bf16 = bf16(acc + addend[m][n]) (addend may be null); tap f32 = acc
+};
+
+struct DenseSeg {
+  const void* W;        // [N, K] row-major, bf16 bits or fp32
+  int N;                // rows of W
+  int w_f32;            // 1: W is fp32, split exactly into three bf16 planes
+  int mode;             // DenseOut
+  void* out;
+  int ldo;
+  const float* addend;  // kAddStoreBf16 only
+  int ld_add;
+  float* tap;           // kAddStoreBf16 only, optional
+  int ld_tap;
+};
+
+struct DenseArgs {
+  const uint16_t* A;    // bf16 [M, lda]
+  int lda, M, K;        // K multiple of 128
+  DenseSeg seg[2];
+  int nseg;
+};
+
+hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- router
+hipError_t launch_router_topk(const float* logits, int ld_logits, const float* select_bias, int T, int E,
+                              int k, float rsf, int32_t* ids, float* w, hipStream_t s);
+
+// ---------------------------------------------------------------- align
+size_t align_scratch_bytes(int T, int E);
+int align_capacity(int T, int k, int E, int B);
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t* counts, int32_t* sorted_ids,
+                        int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, void* scratch, hipStream_t s);
+
+// ---------------------------------------------------------------- MXFP4 contractions
+struct MxArgs {
+  // activations: bf16 rows
+  const uint16_t* A;
+  int lda;
+  int routed;                 // 1: row of slot pos = sorted_ids[pos] / topk (gather); 0: row = pos
+  int a_by_pos;               // routed only: 1 = A row is pos itself (h rows in sorted order)
+  const int32_t* sorted_ids;  // routed
+  const int32_t* expert_ids;  // routed: expert of each layout block of B slots
+  int tiles_per_block;        // routed: B / 16 (the kernel's 16-slot tiles per layout block)
+  const int32_t* num_post;    // routed: device scalar, padded slot count
+  int pairs, topk;            // routed
+  int M;                      // dense: number of rows
+  int max_blocks;             // grid.y upper bound
+  // weights (MXFP4): matrix of expert e at W + e*w_stride, [N, K/2] bytes; scales at S + e*s_stride, [N, K/32]
+  const uint8_t* W;
+  const uint8_t* S;
+  const uint8_t* W2;          // GLU: the up matrix (same layout), null for a plain contraction
+  const uint8_t* S2;
+  size_t w_stride, s_stride;
+  int N, K;
+  // output: GLU -> bf16 [rows, ldo] = act(gate) * up; plain -> f32 [rows, ldo]
+  void* out;
+  int ldo;
+};
+
+hipError_t launch_mx_small(const MxArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- combine + norm
+hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
+                               const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
+
+// fill with a constant (a kernel, so that captured graphs hold no memset node)
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
+
+}  // namespace moe

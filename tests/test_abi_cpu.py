@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+every argument check returns its code before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from latent_moe_expert_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_latent.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmoe_latent.so is not built (run python -m latent_moe_expert_amd.build)")
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "moe_latent_forward" in names and "moe_align_block_size" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.moe_latent_abi_version() == 1
+    for code in range(0, -7, -1):
+        assert lib.moe_latent_strerror(code)
+    assert lib.moe_latent_stage_count() == 9
+    assert lib.moe_latent_stage_name(3) == b"expert_gate_up"
+
+
+def _dims(**kw):
+    base = dict(T=16, hidden=7168, latent=3584, n_experts=896, inter=3072, shared_inter=6144, align_block=0,
+                rms_eps=1e-6, routed_scaling_factor=1.0)
+    base.update(kw)
+    d = _lib.MoeLatentDims(ctypes.sizeof(_lib.MoeLatentDims), *[base[f] for f, _ in _lib.MoeLatentDims._fields_[1:]])
+    return d
+
+
+def _ws(lib, d, k=16):
+    n = ctypes.c_size_t(0)
+    rc = lib.moe_latent_workspace_size(ctypes.byref(d), k, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_and_layout(lib):
+    rc, n = _ws(lib, _dims())
+    assert rc == 0 and n > 0
+    cap, blk = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.moe_latent_align_layout(ctypes.byref(_dims()), 16, ctypes.byref(cap), ctypes.byref(blk)) == 0
+    # T*k = 256 pairs, at most 256 distinct experts, B = 16: 16 * floor((256 + 256*15) / 16) = 4096
+    assert (cap.value, blk.value) == (4096, 16)
+
+
+@pytest.mark.parametrize("kw,k,code", [
+    (dict(hidden=100), 16, -2), (dict(latent=3600), 16, -2), (dict(n_experts=5000), 16, -2),
+    (dict(align_block=24), 16, -2), (dict(T=-1), 16, -1), (dict(n_experts=8), 9, -1),
+    (dict(), 0, -1), (dict(), 65, -2), (dict(rms_eps=-1.0), 16, -1),
+])
+def test_dims_validation(lib, kw, k, code):
+    rc, _ = _ws(lib, _dims(**kw), k)
+    assert rc == code
+
+
+def test_struct_size_mismatch(lib):
+    d = _dims()
+    d.struct_size = 12
+    assert _ws(lib, d)[0] == -6
+
+
+def _forward(lib, d, x=0x10000, y=0x90000000, ws=0x200000000, ws_bytes=None, shared=True, k=16, down=0x1000):
+    router = _lib.MoeRouter(0x3000, None)
+    sh = _lib.MoeShared(0x5000, 0x6000) if shared else None
+    if ws_bytes is None:
+        ws_bytes = _ws(lib, d, k)[1]
+    return lib.moe_latent_forward(ctypes.byref(d), x, down, None, ctypes.byref(router), 0x7000, 0x8000, 0x9000,
+                                  ctypes.byref(sh) if sh is not None else None, k, y, ws, ws_bytes, None)
+
+
+def test_forward_argument_errors_before_any_launch(lib):
+    d = _dims()
+    assert _forward(lib, d, x=None) == -1
+    assert _forward(lib, d, down=None) == -1
+    assert _forward(lib, d, shared=False) == -1            # shared_inter > 0 needs shared experts
+    assert _forward(lib, _dims(shared_inter=0), shared=True) == -1
+    assert _forward(lib, d, ws=None) == -4
+    assert _forward(lib, d, ws_bytes=1024) == -4
+    assert _forward(lib, d, ws=0x200000010) == -4           # not 256-byte aligned
+    assert _forward(lib, d, y=0x10000 + 64) == -3           # y overlaps x
+    n = _ws(lib, d)[1]
+    assert _forward(lib, d, y=0x200000000 + n // 2) == -3   # y inside the workspace
+    assert _forward(lib, _dims(T=0)) == 0                  # nothing to do, nothing enqueued
+
+
+def test_align_argument_errors(lib):
+    n = ctypes.c_size_t()
+    assert lib.moe_align_workspace_size(16, 16, 896, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.moe_align_workspace_size(16, 16, 5000, ctypes.byref(n)) == -2
+    P = 0x100000
+    assert lib.moe_align_block_size(P, 16, 16, 896, 0, P, P, P, P, P, P, n.value, None) == -1
+    assert lib.moe_align_block_size(P, 16, 16, 896, 16, None, P, P, P, P, P, n.value, None) == -1
+    assert lib.moe_align_block_size(P, 16, 16, 896, 16, P, P, P, P, P, P, 8, None) == -4
+
+
+def test_timing_read_when_empty(lib):
+    assert lib.moe_latent_timing_enable(0) == 0
+    arr = (ctypes.c_float * 9)()
+    nf = ctypes.c_int(-1)
+    assert lib.moe_latent_timing_read(arr, ctypes.byref(nf)) == 0 and nf.value == 0
