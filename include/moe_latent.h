@@ -47,8 +47,10 @@ extern "C" {
 #define MOE_EABI (-6)         /* struct_size does not match this library */
 
 /* Layer sizes. Limits checked by every call (else MOE_EUNSUPPORTED):
- * hidden, latent, inter, shared_inter multiples of 128; 1 <= n_experts <= 4096;
- * latent <= 8192; align_block 0 (library choice, 16) or a multiple of 16. */
+ * hidden, latent, inter, shared_inter multiples of 256; 1 <= n_experts <= 4096;
+ * latent <= 8192; align_block 0 (library choice, 16) or a multiple of 16; the
+ * expert-sorted intermediate (capacity x inter bf16) and x (T x hidden bf16)
+ * below 2 GiB each. */
 typedef struct moe_latent_dims {
   uint32_t struct_size;        /* = sizeof(moe_latent_dims) */
   int32_t T;                   /* tokens (0 is allowed: nothing is enqueued, pointers are not read) */

@@ -63,10 +63,20 @@ int check_dims(const moe_latent_dims* d, int topk) {
       d->align_block < 0 || topk < 1 || topk > d->n_experts)
     return MOE_EINVAL;
   if (!(d->rms_eps >= 0.f) || !(d->routed_scaling_factor == d->routed_scaling_factor)) return MOE_EINVAL;
-  if (d->hidden % 128 || d->latent % 128 || d->inter % 128 || d->shared_inter % 128) return MOE_EUNSUPPORTED;
+  if (d->hidden % 256 || d->latent % 256 || d->inter % 256 || d->shared_inter % 256) return MOE_EUNSUPPORTED;
   if (d->n_experts > kMaxExperts || topk > kMaxTopk || d->latent > kMaxLatent) return MOE_EUNSUPPORTED;
   if (d->align_block % 16) return MOE_EUNSUPPORTED;
   if ((long long)d->T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
+  // activation tensors the kernels index with 32-bit byte offsets stay below 2 GiB
+  {
+    const long long B = d->align_block ? d->align_block : 16;
+    const long long pairs = (long long)d->T * topk;
+    const long long cap = B * ((pairs + (pairs < d->n_experts ? pairs : d->n_experts) * (B - 1)) / B);
+    const long long lim = 1ll << 31;
+    if (cap * d->inter * 2 >= lim || (long long)d->T * d->hidden * 2 >= lim ||
+        (long long)d->T * d->shared_inter * 2 >= lim)
+      return MOE_EUNSUPPORTED;
+  }
   return MOE_OK;
 }
 

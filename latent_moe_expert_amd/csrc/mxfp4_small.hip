@@ -5,19 +5,28 @@
 // [N, K] is U8 [N, K/2] with two E2M1 nibbles per byte, low nibble first, plus
 // one E8M0 exponent per 32 consecutive weights of a row, U8 [N, K/32].
 //
-// Work unit: one 16-slot block of the expert-sorted layout (or 16 rows of a
-// dense batch) x a band of weight rows. In each k-step of 128, lane (n = l%16,
-// q = l/16) loads 16 bytes = one whole scale group (32 weights) of weight row n,
-// plus its E8M0 code, and converts them with the scaled FP4->bf16 instruction
-// (exact for every code); the matching 32 activations of token n come straight
-// from global memory as bf16. Four bf16 MFMA 16x16x32 consume the group: lane
-// group q supplies K sub-range [32q, 32q+32) of the step for both operands, so
-// the contraction needs no shuffles. One pass streams every weight byte exactly
-// once per 16 tokens; decode is bound by those bytes (the experts' I/O is the
-// per-token cost the pages measure).
+// Work unit: one 16-slot tile of the expert-sorted layout (or 16 rows of a
+// dense batch) x 64 weight rows per wave (GLU: 32 gate rows and the same 32 up
+// rows; plain: 64 rows), 4 waves per block, full K per wave.
 //
-// GLU variant: a wave holds tiles of the gate (w1) and up (w3) rows with the
-// same indices, so the epilogue applies act(gate) * up in registers and writes
+// Memory path. Decode streams each touched expert's bytes once, so the kernel
+// lives on HBM efficiency. Every weight load instruction of a wave covers 8
+// whole rows x 128 contiguous bytes (256 weights = two k-steps of a row): on
+// MI355X that pattern streams as fast as a contiguous copy, while the MFMA's
+// native fragment (16 rows x 64 bytes per instruction) measured about 27%
+// slower. The bytes go through a wave-private LDS tile, XOR-swizzled so that
+// both the 16-byte writes and the MFMA fragment reads are bank-conflict free,
+// and no block barrier is needed. Activations come in through buffer loads:
+// slots without a token get an out-of-range offset, read as zeros with no
+// memory traffic.
+//
+// Math. Lane (n = l%16, q = l/16) of an MFMA fragment holds one whole E8M0
+// group (32 weights of row n); the scaled FP4->bf16 conversion applies the
+// group's scale exactly, and four bf16 MFMA 16x16x32 consume the group against
+// the matching 32 activations (lane group q supplies the same K sub-range in
+// both operands, so no reordering of K is visible in the result).
+//
+// GLU variant: the epilogue applies act(gate) * up in registers and writes
 // bf16 h; the plain variant (w2, or the shared down) writes fp32.
 #include "common.h"
 #include "kernels.h"
@@ -26,12 +35,27 @@ namespace moe {
 
 namespace {
 
-template <bool GLU, int NTW>
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any real tensor: reads 0
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+template <bool GLU>
 __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
-  constexpr int CH = GLU ? 2 * NTW : NTW;  // 16-row weight tiles per wave per k-step
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][64 * 128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, q = lane >> 4;
   const int blk = blockIdx.y;
+  uint8_t* lds = lds_all[wave];
 
   int expert = 0;
   if (a.routed) {
@@ -41,10 +65,51 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
   } else if (blk * 16 >= a.M) {
     return;
   }
-  const int row0 = (blockIdx.x * 4 + wave) * NTW * 16;  // first weight row of this wave
-  if (row0 >= a.N) return;
+  constexpr int kColsPerWave = GLU ? 32 : 64;
+  const int col0 = (blockIdx.x * 4 + wave) * kColsPerWave;
+  if (col0 >= a.N) return;  // wave-uniform; the kernel has no block barrier
 
-  // activation row feeding MFMA row nl
+  const int K = a.K;
+  const uint32_t kb2 = (uint32_t)K / 2, ks32 = (uint32_t)K / 32;
+  const uint32_t mat_bytes = (uint32_t)a.N * kb2, mat_scales = (uint32_t)a.N * ks32;
+  const __amdgpu_buffer_rsrc_t w_lo = make_rsrc(a.W + (size_t)expert * a.w_stride, mat_bytes);
+  const __amdgpu_buffer_rsrc_t s_lo = make_rsrc(a.S + (size_t)expert * a.s_stride, mat_scales);
+  const __amdgpu_buffer_rsrc_t w_hi = GLU ? make_rsrc(a.W2 + (size_t)expert * a.w_stride, mat_bytes) : w_lo;
+  const __amdgpu_buffer_rsrc_t s_hi = GLU ? make_rsrc(a.S2 + (size_t)expert * a.s_stride, mat_scales) : s_lo;
+
+  // wave tile t (16 rows) -> first row in its matrix
+  //   GLU:   t = 0,1 -> gate rows col0 + 16t;  t = 2,3 -> up rows col0 + 16(t-2)
+  //   plain: t -> rows col0 + 16t
+  auto tile_row = [&](int t) -> uint32_t { return (uint32_t)(col0 + (GLU ? (t & 1) : t) * 16); };
+
+  // global load l (0..7) of a double step: slots 8l..8l+7 of the wave's 64; lane = (slot, 16-byte chunk)
+  uint32_t goff[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    const uint32_t row = tile_row(l >> 1) + 8 * (l & 1) + (lane >> 3);
+    goff[l] = row * kb2 + (lane & 7) * 16;
+  }
+  // LDS: slot j, chunk c lives at j*128 + ((c ^ (j & 7)) * 16)
+  uint32_t wlds[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    const int j = 8 * l + (lane >> 3), c = lane & 7;
+    wlds[l] = j * 128 + ((c ^ (j & 7)) * 16);
+  }
+  uint32_t rlds[4][2];  // fragment of tile t, step h: slot 16t + nl, chunk 4h + q
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 16 * t + nl, c = 4 * h + q;
+      rlds[t][h] = j * 128 + ((c ^ (j & 7)) * 16);
+    }
+  // scales of the fragment rows: 8 bytes per row per double step; byte q (step 0) and 4+q (step 1)
+  uint32_t soff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) soff[t] = (tile_row(t) + nl) * ks32;
+
+  // activation row feeding MFMA row nl (slots without a token read zeros)
   int arow = -1;
   {
     const int pos = blk * 16 + nl;
@@ -55,72 +120,63 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
       arow = pos;
     }
   }
-  const uint16_t* aptr = arow >= 0 ? a.A + (size_t)arow * a.lda + q * 32 : nullptr;
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a.A, 0x7fffffffu);
+  const uint32_t aoff = arow >= 0 ? ((uint32_t)arow * (uint32_t)a.lda + q * 32) * 2 : kOob;
+  const uint32_t astep = arow >= 0 ? 512u : 0u;  // bytes of activations per double step
 
-  const int K = a.K;
-  const int nsteps = K >> 7;
-  const size_t kb2 = (size_t)K / 2, ks32 = (size_t)K / 32;
-  const uint8_t* wbase[CH];
-  const uint8_t* sbase[CH];
+  f32x4_t acc[4];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int tile = GLU ? (c % NTW) : c;
-    const uint8_t* Wm = (GLU && c >= NTW) ? a.W2 : a.W;
-    const uint8_t* Sm = (GLU && c >= NTW) ? a.S2 : a.S;
-    const size_t row = (size_t)(row0 + tile * 16 + nl);
-    wbase[c] = Wm + (size_t)expert * a.w_stride + row * kb2 + q * 16;
-    sbase[c] = Sm + (size_t)expert * a.s_stride + row * ks32 + q;
-  }
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  f32x4_t acc[CH];
+  struct Stage {
+    u32x4_t w[8];
+    uint2 sc[4];
+    u32x4_t x[2][4];
+  };
+  auto issue = [&](Stage& st, int d) {
+    const uint32_t kbyte = (uint32_t)d * 128;  // 256 weights of a row per double step
 #pragma unroll
-  for (int c = 0; c < CH; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // software pipeline: loads of step s+1 are issued before the math of step s
-  u32x4_t wcur[CH], wnxt[CH];
-  uint32_t scur[CH], snxt[CH];
-  u32x4_t acur[4], anxt[4];
+    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16((GLU && l >= 4) ? w_hi : w_lo, goff[l] + kbyte);
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    wcur[c] = load_nt_u32x4(wbase[c]);
-    scur[c] = sbase[c][0];
-  }
+    for (int t = 0; t < 4; ++t) st.sc[t] = buf_load8((GLU && t >= 2) ? s_hi : s_lo, soff[t] + (uint32_t)d * 8);
+    const uint32_t ab = aoff + (uint32_t)d * astep;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acur[j] = aptr ? load_u32x4(aptr + 8 * j) : u32x4_t{0u, 0u, 0u, 0u};
-
-  for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        wnxt[c] = load_nt_u32x4(wbase[c] + (size_t)(s + 1) * 64);
-        snxt[c] = sbase[c][(s + 1) * 4];
-      }
+      for (int j = 0; j < 4; ++j) st.x[h][j] = buf_load16(a_rs, ab + (arow >= 0 ? (uint32_t)(h * 256 + j * 16) : 0u));
+  };
+  auto consume = [&](const Stage& st) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        anxt[j] = aptr ? load_u32x4(aptr + (size_t)(s + 1) * 128 + 8 * j) : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int l = 0; l < 8; ++l) *(u32x4_t*)(lds + wlds[l]) = st.w[l];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const float sc = e8m0_as_f32_exponent(scur[c]);
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t bw[4];
-        fp4x8_to_bf16x8(wcur[c][j], sc, bw);
-        const u32x4_t bv = {bw[0], bw[1], bw[2], bw[3]};
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(acur[j]), as_bf16x8(bv), acc[c], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t wf = *(const u32x4_t*)(lds + rlds[t][h]);
+        const uint32_t code = ((h ? st.sc[t].y : st.sc[t].x) >> (8 * q)) & 0xffu;
+        const float sc = e8m0_as_f32_exponent(code);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t bw[4];
+          fp4x8_to_bf16x8(wf[j], sc, bw);
+          const u32x4_t bv = {bw[0], bw[1], bw[2], bw[3]};
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[h][j]), as_bf16x8(bv), acc[t], 0, 0, 0);
+        }
       }
     }
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        wcur[c] = wnxt[c];
-        scur[c] = snxt[c];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acur[j] = anxt[j];
-    }
+  };
+
+  const int nd = K >> 8;  // double steps (K is a multiple of 256)
+  Stage s0, s1;
+  issue(s0, 0);
+  int d = 0;
+  for (; d + 2 <= nd; d += 2) {
+    issue(s1, d + 1);
+    consume(s0);
+    if (d + 2 < nd) issue(s0, d + 2);
+    consume(s1);
   }
+  if (d < nd) consume(s0);
 
   // epilogue: lane holds D[m = 4q + r][n = nl] of each tile
   bool valid[4];
@@ -131,14 +187,15 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
     opos[r] = pos;
     valid[r] = a.routed ? (a.sorted_ids[pos] < a.pairs) : (pos < a.M);
   }
+  constexpr int kOutTiles = GLU ? 2 : 4;
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const int col = row0 + t * 16 + nl;
+  for (int t = 0; t < kOutTiles; ++t) {
+    const int col = col0 + t * 16 + nl;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (!valid[r]) continue;
       if (GLU) {
-        const float h = glu_act(acc[t][r], acc[NTW + t][r]);
+        const float h = glu_act(acc[t][r], acc[t + 2][r]);
         ((uint16_t*)a.out)[(size_t)opos[r] * a.ldo + col] = (uint16_t)f32_to_bf16_bits(h);
       } else {
         ((float*)a.out)[(size_t)opos[r] * a.ldo + col] = acc[t][r];
@@ -147,23 +204,18 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
   }
 }
 
-template <bool GLU, int NTW>
-hipError_t launch_t(const MxArgs& a, hipStream_t s) {
-  const int rows_per_block = 4 * NTW * 16;
-  dim3 grid((a.N + rows_per_block - 1) / rows_per_block, a.max_blocks);
-  hipLaunchKernelGGL((mx_small_kernel<GLU, NTW>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_mx_small(const MxArgs& a, hipStream_t s) {
   if (a.max_blocks <= 0) return hipSuccess;
   const bool glu = a.W2 != nullptr;
-  // narrower bands when few token blocks would leave the chip idle
-  const bool narrow = a.max_blocks * (a.N / (glu ? 128 : 256)) < 512;
-  if (glu) return narrow ? launch_t<true, 1>(a, s) : launch_t<true, 2>(a, s);
-  return narrow ? launch_t<false, 1>(a, s) : launch_t<false, 4>(a, s);
+  const int cols_per_block = 4 * (glu ? 32 : 64);
+  dim3 grid((a.N + cols_per_block - 1) / cols_per_block, a.max_blocks);
+  if (glu)
+    hipLaunchKernelGGL(mx_small_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(mx_small_kernel<false>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

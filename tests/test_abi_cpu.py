@@ -65,7 +65,8 @@ def test_workspace_size_and_layout(lib):
 
 
 @pytest.mark.parametrize("kw,k,code", [
-    (dict(hidden=100), 16, -2), (dict(latent=3600), 16, -2), (dict(n_experts=5000), 16, -2),
+    (dict(hidden=100), 16, -2), (dict(latent=3600), 16, -2), (dict(inter=3200), 16, -2),
+    (dict(n_experts=5000), 16, -2), (dict(T=200000), 16, -2),
     (dict(align_block=24), 16, -2), (dict(T=-1), 16, -1), (dict(n_experts=8), 9, -1),
     (dict(), 0, -1), (dict(), 65, -2), (dict(rms_eps=-1.0), 16, -1),
 ])

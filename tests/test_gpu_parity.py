@@ -42,12 +42,12 @@ def _run_small(c, align_block=0, dense=None, experts=None):
 
 SMALL = [
     # (name, config kwargs): several row tiles, ragged token tails, norm on/off, shared on/off
-    ("ragged37", dict(T=37, hidden=512, latent=384, n_experts=40, topk=6, inter=256, shared_inter=256)),
-    ("multi_tile_experts", dict(T=64, hidden=256, latent=256, n_experts=8, topk=4, inter=384, shared_inter=128)),
-    ("no_norm_no_shared", dict(T=19, hidden=384, latent=256, n_experts=12, topk=3, inter=128, shared_inter=0,
+    ("ragged37", dict(T=37, hidden=512, latent=512, n_experts=40, topk=6, inter=256, shared_inter=256)),
+    ("multi_tile_experts", dict(T=64, hidden=256, latent=256, n_experts=8, topk=4, inter=512, shared_inter=256)),
+    ("no_norm_no_shared", dict(T=19, hidden=512, latent=256, n_experts=12, topk=3, inter=256, shared_inter=0,
                                norm=False)),
-    ("single_token", dict(T=1, hidden=256, latent=128, n_experts=10, topk=2, inter=128, shared_inter=128)),
-    ("rsf_and_bias", dict(T=23, hidden=256, latent=256, n_experts=24, topk=5, inter=256, shared_inter=128,
+    ("single_token", dict(T=1, hidden=256, latent=256, n_experts=10, topk=2, inter=256, shared_inter=256)),
+    ("rsf_and_bias", dict(T=23, hidden=256, latent=256, n_experts=24, topk=5, inter=256, shared_inter=256,
                           routed_scaling_factor=2.446, zipf_s=1.1, zipf_c=0.05)),
 ]
 
@@ -64,7 +64,7 @@ def test_small_layer_parity(name, kw):
 def test_align_block_multiple_of_16(B):
     """Layout blocks of B = 32 or 48 slots read by the 16-slot kernel tiles (ids expanded B/16 times)."""
     H = _harness()
-    c = li.small_config(T=29, n_experts=9, topk=3, hidden=256, latent=256, inter=128, shared_inter=0)
+    c = li.small_config(T=29, n_experts=9, topk=3, hidden=256, latent=256, inter=256, shared_inter=0)
     out, ref, _ = _run_small(c, align_block=B)
     assert out["B"] == B
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
@@ -72,7 +72,7 @@ def test_align_block_multiple_of_16(B):
 
 def test_k_equals_E_dense_equivalence():
     H = _harness()
-    c = li.small_config(T=9, n_experts=6, topk=6, hidden=256, latent=128, inter=128, shared_inter=0, norm=False)
+    c = li.small_config(T=9, n_experts=6, topk=6, hidden=256, latent=256, inter=256, shared_inter=0, norm=False)
     out, ref, _ = _run_small(c)
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
     assert np.all(out["topk_ids"] == np.arange(6))
@@ -81,7 +81,7 @@ def test_k_equals_E_dense_equivalence():
 def test_expert_ids_above_255():
     """Experts 255, 256 and 299 forced through the selection bias must all run."""
     H = _harness()
-    c = li.small_config(T=12, n_experts=300, topk=4, hidden=256, latent=128, inter=128, shared_inter=0)
+    c = li.small_config(T=12, n_experts=300, topk=4, hidden=256, latent=256, inter=256, shared_inter=0)
     d = li.build(c)
     bias = np.zeros(c.n_experts, np.float32)
     bias[[255, 256, 299]] = 3.0
@@ -99,7 +99,7 @@ def test_expert_ids_above_255():
 def test_empty_batch_enqueues_nothing():
     H = _harness()
     from latent_moe_expert_amd import layer as L
-    c = li.small_config(T=3, hidden=256, latent=128, n_experts=6, topk=2, inter=128, shared_inter=128)
+    c = li.small_config(T=3, hidden=256, latent=256, n_experts=6, topk=2, inter=256, shared_inter=256)
     d = li.build(c)
     dl = H.DeviceLayer(c, dense={k: d[k] for k in ("down", "up", "norm", "router", "select_bias")},
                        experts=(d["exp_packed"], d["exp_scales"]))
@@ -156,7 +156,7 @@ def test_moe_route_entry_point():
     from latent_moe_expert_amd import layer as L
     from oracle.layer import route
     H = _harness()
-    c = li.small_config(T=50, n_experts=64, topk=8, hidden=512, inter=128, shared_inter=128)
+    c = li.small_config(T=50, n_experts=64, topk=8, hidden=512, latent=256, inter=256, shared_inter=256)
     d = li.build(c, experts=False)
     dims = L.make_dims(c.T, c.hidden, c.latent, c.n_experts, c.inter, c.shared_inter)
     x = H.to_dev_bf16(d["x"])
