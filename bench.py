@@ -125,9 +125,12 @@ def main():
     D_steps = [D[i % 4] for i in range(args.steps)]
     D_mean = float(np.mean(D_steps))
     pairs = c.T * c.topk
-    # algorithmic bytes of one gate/up launch: each touched expert's w1|w3 once, the gathered
-    # latent rows once per pair, and h written once per pair
-    gu_bytes = D_mean * gu_per_expert + pairs * c.latent * 2 + pairs * c.inter * 2
+    # algorithmic bytes of one gate/up launch (routed experts and, in the same launch, the
+    # shared experts' gate/up): each touched expert's w1|w3 once, the gathered latent rows
+    # once per pair, h written once per pair; the shared gate|up once, x once, hs written once
+    sh_gu = 2 * (c.shared_inter * c.hidden // 2 + c.shared_inter * c.hidden // 32) if c.shared_inter else 0
+    gu_bytes = (D_mean * gu_per_expert + pairs * c.latent * 2 + pairs * c.inter * 2
+                + sh_gu + (c.T * c.hidden * 2 + c.T * c.shared_inter * 2 if c.shared_inter else 0))
     gu_ms = stage_ms["expert_gate_up"]
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     sh_bytes = gen.shared_record_bytes(c) + gen.shared_scale_bytes(c) if c.shared_inter else 0
@@ -152,7 +155,7 @@ def main():
                                f"activations bf16, fp32 accumulation",
                    "global_batch": c.T, "parallelism": "none (1 GPU)",
                    "distinct_experts_per_step": D_mean},
-        "roofline": {"bound": "hbm", "kernel": "expert_gate_up (routed MXFP4 gate/up + GLU)",
+        "roofline": {"bound": "hbm", "kernel": "mx_small_kernel<GLU> (routed + shared MXFP4 gate/up + GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": int(gu_bytes), "avg_launch_ms": round(gu_ms, 5)},

@@ -128,6 +128,64 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   }
 }
 
+// All T tokens in one chunk (T <= 64): masks, counts, scan, padding and scatter
+// in a single block, so decode pays one launch instead of three.
+__global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                            int B, int cap, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ sorted_ids,
+                                                            int32_t* __restrict__ expert_ids,
+                                                            int32_t* __restrict__ num_post,
+                                                            int32_t* __restrict__ inv_pos) {
+  extern __shared__ unsigned long long mask[];      // [E]
+  int* offs = (int*)(mask + E);                      // [E]
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  build_masks(ids, T, k, E, 0, mask);
+  const int pairs = T * k;
+  const int per = (E + 1023) / 1024;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = __popcll(mask[e]);
+    counts[e] = c;
+    local += (c + B - 1) / B * B;
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - local;
+  for (int e = e0; e < e1; ++e) {
+    offs[e] = run;
+    const int c = __popcll(mask[e]);
+    const int p = (c + B - 1) / B * B;
+    for (int b = 0; b < p / B; ++b) expert_ids[run / B + b] = e;
+    for (int i = c; i < p; ++i) sorted_ids[run + i] = pairs;
+    run += p;
+  }
+  const int total = part[1023];
+  if (tid == 0) *num_post = total;
+  for (int i = total + tid; i < cap; i += 1024) sorted_ids[i] = pairs;
+  for (int b = total / B + tid; b < cap / B; b += 1024) expert_ids[b] = -1;
+  __syncthreads();
+  for (int i = tid; i < pairs; i += 1024) {
+    const int e = ids[i];
+    if (e < 0 || e >= E) {
+      inv_pos[i] = -1;
+      continue;
+    }
+    const int tl = i / k;
+    const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
+    const int pos = offs[e] + __popcll(below);
+    sorted_ids[pos] = i;
+    inv_pos[i] = pos;
+  }
+}
+
 }  // namespace
 
 int align_capacity(int T, int k, int E, int B) {
@@ -148,6 +206,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t*
   int32_t* chunk = (int32_t*)scratch;
   int32_t* offs = chunk + (size_t)nchunks * E;
   const size_t lds = (size_t)E * sizeof(unsigned long long);
+  if (nchunks <= 1) {
+    hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(1024), lds + (size_t)E * sizeof(int), s, ids, T, k, E, B,
+                       cap, counts, sorted_ids, expert_ids, num_post, inv_pos);
+    return hipGetLastError();
+  }
   if (nchunks > 0) hipLaunchKernelGGL(align_count_kernel, dim3(nchunks), dim3(256), lds, s, ids, T, k, E, chunk);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, B, T * k, cap, chunk, counts, offs,
                      sorted_ids, expert_ids, num_post);

@@ -27,6 +27,8 @@ constexpr int kMaxLatent = 8192;
 
 // ------------------------------------------------------------------ stage timing
 enum Stage { kProjRouter, kTopk, kAlign, kExpGateUp, kExpDown, kCombine, kShGateUp, kShDown, kUpProj, kNumStages };
+// the shared experts' contractions run inside the expert_gate_up / expert_down
+// launches (their stages stay in the list and measure ~0)
 const char* kStageNames[kNumStages] = {"proj_router", "topk", "align", "expert_gate_up", "expert_down",
                                        "combine_norm", "shared_gate_up", "shared_down", "up_proj"};
 constexpr int kMaxTimed = 256;
@@ -53,8 +55,18 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
   int T, H, L, E, I, Is, k, B, cap, pairs;
-  size_t z, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys, total;
+  bool small;      // T <= 64: split-K streaming projections
+  int sz, sr, su;  // K slices of the down-projection, the router and the up-projection
+  size_t z, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
+  size_t z_part, r_part, y_part, total;
 };
+
+// K slices of a split-K projection: about 8 row steps of 128 bytes per slice
+int slices(int K, int bytes_per_weight) {
+  const int steps = K * bytes_per_weight / 128;
+  int sp = steps / 8;
+  return sp < 1 ? 1 : (sp > 32 ? 32 : sp);
+}
 
 int check_dims(const moe_latent_dims* d, int topk) {
   if (!d) return MOE_EINVAL;
@@ -87,6 +99,10 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.B = d->align_block ? d->align_block : 16;
   p.pairs = p.T * p.k;
   p.cap = moe::align_capacity(p.T, p.k, p.E, p.B);
+  p.small = p.T <= 64;
+  p.sz = slices(p.H, 2);
+  p.sr = slices(p.H, 4);
+  p.su = slices(p.L, 2);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -108,6 +124,10 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.cn = take((size_t)p.T * p.L * 2);
   p.hs = take((size_t)p.T * p.Is * 2);
   p.ys = take((size_t)p.T * p.H * 4);
+  const size_t ts = p.small ? (size_t)p.T : 0;
+  p.z_part = take((size_t)p.sz * ts * p.L * 4);
+  p.r_part = take((size_t)p.sr * ts * p.E * 4);
+  p.y_part = take((size_t)p.su * ts * p.H * 4);
   p.total = o;
   return p;
 }
@@ -223,8 +243,18 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
   } while (0)
 
   STAGE_MARK(0);
-  // a1: down-projection and router logits, one launch
-  {
+  // a1: down-projection and router logits in one launch
+  if (p.small) {
+    moe::GemvArgs g{};
+    g.A = (const uint16_t*)x;
+    g.lda = p.H;
+    g.M = p.T;
+    g.K = p.H;
+    g.nseg = 2;
+    g.seg[0] = {down, p.L, 0, p.sz, at<float>(ws, p.z_part)};
+    g.seg[1] = {router->weight, p.E, 1, p.sr, at<float>(ws, p.r_part)};
+    MOE_HIP(moe::launch_dense_gemv(g, s));
+  } else {
     moe::DenseArgs a{};
     a.A = (const uint16_t*)x;
     a.lda = p.H;
@@ -236,18 +266,55 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     MOE_HIP(moe::launch_dense(a, s));
   }
   STAGE_MARK(1);
-  // a2: sigmoid, bias, top-k, weights
-  MOE_HIP(moe::launch_router_topk(logits, p.E, router->select_bias, p.T, p.E, p.k, d->routed_scaling_factor, ids, w,
-                                  s));
+  // a2: (finish the split-K sums,) sigmoid, bias, top-k, weights
+  {
+    moe::RouteArgs r{};
+    r.logits = logits;
+    r.r_part = p.small ? at<float>(ws, p.r_part) : nullptr;
+    r.sr = p.small ? p.sr : 0;
+    r.z_part = p.small ? at<float>(ws, p.z_part) : nullptr;
+    r.sz = p.sz;
+    r.L = p.L;
+    r.z_out = z;
+    r.logits_out = p.small ? logits : nullptr;
+    r.bias = router->select_bias;
+    r.T = p.T;
+    r.E = p.E;
+    r.k = p.k;
+    r.rsf = d->routed_scaling_factor;
+    r.ids = ids;
+    r.w = w;
+    MOE_HIP(moe::launch_route(r, s));
+  }
   STAGE_MARK(2);
   // a3: moe_align_block_size
   MOE_HIP(moe::launch_align(ids, p.T, p.k, p.E, p.B, counts, sorted, expert_ids, num_post, inv_pos,
                             at<void>(ws, p.align_scratch), s));
   STAGE_MARK(3);
-  // a4 + a5: gate/up contraction with the GLU epilogue
+  // a4 + a5 (and a10's gate/up): GLU contractions. The shared experts' blocks go
+  // first in the same launch, so their long K rows overlap the routed work.
   const size_t gu_bytes = (size_t)p.I * p.L / 2, gu_scales = (size_t)p.I * p.L / 32;
+  const size_t sgu = (size_t)p.Is * p.H / 2, sgs = (size_t)p.Is * p.H / 32;
   {
-    moe::MxArgs g{};
+    moe::MxArgs m{};
+    int n = 0;
+    if (shared) {
+      moe::MxProblem& g = m.p[n++];
+      g.A = (const uint16_t*)x;
+      g.lda = p.H;
+      g.routed = 0;
+      g.M = p.T;
+      g.max_blocks = (p.T + 15) / 16;
+      g.W = shared->packed;
+      g.S = shared->scales;
+      g.W2 = shared->packed + sgu;
+      g.S2 = shared->scales + sgs;
+      g.N = p.Is;
+      g.K = p.H;
+      g.out = hs;
+      g.ldo = p.Is;
+    }
+    moe::MxProblem& g = m.p[n++];
     g.A = z;
     g.lda = p.L;
     g.routed = 1;
@@ -269,12 +336,29 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     g.K = p.L;
     g.out = h;
     g.ldo = p.I;
-    MOE_HIP(moe::launch_mx_small(g, s));
+    m.nprob = n;
+    MOE_HIP(moe::launch_mx_small(m, s));
   }
   STAGE_MARK(4);
-  // a6: down contraction
+  // a6 (and a10's down): plain contractions, shared blocks first
   {
-    moe::MxArgs g{};
+    moe::MxArgs m{};
+    int n = 0;
+    if (shared) {
+      moe::MxProblem& dn = m.p[n++];
+      dn.A = hs;
+      dn.lda = p.Is;
+      dn.routed = 0;
+      dn.M = p.T;
+      dn.max_blocks = (p.T + 15) / 16;
+      dn.W = shared->packed + 2 * sgu;
+      dn.S = shared->scales + 2 * sgs;
+      dn.N = p.H;
+      dn.K = p.Is;
+      dn.out = ys;
+      dn.ldo = p.H;
+    }
+    moe::MxProblem& g = m.p[n++];
     g.A = h;
     g.lda = p.I;
     g.routed = 1;
@@ -294,51 +378,30 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     g.K = p.I;
     g.out = O;
     g.ldo = p.L;
-    MOE_HIP(moe::launch_mx_small(g, s));
+    m.nprob = n;
+    MOE_HIP(moe::launch_mx_small(m, s));
   }
   STAGE_MARK(5);
   // a7 + a8: weighted combine and RMSNorm
   MOE_HIP(moe::launch_combine_norm(O, p.L, inv_pos, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
                                    taps ? taps->c : nullptr, cn, s));
   STAGE_MARK(6);
-  // a10: shared experts on the full hidden state
-  if (shared) {
-    const size_t sgu = (size_t)p.Is * p.H / 2, sgs = (size_t)p.Is * p.H / 32;
-    moe::MxArgs g{};
-    g.A = (const uint16_t*)x;
-    g.lda = p.H;
-    g.routed = 0;
-    g.M = p.T;
-    g.max_blocks = (p.T + 15) / 16;
-    g.W = shared->packed;
-    g.S = shared->scales;
-    g.W2 = shared->packed + sgu;
-    g.S2 = shared->scales + sgs;
-    g.N = p.Is;
-    g.K = p.H;
-    g.out = hs;
-    g.ldo = p.Is;
-    MOE_HIP(moe::launch_mx_small(g, s));
-    STAGE_MARK(7);
-    moe::MxArgs dn{};
-    dn.A = hs;
-    dn.lda = p.Is;
-    dn.routed = 0;
-    dn.M = p.T;
-    dn.max_blocks = (p.T + 15) / 16;
-    dn.W = shared->packed + 2 * sgu;
-    dn.S = shared->scales + 2 * sgs;
-    dn.N = p.H;
-    dn.K = p.Is;
-    dn.out = ys;
-    dn.ldo = p.H;
-    MOE_HIP(moe::launch_mx_small(dn, s));
-  } else {
-    STAGE_MARK(7);
-  }
+  // (the shared experts ran inside the two contraction launches above)
+  STAGE_MARK(7);
   STAGE_MARK(8);
   // a9: up-projection, plus the shared output, rounded to bf16
-  {
+  if (p.small) {
+    moe::GemvArgs g{};
+    g.A = cn;
+    g.lda = p.L;
+    g.M = p.T;
+    g.K = p.L;
+    g.nseg = 1;
+    g.seg[0] = {up, p.H, 0, p.su, at<float>(ws, p.y_part)};
+    MOE_HIP(moe::launch_dense_gemv(g, s));
+    MOE_HIP(moe::launch_finish_up(at<float>(ws, p.y_part), p.su, p.T, p.H, shared ? ys : nullptr, (uint16_t*)y,
+                                  taps ? taps->y_routed : nullptr, s));
+  } else {
     moe::DenseArgs a{};
     a.A = cn;
     a.lda = p.L;
@@ -398,8 +461,17 @@ int moe_route(const moe_latent_dims* d, const void* x, const moe_router* router,
   a.nseg = 1;
   a.seg[0] = {router->weight, d->n_experts, 1, moe::kStoreF32, logits, d->n_experts, nullptr, 0, nullptr, 0};
   MOE_HIP(moe::launch_dense(a, s));
-  MOE_HIP(moe::launch_router_topk(logits, d->n_experts, router->select_bias, d->T, d->n_experts, topk,
-                                  d->routed_scaling_factor, topk_ids, topk_w, s));
+  moe::RouteArgs r{};
+  r.logits = logits;
+  r.sr = 0;
+  r.bias = router->select_bias;
+  r.T = d->T;
+  r.E = d->n_experts;
+  r.k = topk;
+  r.rsf = d->routed_scaling_factor;
+  r.ids = topk_ids;
+  r.w = topk_w;
+  MOE_HIP(moe::launch_route(r, s));
   return MOE_OK;
 }
 

@@ -17,11 +17,16 @@ namespace {
 
 constexpr int kMaxSlots = 64;
 
+// One block per token; thread owns float4 columns v = tid + 256*i (i < KV). Slots
+// are taken in groups of G = 32/KV with every load of a group issued before any
+// use, then added in slot order (a fixed rounding order).
+template <int KV>
 __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restrict__ O, int L,
                                                            const int32_t* __restrict__ inv_pos,
                                                            const float* __restrict__ w, int k,
                                                            const uint16_t* __restrict__ norm, float eps,
                                                            float* __restrict__ c_tap, uint16_t* __restrict__ c_norm) {
+  constexpr int G = 32 / KV;
   __shared__ int pos[kMaxSlots];
   __shared__ float wt[kMaxSlots];
   __shared__ float red[4];
@@ -31,23 +36,39 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restri
     wt[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  // each thread owns latent columns l = tid + 256*i; keep them in registers (L <= 256*kCols)
-  constexpr int kCols = 32;
-  float cv[kCols];
+  const int nvec = L >> 2;
+  f32x4_t acc[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += G) {
+    f32x4_t v[G][KV];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int j = j0 + g;
+      const int p = j < k ? pos[j] : -1;
+      const f32x4_t* row = (const f32x4_t*)(O + (size_t)(p < 0 ? 0 : p) * L);
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        const int vi = threadIdx.x + 256 * i;
+        v[g][i] = (p >= 0 && vi < nvec) ? row[vi] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int j = j0 + g;
+      const float wj = j < k ? wt[j] : 0.f;
+#pragma unroll
+      for (int i = 0; i < KV; ++i) acc[i] += wj * v[g][i];
+    }
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) {
-    const int l = threadIdx.x + 256 * i;
-    float c = 0.f;
-    if (l < L) {
-      for (int j = 0; j < k; ++j) {
-        const int p = pos[j];
-        if (p >= 0) c += wt[j] * O[(size_t)p * L + l];
-      }
-      ss += c * c;
-      if (c_tap) c_tap[(size_t)t * L + l] = c;
+  for (int i = 0; i < KV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    if (vi < nvec) {
+      ss += acc[i][0] * acc[i][0] + acc[i][1] * acc[i][1] + acc[i][2] * acc[i][2] + acc[i][3] * acc[i][3];
+      if (c_tap) *(f32x4_t*)(c_tap + (size_t)t * L + 4 * vi) = acc[i];
     }
-    cv[i] = c;
   }
   float scale = 1.f;
   if (norm) {
@@ -58,11 +79,17 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restri
     scale = rsqrtf(tot / (float)L + eps);
   }
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) {
-    const int l = threadIdx.x + 256 * i;
-    if (l < L) {
-      const float g = norm ? bf16_bits_to_f32(norm[l]) : 1.f;
-      c_norm[(size_t)t * L + l] = (uint16_t)f32_to_bf16_bits(norm ? cv[i] * scale * g : cv[i]);
+  for (int i = 0; i < KV; ++i) {
+    const int vi = threadIdx.x + 256 * i;
+    if (vi < nvec) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g = norm ? bf16_bits_to_f32(norm[4 * vi + e]) : 1.f;
+        o[e] = norm ? acc[i][e] * scale * g : acc[i][e];
+      }
+      uint2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *(uint2*)(c_norm + (size_t)t * L + 4 * vi) = packed;
     }
   }
 }
@@ -83,7 +110,16 @@ hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
 hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
                                const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
+  const int nvec = L / 4;
+  const int kv = (nvec + 255) / 256;
+  if (kv <= 1)
+    hipLaunchKernelGGL(combine_norm_kernel<1>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
+  else if (kv <= 2)
+    hipLaunchKernelGGL(combine_norm_kernel<2>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
+  else if (kv <= 4)
+    hipLaunchKernelGGL(combine_norm_kernel<4>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
+  else
+    hipLaunchKernelGGL(combine_norm_kernel<8>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
   return hipGetLastError();
 }
 

@@ -1,0 +1,215 @@
+// Dense projections for decode-sized batches (T <= 64): split-K streaming GEMV.
+//
+// At decode the two latent projections and the router read 128 MB of weights
+// for 16 tokens, so they are bound by HBM like the experts. Each wave streams
+// 64 weight rows over one K slice with the same memory path as the MXFP4
+// kernel: every load instruction covers 8 rows x 128 contiguous bytes, staged
+// through a wave-private XOR-swizzled LDS tile into bf16 MFMA 16x16x32
+// fragments. K is split across waves so that a few hundred blocks cover the
+// chip; partial sums go to fp32 planes [slice][token][row] and are summed in a
+// fixed slice order by the consumer (the route kernel for the latent row and
+// the logits, finish_up for the output), so results stay run-to-run identical.
+//
+// fp32 router weights are split exactly into three bf16 planes (truncation:
+// w = hi + mid + lo), so each partial is a sum of exact bf16 products in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void split3x2(float f0, float f1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t h0 = __float_as_uint(f0) & 0xffff0000u, h1 = __float_as_uint(f1) & 0xffff0000u;
+  const float r0 = f0 - __uint_as_float(h0), r1 = f1 - __uint_as_float(h1);
+  const uint32_t m0 = __float_as_uint(r0) & 0xffff0000u, m1 = __float_as_uint(r1) & 0xffff0000u;
+  const float l0 = r0 - __uint_as_float(m0), l1 = r1 - __uint_as_float(m1);
+  hi = (h0 >> 16) | h1;
+  mid = (m0 >> 16) | m1;
+  lo = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xffff0000u);
+}
+
+template <int MT>
+__global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int blocks0, int bands0, int bands1) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][64 * 128];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, q = lane >> 4;
+  const bool second = (int)blockIdx.x >= blocks0;
+  const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
+  const GemvSeg& sg = args.seg[second ? 1 : 0];
+  const int bands = second ? bands1 : bands0;
+  const int band = local % bands, slice = local / bands;
+  const int row0 = (band * 4 + wave) * 64;
+  if (row0 >= sg.N) return;  // wave-uniform; no block barrier in this kernel
+  uint8_t* lds = lds_all[wave];
+
+  const bool F32 = sg.w_f32 != 0;                     // block-uniform weight format
+  const int kEs = F32 ? 4 : 2;                        // bytes per weight
+  const int K = args.K;
+  const uint32_t rowb = (uint32_t)K * kEs;            // bytes per weight row
+  const int nsteps = (int)(rowb / 128);               // 128 bytes of every row per step
+  const int per = (nsteps + sg.splits - 1) / sg.splits;
+  const int s0 = slice * per, s1 = min(nsteps, s0 + per);
+  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * rowb);
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, 0x7fffffffu);
+
+  uint32_t goff[8], wlds[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    const int row = min(row0 + 8 * l + (lane >> 3), sg.N - 1);  // rows past N are never stored
+    goff[l] = (uint32_t)row * rowb + (lane & 7) * 16;
+    const int j = 8 * l + (lane >> 3), c = lane & 7;
+    wlds[l] = j * 128 + ((c ^ (j & 7)) * 16);
+  }
+  auto frag = [&](int t, int c) -> uint32_t {
+    const int j = 16 * t + nl;
+    return j * 128 + ((c ^ (j & 7)) * 16);
+  };
+  uint32_t aoff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + nl;
+    aoff[mt] = m < args.M ? ((uint32_t)m * (uint32_t)args.lda + q * 8) * 2 : 0x80000000u;
+  }
+
+  f32x4_t acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // MFMA k-steps (32 K each) per 128-byte step: 2 for bf16 weights, 1 for fp32
+  struct Stage {
+    u32x4_t w[8];
+    u32x4_t x[MT][2];
+  };
+  auto issue = [&](Stage& st, int s) {
+    const uint32_t kb = (uint32_t)s * 128;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16(w_rs, goff[l] + kb);
+    const uint32_t kelem = kb / kEs;  // first K index of the step
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (h == 0 || !F32)
+          st.x[mt][h] = buf_load16(a_rs, aoff[mt] == 0x80000000u ? aoff[mt] : aoff[mt] + (kelem + h * 32) * 2);
+  };
+  auto consume = [&](const Stage& st) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) *(u32x4_t*)(lds + wlds[l]) = st.w[l];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (!F32) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4_t wf = *(const u32x4_t*)(lds + frag(t, 4 * h + q));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[mt][h]), as_bf16x8(wf), acc[mt][t], 0, 0, 0);
+        }
+      } else {
+        const u32x4_t w0 = *(const u32x4_t*)(lds + frag(t, 2 * q));
+        const u32x4_t w1 = *(const u32x4_t*)(lds + frag(t, 2 * q + 1));
+        uint32_t h4[4], m4[4], l4[4];
+        split3x2(__uint_as_float(w0[0]), __uint_as_float(w0[1]), h4[0], m4[0], l4[0]);
+        split3x2(__uint_as_float(w0[2]), __uint_as_float(w0[3]), h4[1], m4[1], l4[1]);
+        split3x2(__uint_as_float(w1[0]), __uint_as_float(w1[1]), h4[2], m4[2], l4[2]);
+        split3x2(__uint_as_float(w1[2]), __uint_as_float(w1[3]), h4[3], m4[3], l4[3]);
+        const u32x4_t hi = {h4[0], h4[1], h4[2], h4[3]};
+        const u32x4_t mi = {m4[0], m4[1], m4[2], m4[3]};
+        const u32x4_t lo = {l4[0], l4[1], l4[2], l4[3]};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[mt][0]), as_bf16x8(hi), acc[mt][t], 0, 0, 0);
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[mt][0]), as_bf16x8(mi), acc[mt][t], 0, 0, 0);
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[mt][0]), as_bf16x8(lo), acc[mt][t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (s0 < s1) {
+    Stage st0, st1;
+    issue(st0, s0);
+    int s = s0;
+    for (; s + 2 <= s1; s += 2) {
+      issue(st1, s + 1);
+      consume(st0);
+      if (s + 2 < s1) issue(st0, s + 2);
+      consume(st1);
+    }
+    if (s < s1) consume(st0);
+  }
+
+  // partial sums of this slice: lane holds D[m = 4q + r][n = nl] of each tile
+  float* part = sg.part + (size_t)slice * args.M * sg.N;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = row0 + 16 * t + nl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 16 + 4 * q + r;
+        if (m < args.M && n < sg.N) part[(size_t)m * sg.N + n] = acc[mt][t][r];
+      }
+    }
+}
+
+__global__ __launch_bounds__(256) void finish_up_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                        const float* __restrict__ addend, uint16_t* __restrict__ y,
+                                                        float* __restrict__ tap) {
+  const size_t total = (size_t)M * N / 4;
+  const size_t plane = (size_t)M * N;
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) acc += *(const f32x4_t*)(part + s * plane + 4 * i);
+    if (tap) *(f32x4_t*)(tap + 4 * i) = acc;
+    if (addend) acc += *(const f32x4_t*)(addend + 4 * i);
+    *(uint2*)(y + 4 * i) = uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  }
+}
+
+hipError_t launch_kind(const GemvArgs& a, int blocks0, int bands0, int bands1, int total, hipStream_t s) {
+  const int mt = (a.M + 15) / 16;
+  if (mt <= 1)
+    hipLaunchKernelGGL(dense_gemv_kernel<1>, dim3(total), dim3(256), 0, s, a, blocks0, bands0, bands1);
+  else if (mt <= 2)
+    hipLaunchKernelGGL(dense_gemv_kernel<2>, dim3(total), dim3(256), 0, s, a, blocks0, bands0, bands1);
+  else
+    hipLaunchKernelGGL(dense_gemv_kernel<4>, dim3(total), dim3(256), 0, s, a, blocks0, bands0, bands1);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dense_gemv(const GemvArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.M > 64) return hipErrorInvalidValue;
+  int bands[2] = {1, 1}, blocks[2] = {0, 0};
+  for (int i = 0; i < a.nseg; ++i) {
+    bands[i] = (a.seg[i].N + 255) / 256;
+    blocks[i] = bands[i] * a.seg[i].splits;
+  }
+  return launch_kind(a, blocks[0], bands[0], bands[1], blocks[0] + blocks[1], s);
+}
+
+hipError_t launch_finish_up(const float* part, int splits, int M, int N, const float* addend, uint16_t* y, float* tap,
+                            hipStream_t s) {
+  const size_t total = (size_t)M * N / 4;
+  if (!total) return hipSuccess;
+  const size_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(finish_up_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, s, part, splits,
+                     M, N, addend, y, tap);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -36,9 +36,42 @@ struct DenseArgs {
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- decode-size dense projections
+// Split-K streaming GEMV for M <= 64 tokens: part[slice][m][n] = sum over the slice's K of A[m][k] W[n][k].
+struct GemvSeg {
+  const void* W;   // [N, K] row-major, bf16 bits or fp32
+  int N;           // rows of W
+  int w_f32;       // 1: fp32 weights, split exactly into three bf16 planes
+  int splits;      // K slices (each a whole number of 128-byte row steps)
+  float* part;     // [splits][M][N] fp32 partial sums
+};
+struct GemvArgs {
+  const uint16_t* A;  // bf16 [M, lda]
+  int lda, M, K;      // K * (2 or 4) bytes a multiple of 128
+  GemvSeg seg[2];
+  int nseg;
+};
+hipError_t launch_dense_gemv(const GemvArgs& a, hipStream_t s);
+// y = bf16(sum_s part[s] + addend); tap = sum_s part[s] (fp32), both [M, N]; N % 4 == 0
+hipError_t launch_finish_up(const float* part, int splits, int M, int N, const float* addend, uint16_t* y, float* tap,
+                            hipStream_t s);
+
 // ---------------------------------------------------------------- router
-hipError_t launch_router_topk(const float* logits, int ld_logits, const float* select_bias, int T, int E,
-                              int k, float rsf, int32_t* ids, float* w, hipStream_t s);
+struct RouteArgs {
+  const float* logits;  // [T][E] router logits the selection reads
+  const float* r_part;  // optional split-K logit planes [sr][T][E], summed into logits_out (== logits)
+  int sr;
+  const float* z_part;  // optional latent partial planes [sz][T][L], summed and rounded to bf16 into z_out
+  int sz, L;
+  uint16_t* z_out;
+  float* logits_out;
+  const float* bias;    // selection-only bias [E] or null
+  int T, E, k;
+  float rsf;
+  int32_t* ids;         // [T][k], ascending expert id per token
+  float* w;             // [T][k]
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- align
 size_t align_scratch_bytes(int T, int E);
@@ -47,7 +80,8 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t*
                         int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, void* scratch, hipStream_t s);
 
 // ---------------------------------------------------------------- MXFP4 contractions
-struct MxArgs {
+// One grouped contraction problem: out[row] = act(A_row . W1^T, A_row . W2^T) (GLU) or A_row . W^T.
+struct MxProblem {
   // activations: bf16 rows
   const uint16_t* A;
   int lda;
@@ -59,17 +93,24 @@ struct MxArgs {
   const int32_t* num_post;    // routed: device scalar, padded slot count
   int pairs, topk;            // routed
   int M;                      // dense: number of rows
-  int max_blocks;             // grid.y upper bound
+  int max_blocks;             // 16-slot tiles to cover (upper bound; extra tiles exit)
   // weights (MXFP4): matrix of expert e at W + e*w_stride, [N, K/2] bytes; scales at S + e*s_stride, [N, K/32]
   const uint8_t* W;
   const uint8_t* S;
   const uint8_t* W2;          // GLU: the up matrix (same layout), null for a plain contraction
   const uint8_t* S2;
   size_t w_stride, s_stride;
-  int N, K;
+  int N, K;                   // K multiple of 256, N multiple of the block's columns
   // output: GLU -> bf16 [rows, ldo] = act(gate) * up; plain -> f32 [rows, ldo]
   void* out;
   int ldo;
+};
+
+// Up to two problems of the same kind (both GLU or both plain) in one launch;
+// problem 0's blocks come first in the grid.
+struct MxArgs {
+  MxProblem p[2];
+  int nprob;
 };
 
 hipError_t launch_mx_small(const MxArgs& a, hipStream_t s);

@@ -50,11 +50,17 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 template <bool GLU>
-__global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
+__global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0, int bands0, int bands1) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][64 * 128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, q = lane >> 4;
-  const int blk = blockIdx.y;
+  // block -> (problem, column band, 16-slot tile); problem 0 first
+  const bool second = (int)blockIdx.x >= blocks0;
+  const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
+  const int bands = second ? bands1 : bands0;
+  const MxProblem& a = args.p[second ? 1 : 0];
+  const int band = local % bands;
+  const int blk = local / bands;
   uint8_t* lds = lds_all[wave];
 
   int expert = 0;
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
     return;
   }
   constexpr int kColsPerWave = GLU ? 32 : 64;
-  const int col0 = (blockIdx.x * 4 + wave) * kColsPerWave;
+  const int col0 = (band * 4 + wave) * kColsPerWave;
   if (col0 >= a.N) return;  // wave-uniform; the kernel has no block barrier
 
   const int K = a.K;
@@ -207,14 +213,22 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs a) {
 }  // namespace
 
 hipError_t launch_mx_small(const MxArgs& a, hipStream_t s) {
-  if (a.max_blocks <= 0) return hipSuccess;
-  const bool glu = a.W2 != nullptr;
+  const bool glu = a.p[0].W2 != nullptr;
   const int cols_per_block = 4 * (glu ? 32 : 64);
-  dim3 grid((a.N + cols_per_block - 1) / cols_per_block, a.max_blocks);
+  int bands[2] = {0, 0}, blocks[2] = {0, 0};
+  for (int i = 0; i < a.nprob; ++i) {
+    bands[i] = (a.p[i].N + cols_per_block - 1) / cols_per_block;
+    blocks[i] = a.p[i].max_blocks > 0 ? bands[i] * a.p[i].max_blocks : 0;
+  }
+  const long long total = (long long)blocks[0] + blocks[1];
+  if (total <= 0) return hipSuccess;
+  if (total > 0x7fffffffll) return hipErrorInvalidValue;
   if (glu)
-    hipLaunchKernelGGL(mx_small_kernel<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mx_small_kernel<true>, dim3((unsigned)total), dim3(256), 0, s, a, blocks[0], bands[0],
+                       bands[1] ? bands[1] : 1);
   else
-    hipLaunchKernelGGL(mx_small_kernel<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mx_small_kernel<false>, dim3((unsigned)total), dim3(256), 0, s, a, blocks[0], bands[0],
+                       bands[1] ? bands[1] : 1);
   return hipGetLastError();
 }
 

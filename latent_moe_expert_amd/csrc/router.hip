@@ -4,10 +4,15 @@
 // correction bias is used for selection only and the weights are renormalised
 // over the selected top-k, then multiplied by routed_scaling_factor).
 //
-// One wave per token. Lane l owns experts l, l+64, l+128, ... and keeps their
-// keys in LDS; k rounds of (local best, wave arg-max) pick the winners, ties
-// going to the lower expert id. The k ids are then written in ascending id
-// order with their weights s_j / sum(s_sel) * rsf (unbiased scores).
+// One block per token. Keys key_e = sigmoid(logit_e) + bias_e become unique
+// 64-bit composites (key bits, then the inverted expert id) so that ordering
+// them descending ranks larger keys first with ties going to the lower id; a
+// bitonic sort in LDS does that and the first k are selected. They are written
+// in ascending id order with weights s_e / sum(s_selected) * rsf from the
+// unbiased scores, summed in ascending id order.
+//
+// When the down-projection and router logits arrive as partial sums over K
+// slices, a wide kernel first sums them (latent rounded to bf16) in slice order.
 #include <float.h>
 
 #include "common.h"
@@ -17,64 +22,126 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ void better(float& bk, int& bi, float k2, int i2) {
-  // larger key wins; equal keys -> lower id
-  if (k2 > bk || (k2 == bk && i2 < bi)) { bk = k2; bi = i2; }
+constexpr int kMaxE = 4096;
+
+// Sums split-K partial planes: the latent rows (rounded to bf16) and the router
+// logits (fp32), each element over its slices in slice order (loads issued in
+// batches of 8 so that they overlap).
+__global__ __launch_bounds__(256) void reduce_planes_kernel(RouteArgs a) {
+  const size_t nz = a.z_part ? (size_t)a.T * a.L / 4 : 0;  // float4 groups of the latent
+  const size_t nr = a.r_part ? (size_t)a.T * a.E : 0;        // logits, one by one
+  const size_t zplane = (size_t)a.T * a.L, rplane = (size_t)a.T * a.E;
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < nz + nr; i += (size_t)gridDim.x * 256) {
+    if (i < nz) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < a.sz; s0 += 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = s0 + u < a.sz ? *(const f32x4_t*)(a.z_part + (s0 + u) * zplane + 4 * i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      *(uint2*)(a.z_out + 4 * i) = uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    } else {
+      const size_t j = i - nz;
+      float acc = 0.f;
+      for (int s0 = 0; s0 < a.sr; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s0 + u < a.sr ? a.r_part[(s0 + u) * rplane + j] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      a.logits_out[j] = acc;
+    }
+  }
 }
 
-__global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict__ logits, int ld,
-                                                         const float* __restrict__ bias, int E, int k,
-                                                         float rsf, int32_t* __restrict__ ids,
-                                                         float* __restrict__ wout) {
-  extern __shared__ float keys[];  // [E]
+// Order-preserving map of a float to uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One block per token: the keys become unique 64-bit composites
+//   (ordered key bits << 32) | (0xffffffff - expert id),
+// so "larger composite" means larger key, ties to the lower id. A bitonic sort
+// in LDS orders them descending; the first k are the selected experts.
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+  __shared__ unsigned long long comp[kMaxE];
+  __shared__ float sco[kMaxE];
+  __shared__ float sel_s[64];
+  __shared__ int sel_e[64];
+  __shared__ float total;
   const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* lg = logits + (size_t)t * ld;
-  for (int e = lane; e < E; e += 64) {
-    const float s = sigmoidf_dev(lg[e]);
-    const float key = s + (bias ? bias[e] : 0.f);
-    keys[e] = (key == key) ? key : -FLT_MAX;  // a NaN key never wins
-  }
-  // each lane only touches its own entries below, so no barrier is needed
-  int my_sel = -1;
-  for (int r = 0; r < k; ++r) {
-    float bk = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int e = lane; e < E; e += 64) better(bk, bi, keys[e], e);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float k2 = __shfl_xor(bk, o, 64);
-      const int i2 = __shfl_xor(bi, o, 64);
-      better(bk, bi, k2, i2);
+  const int tid = threadIdx.x;
+  const int E = a.E, k = a.k;
+  int n2 = 64;
+  while (n2 < E) n2 <<= 1;  // power of two >= E; padding composites are 0 and sort last
+  const float* lg = a.logits + (size_t)t * E;
+
+  for (int e = tid; e < n2; e += 256) {
+    unsigned long long c = 0ull;
+    if (e < E) {
+      const float sc = sigmoidf_dev(lg[e]);
+      float kv = sc + (a.bias ? a.bias[e] : 0.f);
+      kv = (kv == kv) ? kv : -FLT_MAX;  // a NaN key ranks below every real key
+      sco[e] = sc;
+      c = ((unsigned long long)ordered_bits(kv) << 32) | (0xffffffffu - (uint32_t)e);
     }
-    // bi is uniform now; -INFINITY entries are taken ones (keys are > -inf otherwise)
-    if (bi < 0 || bi >= E) bi = 0;  // cannot happen for finite keys and k <= E
-    if ((bi & 63) == lane) keys[bi] = -INFINITY;
-    if (lane == r) my_sel = bi;
+    comp[e] = c;
   }
-  // ascending id order: rank among the selected
-  int rank = 0;
-  for (int i = 0; i < k; ++i) {
-    const int other = __shfl(my_sel, i, 64);
-    rank += (lane < k && other < my_sel) ? 1 : 0;
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (n2 >> 1); i += 256) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const unsigned long long x = comp[lo], y = comp[hi];
+        if ((x < y) == desc) {
+          comp[lo] = y;
+          comp[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
   }
-  const float s = (lane < k) ? sigmoidf_dev(lg[my_sel]) : 0.f;
-  // sum of the selected scores, in selection order (a fixed rounding order)
-  float ssum = 0.f;
-  for (int i = 0; i < k; ++i) ssum += __shfl(s, i, 64);
-  if (lane < k) {
-    ids[(size_t)t * k + rank] = my_sel;
-    wout[(size_t)t * k + rank] = s / ssum * rsf;
+  // the k winners; write them in ascending id order
+  if (tid < k) {
+    const int e = (int)(0xffffffffu - (uint32_t)(comp[tid] & 0xffffffffull));
+    int p = 0;
+    for (int j = 0; j < k; ++j) {
+      const int o = (int)(0xffffffffu - (uint32_t)(comp[j] & 0xffffffffull));
+      p += o < e ? 1 : 0;
+    }
+    sel_e[p] = e;
+    sel_s[p] = sco[e];
+  }
+  __syncthreads();
+  if (tid == 0) {  // ascending id order: a fixed rounding order
+    float tot = 0.f;
+    for (int p = 0; p < k; ++p) tot += sel_s[p];
+    total = tot;
+  }
+  __syncthreads();
+  if (tid < k) {
+    a.ids[(size_t)t * k + tid] = sel_e[tid];
+    a.w[(size_t)t * k + tid] = sel_s[tid] / total * a.rsf;
   }
 }
 
 }  // namespace
 
-hipError_t launch_router_topk(const float* logits, int ld_logits, const float* select_bias, int T, int E, int k,
-                              float rsf, int32_t* ids, float* w, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(T), dim3(64), (size_t)E * sizeof(float), s, logits, ld_logits,
-                     select_bias, E, k, rsf, ids, w);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.r_part || a.z_part) {  // finish split-K sums first, in parallel over all elements
+    const size_t n = (a.z_part ? (size_t)a.T * a.L / 4 : 0) + (a.r_part ? (size_t)a.T * a.E : 0);
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(reduce_planes_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
