@@ -25,11 +25,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "latent-MoE layer tokens/s; % peak HBM GB/s (decode), % MXFP4 MFMA (prefill)"
 HBM_PEAK_GBS = 8000.0
-EXPERT_GATE_UP_BYTES = None  # set from the config below
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC summary,
+    or None when that summary was taken on a different kernel source or workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "mx_small_decode16_traffic.md")
+    try:
+        line = next(l for l in open(path) if l.startswith("traffic_record:"))
+        rec = json.loads(line.split(":", 1)[1])
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, StopIteration, ValueError, KeyError):
+        return None
+    if rec.get("workload") != workload or hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
 
 
 def cpu_baseline(c, dl, x_bits, n_tokens: int):
@@ -66,6 +81,8 @@ def main():
     ap.add_argument("--config", default="decode16", help="named workload (decode16, decode256, prefill8192)")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="before the steps, run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; runs on more than one GPU are not part of it",
@@ -78,6 +95,14 @@ def main():
     from workload import gen
 
     c = gen.named_config(args.config)
+    if args.copy_mb:
+        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.copy_mb} MiB device copies")
+        del src, dst
     t0 = time.time()
     dl = DeviceLayer(c)
     xs_bits = gen.make_x(c, 0, T=4 * c.T)
@@ -157,7 +182,7 @@ def main():
                    "distinct_experts_per_step": D_mean},
         "roofline": {"bound": "hbm", "kernel": "mx_small_kernel<GLU> (routed + shared MXFP4 gate/up + GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
                      "bytes_per_launch": int(gu_bytes), "avg_launch_ms": round(gu_ms, 5)},
         "expert_kernels_hbm_frac": round(exp_bytes / (exp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},

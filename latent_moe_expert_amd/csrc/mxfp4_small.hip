@@ -44,6 +44,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Weight bytes are read exactly once: non-temporal, so that the stream does not push the
+// re-used lines (scales, activations) out of L2.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4_t buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
 
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   auto issue = [&](Stage& st, int d) {
     const uint32_t kbyte = (uint32_t)d * 128;  // 256 weights of a row per double step
 #pragma unroll
-    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16((GLU && l >= 4) ? w_hi : w_lo, goff[l] + kbyte);
+    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16_stream((GLU && l >= 4) ? w_hi : w_lo, goff[l] + kbyte);
 #pragma unroll
     for (int t = 0; t < 4; ++t) st.sc[t] = buf_load8((GLU && t >= 2) ? s_hi : s_lo, soff[t] + (uint32_t)d * 8);
     const uint32_t ab = aoff + (uint32_t)d * astep;
