@@ -7,7 +7,8 @@
 //
 // Work unit: one 16-slot tile of the expert-sorted layout (or 16 rows of a
 // dense batch) x 64 weight rows per wave (GLU: 32 gate rows and the same 32 up
-// rows; plain: 64 rows), 4 waves per block, full K per wave.
+// rows; plain: 64 rows), 4 waves per block, full K per wave. The block loads
+// the tile's activations once per step into a shared, swizzled LDS tile.
 //
 // Memory path. Decode streams each touched expert's bytes once, so the kernel
 // lives on HBM efficiency. Every weight load instruction of a wave covers 8
@@ -16,7 +17,7 @@
 // native fragment (16 rows x 64 bytes per instruction) measured about 27%
 // slower. The bytes go through a wave-private LDS tile, XOR-swizzled so that
 // both the 16-byte writes and the MFMA fragment reads are bank-conflict free,
-// and no block barrier is needed. Activations come in through buffer loads:
+// and no barrier is needed for them. Activations come in through buffer loads:
 // slots without a token get an out-of-range offset, read as zeros with no
 // memory traffic.
 //
@@ -47,18 +48,14 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 // Weight bytes are read exactly once: non-temporal, so that the stream does not push the
 // re-used lines (scales, activations) out of L2.
 constexpr int kNonTemporal = 2;
-__device__ __forceinline__ u32x4_t buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
-}
-
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
 
 template <bool GLU>
 __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0, int bands0, int bands1) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][64 * 128];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // per wave: an 8 KB weight tile; per block: two 8 KB activation tiles (16 slots x 256 K bf16)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[4][64 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][16 * 512];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int nl = lane & 15, q = lane >> 4;
   // block -> (problem, column band, 16-slot tile); problem 0 first
   const bool second = (int)blockIdx.x >= blocks0;
@@ -67,8 +64,9 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   const MxProblem& a = args.p[second ? 1 : 0];
   const int band = local % bands;
   const int blk = local / bands;
-  uint8_t* lds = lds_all[wave];
+  uint8_t* lds = lds_w[wave];
 
+  // block-uniform exits only (the loop below has block barriers)
   int expert = 0;
   if (a.routed) {
     if (blk * 16 >= *a.num_post) return;
@@ -78,8 +76,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     return;
   }
   constexpr int kColsPerWave = GLU ? 32 : 64;
-  const int col0 = (band * 4 + wave) * kColsPerWave;
-  if (col0 >= a.N) return;  // wave-uniform; the kernel has no block barrier
+  const int col0 = (band * 4 + wave) * kColsPerWave;  // N is a multiple of the block's columns
 
   const int K = a.K;
   const uint32_t kb2 = (uint32_t)K / 2, ks32 = (uint32_t)K / 32;
@@ -89,52 +86,41 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   const __amdgpu_buffer_rsrc_t w_hi = GLU ? make_rsrc(a.W2 + (size_t)expert * a.w_stride, mat_bytes) : w_lo;
   const __amdgpu_buffer_rsrc_t s_hi = GLU ? make_rsrc(a.S2 + (size_t)expert * a.s_stride, mat_scales) : s_lo;
 
-  // wave tile t (16 rows) -> first row in its matrix
-  //   GLU:   t = 0,1 -> gate rows col0 + 16t;  t = 2,3 -> up rows col0 + 16(t-2)
-  //   plain: t -> rows col0 + 16t
-  auto tile_row = [&](int t) -> uint32_t { return (uint32_t)(col0 + (GLU ? (t & 1) : t) * 16); };
+  // Wave tile t (16 rows) starts at row col0 + 16*tt(t) of its matrix, tt(t) = t&1 (GLU: t<2 gate,
+  // t>=2 up) or t (plain). Load l (0..7) of a double step covers the wave's slots 8l..8l+7;
+  // lane = (slot 8l + lane/8, 16-byte chunk lane%8). Row offsets are uniform per l.
+  auto tt = [](int t) { return GLU ? (t & 1) : t; };
+  const uint32_t gbase = (uint32_t)(col0 + (lane >> 3)) * kb2 + (lane & 7) * 16;
+  // LDS: slot j, chunk c lives at j*128 + ((c ^ (j & 7)) * 16); for load l, j & 7 = lane >> 3
+  const uint32_t wbase = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16);
+  // fragment of tile t, step h: slot 16t + nl, chunk 4h + q
+  const uint32_t rbase0 = nl * 128 + (((q) ^ (nl & 7)) * 16);
+  const uint32_t rbase1 = nl * 128 + (((4 + q) ^ (nl & 7)) * 16);
+  const uint32_t sbase = (uint32_t)(col0 + nl) * ks32;  // scales: 8 bytes per row per double step
 
-  // global load l (0..7) of a double step: slots 8l..8l+7 of the wave's 64; lane = (slot, 16-byte chunk)
-  uint32_t goff[8];
-#pragma unroll
-  for (int l = 0; l < 8; ++l) {
-    const uint32_t row = tile_row(l >> 1) + 8 * (l & 1) + (lane >> 3);
-    goff[l] = row * kb2 + (lane & 7) * 16;
-  }
-  // LDS: slot j, chunk c lives at j*128 + ((c ^ (j & 7)) * 16)
-  uint32_t wlds[8];
-#pragma unroll
-  for (int l = 0; l < 8; ++l) {
-    const int j = 8 * l + (lane >> 3), c = lane & 7;
-    wlds[l] = j * 128 + ((c ^ (j & 7)) * 16);
-  }
-  uint32_t rlds[4][2];  // fragment of tile t, step h: slot 16t + nl, chunk 4h + q
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 16 * t + nl, c = 4 * h + q;
-      rlds[t][h] = j * 128 + ((c ^ (j & 7)) * 16);
-    }
-  // scales of the fragment rows: 8 bytes per row per double step; byte q (step 0) and 4+q (step 1)
-  uint32_t soff[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) soff[t] = (tile_row(t) + nl) * ks32;
-
-  // activation row feeding MFMA row nl (slots without a token read zeros)
-  int arow = -1;
+  // activation tile: thread tid fills slot tid/16, chunks tid%16 and tid%16 + 16 (16 bytes each)
+  uint32_t aoff_fill;
   {
-    const int pos = blk * 16 + nl;
+    const int slot = tid >> 4;
+    const int pos = blk * 16 + slot;
+    int arow = -1;
     if (a.routed) {
       const int sid = a.sorted_ids[pos];
       if (sid < a.pairs) arow = a.a_by_pos ? pos : sid / a.topk;
     } else if (pos < a.M) {
       arow = pos;
     }
+    aoff_fill = arow >= 0 ? ((uint32_t)arow * (uint32_t)a.lda) * 2 + (tid & 15) * 16 : kOob;
   }
+  const uint32_t a_step = aoff_fill == kOob ? 0u : 512u;
+  const int fslot = tid >> 4, fc = tid & 15;
+  const uint32_t afill0 = fslot * 512 + (((fc) ^ fslot) * 16);
+  const uint32_t afill1 = fslot * 512 + (((fc + 16) ^ fslot) * 16);
+  // fragment reads: lane (nl, q), step h, MFMA j: chunk h*16 + 4q + j of slot nl
+  uint32_t aread[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aread[j] = nl * 512 + (((4 * q + j) ^ nl) * 16);
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a.A, 0x7fffffffu);
-  const uint32_t aoff = arow >= 0 ? ((uint32_t)arow * (uint32_t)a.lda + q * 32) * 2 : kOob;
-  const uint32_t astep = arow >= 0 ? 512u : 0u;  // bytes of activations per double step
 
   f32x4_t acc[4];
 #pragma unroll
@@ -143,28 +129,45 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   struct Stage {
     u32x4_t w[8];
     uint2 sc[4];
-    u32x4_t x[2][4];
   };
-  auto issue = [&](Stage& st, int d) {
-    const uint32_t kbyte = (uint32_t)d * 128;  // 256 weights of a row per double step
+  u32x4_t anext[2];
+  auto issue = [&](Stage& st, int d, bool with_a) {
+    if (with_a) {  // activations first: they are waited on before this step's weights
+      const uint32_t ao = aoff_fill + (uint32_t)d * a_step;
+      anext[0] = buf_load16(a_rs, ao);
+      anext[1] = buf_load16(a_rs, aoff_fill == kOob ? kOob : ao + 256);
+    }
+    const uint32_t vo = gbase + (uint32_t)d * 128;  // 256 weights of a row per double step
 #pragma unroll
-    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16_stream((GLU && l >= 4) ? w_hi : w_lo, goff[l] + kbyte);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) st.sc[t] = buf_load8((GLU && t >= 2) ? s_hi : s_lo, soff[t] + (uint32_t)d * 8);
-    const uint32_t ab = aoff + (uint32_t)d * astep;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st.x[h][j] = buf_load16(a_rs, ab + (arow >= 0 ? (uint32_t)(h * 256 + j * 16) : 0u));
-  };
-  auto consume = [&](const Stage& st) {
-#pragma unroll
-    for (int l = 0; l < 8; ++l) *(u32x4_t*)(lds + wlds[l]) = st.w[l];
+    for (int l = 0; l < 8; ++l) {
+      const int t = l >> 1;
+      const uint32_t so = (uint32_t)(16 * tt(t) + 8 * (l & 1)) * kb2;
+      st.w[l] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128((GLU && t >= 2) ? w_hi : w_lo,
+                                                                                     vo, so, kNonTemporal));
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      const uint32_t so = (uint32_t)(16 * tt(t)) * ks32 + (uint32_t)d * 8;
+      st.sc[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64((GLU && t >= 2) ? s_hi : s_lo,
+                                                                                  sbase, so, 0));
+    }
+  };
+  auto fill_a = [&](int buf) {
+    *(u32x4_t*)(lds_a[buf] + afill0) = anext[0];
+    *(u32x4_t*)(lds_a[buf] + afill1) = anext[1];
+  };
+  auto consume = [&](const Stage& st, int buf) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t wf = *(const u32x4_t*)(lds + rlds[t][h]);
+    for (int l = 0; l < 8; ++l) *(u32x4_t*)(lds + l * 1024 + wbase) = st.w[l];
+    const uint8_t* at = lds_a[buf];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = *(const u32x4_t*)(at + h * 256 + aread[j]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4_t wf = *(const u32x4_t*)(lds + t * 2048 + (h ? rbase1 : rbase0));
         const uint32_t code = ((h ? st.sc[t].y : st.sc[t].x) >> (8 * q)) & 0xffu;
         const float sc = e8m0_as_f32_exponent(code);
 #pragma unroll
@@ -172,23 +175,33 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
           uint32_t bw[4];
           fp4x8_to_bf16x8(wf[j], sc, bw);
           const u32x4_t bv = {bw[0], bw[1], bw[2], bw[3]};
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[h][j]), as_bf16x8(bv), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x[j]), as_bf16x8(bv), acc[t], 0, 0, 0);
         }
       }
     }
   };
 
+  // Pipeline: step d's weights sit in registers and its activations in lds_a[d & 1] while
+  // step d+1's loads are in flight; one barrier per step publishes the next activation tile.
   const int nd = K >> 8;  // double steps (K is a multiple of 256)
   Stage s0, s1;
-  issue(s0, 0);
+  issue(s0, 0, true);
+  fill_a(0);
+  __syncthreads();
   int d = 0;
   for (; d + 2 <= nd; d += 2) {
-    issue(s1, d + 1);
-    consume(s0);
-    if (d + 2 < nd) issue(s0, d + 2);
-    consume(s1);
+    const bool more1 = d + 1 < nd;  // always true here
+    if (more1) issue(s1, d + 1, true);
+    consume(s0, d & 1);
+    if (more1) fill_a((d + 1) & 1);
+    __syncthreads();
+    const bool more2 = d + 2 < nd;
+    if (more2) issue(s0, d + 2, true);
+    consume(s1, (d + 1) & 1);
+    if (more2) fill_a((d + 2) & 1);
+    __syncthreads();
   }
-  if (d < nd) consume(s0);
+  if (d < nd) consume(s0, d & 1);
 
   // epilogue: lane holds D[m = 4q + r][n = nl] of each tile
   bool valid[4];
@@ -207,8 +220,8 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     for (int r = 0; r < 4; ++r) {
       if (!valid[r]) continue;
       if (GLU) {
-        const float h = glu_act(acc[t][r], acc[t + 2][r]);
-        ((uint16_t*)a.out)[(size_t)opos[r] * a.ldo + col] = (uint16_t)f32_to_bf16_bits(h);
+        const float hv = glu_act(acc[t][r], acc[t + 2][r]);
+        ((uint16_t*)a.out)[(size_t)opos[r] * a.ldo + col] = (uint16_t)f32_to_bf16_bits(hv);
       } else {
         ((float*)a.out)[(size_t)opos[r] * a.ldo + col] = acc[t][r];
       }
@@ -223,7 +236,9 @@ hipError_t launch_mx_small(const MxArgs& a, hipStream_t s) {
   const int cols_per_block = 4 * (glu ? 32 : 64);
   int bands[2] = {0, 0}, blocks[2] = {0, 0};
   for (int i = 0; i < a.nprob; ++i) {
-    bands[i] = (a.p[i].N + cols_per_block - 1) / cols_per_block;
+    // every wave of a block takes part in the block barriers: no partial column bands
+    if (a.p[i].N % cols_per_block || a.p[i].K % 256) return hipErrorInvalidValue;
+    bands[i] = a.p[i].N / cols_per_block;
     blocks[i] = a.p[i].max_blocks > 0 ? bands[i] * a.p[i].max_blocks : 0;
   }
   const long long total = (long long)blocks[0] + blocks[1];
