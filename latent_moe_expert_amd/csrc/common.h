@@ -61,3 +61,20 @@ __device__ __forceinline__ u32x4_t load_nt_u32x4(const void* p) {
   return __builtin_nontemporal_load((const u32x4_t*)p);
 }
 __device__ __forceinline__ u32x4_t load_u32x4(const void* p) { return *(const u32x4_t*)p; }
+
+// ---- buffer resources (raw buffers: an offset past num_records reads 0, with no memory access)
+constexpr uint32_t kOob = 0x80000000u;  // offset past any tensor the kernels index
+constexpr int kNonTemporal = 2;         // cache policy bit of once-read streams
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kNonTemporal));
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}

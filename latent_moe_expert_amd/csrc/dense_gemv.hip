@@ -19,13 +19,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 __device__ __forceinline__ void split3x2(float f0, float f1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   const uint32_t h0 = __float_as_uint(f0) & 0xffff0000u, h1 = __float_as_uint(f1) & 0xffff0000u;
   const float r0 = f0 - __uint_as_float(h0), r1 = f1 - __uint_as_float(h1);

@@ -36,19 +36,6 @@ namespace moe {
 
 namespace {
 
-constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any real tensor: reads 0
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-// Weight bytes are read exactly once: non-temporal, so that the stream does not push the
-// re-used lines (scales, activations) out of L2.
-constexpr int kNonTemporal = 2;
-
 template <bool GLU>
 __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0, int bands0, int bands1) {
   // per wave: an 8 KB weight tile; per block: two 8 KB activation tiles (16 slots x 256 K bf16)
