@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 1
+#define MOE_LATENT_ABI_VERSION 2
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, negative or inconsistent size */
@@ -46,11 +46,25 @@ extern "C" {
 #define MOE_EHIP (-5)         /* a HIP launch failed; moe_latent_last_hip_error() has the code */
 #define MOE_EABI (-6)         /* struct_size does not match this library */
 
+/* Expert contraction kernels (moe_latent_dims.expert_path).
+ *   MOE_PATH_STREAM: per 16-slot tile, weights streamed once per tile and
+ *     dequantised to bf16 for bf16 MFMAs; for decode-sized batches, where the
+ *     layer is bound by reading the touched experts' bytes.
+ *   MOE_PATH_MFMA: grouped GEMM on the scaled MXFP4 MFMA; the activations are
+ *     encoded per 32 values as two MXFP6 (E2M3) planes, hi and lo, whose sum
+ *     keeps about 8 significant bits; for prefill-sized batches. Needs hidden,
+ *     latent, inter and shared_inter to be multiples of 512.
+ *   MOE_PATH_AUTO: MFMA when its size rule holds and the batch averages at
+ *     least 32 token slots per expert (T*k >= 32*E), else STREAM. */
+#define MOE_PATH_AUTO 0
+#define MOE_PATH_STREAM 1
+#define MOE_PATH_MFMA 2
+
 /* Layer sizes. Limits checked by every call (else MOE_EUNSUPPORTED):
- * hidden, latent, inter, shared_inter multiples of 256; 1 <= n_experts <= 4096;
- * latent <= 8192; align_block 0 (library choice, 16) or a multiple of 16; the
- * expert-sorted intermediate (capacity x inter bf16) and x (T x hidden bf16)
- * below 2 GiB each. */
+ * hidden, latent, inter, shared_inter multiples of 256 (512 for MOE_PATH_MFMA);
+ * 1 <= n_experts <= 4096; latent <= 8192; align_block 0 (library choice, 16) or
+ * a multiple of 16; the expert-sorted intermediate (capacity x inter bf16) and
+ * x (T x hidden bf16) below 2 GiB each. */
 typedef struct moe_latent_dims {
   uint32_t struct_size;        /* = sizeof(moe_latent_dims) */
   int32_t T;                   /* tokens (0 is allowed: nothing is enqueued, pointers are not read) */
@@ -62,6 +76,7 @@ typedef struct moe_latent_dims {
   int32_t align_block;         /* B of the expert-sorted layout */
   float rms_eps;               /* RMSNorm epsilon (1e-6) */
   float routed_scaling_factor; /* 1.0 for K3 */
+  int32_t expert_path;         /* MOE_PATH_* */
 } moe_latent_dims;
 
 /* Router (WASTE page, "Shape" router row and "Against the technical report"). */

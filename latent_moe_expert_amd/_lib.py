@@ -8,6 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_latent.so")
 
 MOE_OK = 0
+PATH_AUTO, PATH_STREAM, PATH_MFMA = 0, 1, 2
 ERRORS = {-1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EALIAS", -4: "MOE_EWORKSPACE", -5: "MOE_EHIP",
           -6: "MOE_EABI"}
 
@@ -16,7 +17,7 @@ class MoeLatentDims(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("T", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("latent", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("align_block", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("routed_scaling_factor", ctypes.c_float)]
+                ("routed_scaling_factor", ctypes.c_float), ("expert_path", ctypes.c_int32)]
 
 
 class MoeRouter(ctypes.Structure):

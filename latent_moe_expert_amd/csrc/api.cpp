@@ -56,10 +56,18 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Plan {
   int T, H, L, E, I, Is, k, B, cap, pairs;
   bool small;      // T <= 64: split-K streaming projections
+  bool mfma;       // expert contractions on the scaled MFMA (MOE_PATH_MFMA)
+  int max_jobs;    // mfma: capacity of the job table
   int sz, sr, su;  // K slices of the down-projection, the router and the up-projection
   size_t z, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
-  size_t z_part, r_part, y_part, total;
+  size_t z_part, r_part, y_part;
+  size_t zq, zqs, xq, xqs, hq, hqs, hsq, hsqs, jobs, n_jobs;  // mfma: FP6 activations and the job table
+  size_t total;
 };
+
+bool mfma_sizes_ok(const moe_latent_dims* d) {
+  return d->hidden % 512 == 0 && d->latent % 512 == 0 && d->inter % 512 == 0 && d->shared_inter % 512 == 0;
+}
 
 // K slices of a split-K projection: about 8 row steps of 128 bytes per slice
 int slices(int K, int bytes_per_weight) {
@@ -78,6 +86,8 @@ int check_dims(const moe_latent_dims* d, int topk) {
   if (d->hidden % 256 || d->latent % 256 || d->inter % 256 || d->shared_inter % 256) return MOE_EUNSUPPORTED;
   if (d->n_experts > kMaxExperts || topk > kMaxTopk || d->latent > kMaxLatent) return MOE_EUNSUPPORTED;
   if (d->align_block % 16) return MOE_EUNSUPPORTED;
+  if (d->expert_path < MOE_PATH_AUTO || d->expert_path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if (d->expert_path == MOE_PATH_MFMA && !mfma_sizes_ok(d)) return MOE_EUNSUPPORTED;
   if ((long long)d->T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
   // activation tensors the kernels index with 32-bit byte offsets stay below 2 GiB
   {
@@ -100,6 +110,9 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.pairs = p.T * p.k;
   p.cap = moe::align_capacity(p.T, p.k, p.E, p.B);
   p.small = p.T <= 64;
+  p.mfma = d->expert_path == MOE_PATH_MFMA ||
+           (d->expert_path == MOE_PATH_AUTO && mfma_sizes_ok(d) && (long long)p.pairs >= 32ll * p.E);
+  p.max_jobs = p.mfma ? moe::mx_max_jobs(p.pairs, p.E, moe::kMfmaSlotsPerJob) : 0;
   p.sz = slices(p.H, 2);
   p.sr = slices(p.H, 4);
   p.su = slices(p.L, 2);
@@ -119,15 +132,26 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.num_post = take(4);
   p.inv_pos = take((size_t)p.pairs * 4);
   p.align_scratch = take(moe::align_scratch_bytes(p.T, p.E));
-  p.h = take((size_t)p.cap * p.I * 2);
+  p.h = take(p.mfma ? 0 : (size_t)p.cap * p.I * 2);
   p.O = take((size_t)p.cap * p.L * 4);
   p.cn = take((size_t)p.T * p.L * 2);
-  p.hs = take((size_t)p.T * p.Is * 2);
+  p.hs = take(p.mfma ? 0 : (size_t)p.T * p.Is * 2);
   p.ys = take((size_t)p.T * p.H * 4);
   const size_t ts = p.small ? (size_t)p.T : 0;
   p.z_part = take((size_t)p.sz * ts * p.L * 4);
   p.r_part = take((size_t)p.sr * ts * p.E * 4);
   p.y_part = take((size_t)p.su * ts * p.H * 4);
+  const size_t tq = p.mfma ? (size_t)p.T : 0, cq = p.mfma ? (size_t)p.cap : 0;
+  p.zq = take(tq * p.L * 3 / 2);
+  p.zqs = take(tq * p.L / 16);
+  p.xq = take(p.Is ? tq * p.H * 3 / 2 : 0);
+  p.xqs = take(p.Is ? tq * p.H / 16 : 0);
+  p.hq = take(cq * p.I * 3 / 2);
+  p.hqs = take(cq * p.I / 16);
+  p.hsq = take(tq * p.Is * 3 / 2);
+  p.hsqs = take(tq * p.Is / 16);
+  p.jobs = take((size_t)p.max_jobs * 16);
+  p.n_jobs = take(p.mfma ? 4 : 0);
   p.total = o;
   return p;
 }
@@ -290,11 +314,113 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
   // a3: moe_align_block_size
   MOE_HIP(moe::launch_align(ids, p.T, p.k, p.E, p.B, counts, sorted, expert_ids, num_post, inv_pos,
                             at<void>(ws, p.align_scratch), s));
+  if (p.mfma)
+    MOE_HIP(moe::launch_mx_jobs(counts, p.E, p.B, moe::kMfmaSlotsPerJob, at<int4>(ws, p.jobs),
+                                at<int32_t>(ws, p.n_jobs), s));
   STAGE_MARK(3);
   // a4 + a5 (and a10's gate/up): GLU contractions. The shared experts' blocks go
   // first in the same launch, so their long K rows overlap the routed work.
   const size_t gu_bytes = (size_t)p.I * p.L / 2, gu_scales = (size_t)p.I * p.L / 32;
   const size_t sgu = (size_t)p.Is * p.H / 2, sgs = (size_t)p.Is * p.H / 32;
+  if (p.mfma) {
+    // FP6 hi/lo encodings of the contraction inputs
+    uint8_t* zq = at<uint8_t>(ws, p.zq);
+    uint8_t* zqs = at<uint8_t>(ws, p.zqs);
+    uint8_t* xq = at<uint8_t>(ws, p.xq);
+    uint8_t* xqs = at<uint8_t>(ws, p.xqs);
+    uint8_t* hq = at<uint8_t>(ws, p.hq);
+    uint8_t* hqs = at<uint8_t>(ws, p.hqs);
+    uint8_t* hsq = at<uint8_t>(ws, p.hsq);
+    uint8_t* hsqs = at<uint8_t>(ws, p.hsqs);
+    const int4* jobs = at<int4>(ws, p.jobs);
+    const int32_t* n_jobs = at<int32_t>(ws, p.n_jobs);
+    MOE_HIP(moe::launch_quant_fp6(z, p.L, p.T, p.L, zq, zqs, s));
+    if (shared) MOE_HIP(moe::launch_quant_fp6((const uint16_t*)x, p.H, p.T, p.H, xq, xqs, s));
+    {
+      moe::MfmaArgs m{};
+      int n = 0;
+      if (shared) {
+        moe::MfmaProblem& g = m.p[n++];
+        g.Aq = xq;
+        g.Aqs = xqs;
+        g.a_rows = p.T;
+        g.routed = 0;
+        g.M = p.T;
+        g.W = shared->packed;
+        g.S = shared->scales;
+        g.W2 = shared->packed + sgu;
+        g.S2 = shared->scales + sgs;
+        g.N = p.Is;
+        g.K = p.H;
+        g.outq = hsq;
+        g.outqs = hsqs;
+      }
+      moe::MfmaProblem& g = m.p[n++];
+      g.Aq = zq;
+      g.Aqs = zqs;
+      g.a_rows = p.T;
+      g.routed = 1;
+      g.a_by_pos = 0;
+      g.sorted_ids = sorted;
+      g.topk = p.k;
+      g.jobs = jobs;
+      g.n_jobs = n_jobs;
+      g.max_jobs = p.max_jobs;
+      g.W = experts_packed;
+      g.S = experts_scales;
+      g.W2 = experts_packed + gu_bytes;
+      g.S2 = experts_scales + gu_scales;
+      g.w_stride = 3 * gu_bytes;
+      g.s_stride = 3 * gu_scales;
+      g.N = p.I;
+      g.K = p.L;
+      g.outq = hq;
+      g.outqs = hqs;
+      m.nprob = n;
+      MOE_HIP(moe::launch_mx_mfma(m, s));
+    }
+    STAGE_MARK(4);
+    {
+      moe::MfmaArgs m{};
+      int n = 0;
+      if (shared) {
+        moe::MfmaProblem& dn = m.p[n++];
+        dn.Aq = hsq;
+        dn.Aqs = hsqs;
+        dn.a_rows = p.T;
+        dn.routed = 0;
+        dn.M = p.T;
+        dn.W = shared->packed + 2 * sgu;
+        dn.S = shared->scales + 2 * sgs;
+        dn.N = p.H;
+        dn.K = p.Is;
+        dn.outf = ys;
+        dn.ldo = p.H;
+      }
+      moe::MfmaProblem& g = m.p[n++];
+      g.Aq = hq;
+      g.Aqs = hqs;
+      g.a_rows = p.cap;
+      g.routed = 1;
+      g.a_by_pos = 1;
+      g.sorted_ids = sorted;
+      g.topk = p.k;
+      g.jobs = jobs;
+      g.n_jobs = n_jobs;
+      g.max_jobs = p.max_jobs;
+      g.W = experts_packed + 2 * gu_bytes;
+      g.S = experts_scales + 2 * gu_scales;
+      g.w_stride = 3 * gu_bytes;
+      g.s_stride = 3 * gu_scales;
+      g.N = p.L;
+      g.K = p.I;
+      g.outf = O;
+      g.ldo = p.L;
+      m.nprob = n;
+      MOE_HIP(moe::launch_mx_mfma(m, s));
+    }
+    STAGE_MARK(5);
+  } else {
   {
     moe::MxArgs m{};
     int n = 0;
@@ -382,6 +508,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     MOE_HIP(moe::launch_mx_small(m, s));
   }
   STAGE_MARK(5);
+  }
   // a7 + a8: weighted combine and RMSNorm
   MOE_HIP(moe::launch_combine_norm(O, p.L, inv_pos, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
                                    taps ? taps->c : nullptr, cn, s));

@@ -115,6 +115,49 @@ struct MxArgs {
 
 hipError_t launch_mx_small(const MxArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- MXFP6 activations (scaled-MFMA path)
+// bf16 [rows, lda] -> FP6 E2M3 hi/lo tensor of rows of K values (layout in mxfp6.h); K % 512 == 0
+hipError_t launch_quant_fp6(const uint16_t* A, int lda, int rows, int K, uint8_t* data, uint8_t* scales,
+                            hipStream_t s);
+
+// Work list of the grouped MFMA contraction: one job per chunk of at most `slots_per_job`
+// token slots of one expert, in the expert-sorted layout with block B.
+// jobs[j] = {first slot, valid slots, expert, 0}; *n_jobs = number of jobs.
+int mx_max_jobs(int pairs, int E, int slots_per_job);
+hipError_t launch_mx_jobs(const int32_t* counts, int E, int B, int slots_per_job, int4* jobs, int32_t* n_jobs,
+                          hipStream_t s);
+
+// Grouped MXFP4 contraction on the scaled MFMA: A = FP6 hi/lo activations, B = MXFP4 weights.
+struct MfmaProblem {
+  const uint8_t* Aq;          // FP6 data of the A rows (row stride 1.5*K bytes)
+  const uint8_t* Aqs;         // FP6 scales (row stride K/16 bytes)
+  int a_rows;                 // rows of the A tensor (bounds its buffer resources)
+  int routed;                 // 1: jobs from the table below; 0: dense rows 0..M-1
+  int a_by_pos;               // routed: A row = slot position; else sorted_ids[slot] / topk
+  const int32_t* sorted_ids;  // routed
+  int topk;
+  const int4* jobs;           // routed
+  const int32_t* n_jobs;      // routed, device scalar
+  int max_jobs;               // routed: capacity of the job table
+  int M;                      // dense rows
+  const uint8_t* W;           // MXFP4 [N, K/2] of expert e at W + e*w_stride (GLU: gate)
+  const uint8_t* S;           // E8M0 [N, K/32]
+  const uint8_t* W2;          // GLU: up matrix; null for a plain contraction
+  const uint8_t* S2;
+  size_t w_stride, s_stride;
+  int N, K;                   // GLU: N = h width, multiple of 512; plain: N multiple of 256; K multiple of 512
+  uint8_t* outq;              // GLU: FP6 h rows (routed: slot position, dense: row), width N
+  uint8_t* outqs;
+  float* outf;                // plain: fp32 [row, ldo] (routed: slot position)
+  int ldo;
+};
+struct MfmaArgs {
+  MfmaProblem p[2];
+  int nprob;                  // both GLU or both plain; problem 0's blocks first
+};
+constexpr int kMfmaSlotsPerJob = 192;  // 12 MFMA row tiles of 16
+hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- combine + norm
 hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
                                const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);

@@ -1,0 +1,447 @@
+// Grouped MXFP4 contractions on gfx950's scaled MFMA (prefill-sized token counts).
+//
+// Each routed expert holds its tokens' rows contiguously in the expert-sorted
+// layout (moe_align_block_size, pages: "Kimi K3, as released", tensor listing;
+// the vLLM-style align block). A job is one chunk of at most 192 slots of one
+// expert; a block computes one job against one 256-row tile of the expert's
+// weights with the full K, so every weight byte is read from HBM once per chunk,
+// and almost every expert of an 8192-token batch fits in one chunk.
+//
+// Operands. v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a 16x128 A tile by a
+// 128x16 B tile, each lane holding 32 consecutive K values of one row (lane
+// group q = lane/16 owns K block q) and one E8M0 scale for them. The weights are
+// the B operand straight from their shipped layout: a lane's 32 weights are one
+// E8M0 group, 16 bytes of a row, so the MXFP4 bytes and their scale bytes go
+// into the MFMA unchanged. The activations are the A operand in the FP6 E2M3
+// hi/lo encoding (mxfp6.h); hi and lo each take one MFMA at the FP4 rate.
+//
+// K order. Within a window of 16 groups (512 K values), k-step s gives lane
+// group q the group 4q + s. Then each lane's weight bytes for the window are one
+// 64-byte run of its row, and each lane's four scales are one aligned dword
+// (opsel s picks the byte), for weights and activations alike.
+//
+// Dataflow per block (4 waves, 1 per SIMD). The A rows of a k-step (192 rows x
+// 192 bytes, gathered through the sorted token ids) go to LDS by LDS-DMA loads
+// (no registers), into a ring of four stages, three k-steps ahead of their use;
+// every wave reads all of them, one barrier per k-step. Each wave owns 64 weight
+// rows (GLU: 32 gate + the same 32 up rows) and loads them straight into MFMA
+// registers, one window ahead; weights are read once, so those loads are
+// non-temporal. Blocks of one job are adjacent in the grid order of one XCD, so
+// the job's activation rows are served from that XCD's L2.
+//
+// Waits. vmcnt retires loads in issue order, so waiting for a stage also waits
+// for every load issued before it; the ring depth sets how old those loads are.
+// The waits are explicit counts (every k-step issues the same loads, none under
+// a runtime branch), and each ring stage is its own LDS array with a
+// compile-time index, so the compiler can tell that a stage being read is not
+// the target of the loads in flight.
+//
+// Epilogue. Plain: fp32 rows at the job's slot positions. GLU: h = act(gate)*up
+// goes through LDS and is written directly in the FP6 hi/lo encoding that the
+// down contraction reads.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+#include "mxfp6.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMF = kMfmaSlotsPerJob / 16;  // row tiles per job
+constexpr int kRows = kMfmaSlotsPerJob;     // 192
+constexpr int kArow = 192;                  // LDS bytes per staged row (12 chunks of 16 B, rotated)
+constexpr int kAStage = kRows * kArow;      // bytes per A stage (sized for the largest job)
+constexpr int kSDma = 2;                    // 16-byte scale chunks per thread per window
+constexpr int kSStage = kSDma * 256 * 16;
+constexpr int kHRow = 132;                  // floats per row of the GLU epilogue tile
+constexpr int kHTiles = 3;                  // row tiles per epilogue pass
+static_assert(kRows * 2 <= kSDma * 256, "scale chunks");
+static_assert(kHTiles * 16 * kHRow * 4 <= kAStage, "GLU epilogue tile must fit a stage");
+static_assert(4 * kAStage + kSStage <= 160 * 1024, "LDS");
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at 15:14)
+#define MOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | ((((n) >> 4) & 3) << 14))
+
+// Workgroup barrier of the ring. Each wave establishes completion of its own
+// LDS-DMA loads with an explicit vmcnt wait first; __syncthreads() would wait for
+// every outstanding load. The empty asm statements keep the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
+                                           0, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
+
+// LDS position of 16-byte chunk c of a staged row whose index within its 16-row tile is
+// nl: rotating the chunks by nl/4 makes the MFMA fragment reads (16 rows x 24 bytes per
+// lane group) bank-conflict free.
+__host__ __device__ constexpr int a_chunk_pos(int c, int nl) { return (c + nl / 4) % 12; }
+
+// One job (at most NT row tiles of 16) against one column tile. NT is a compile-time
+// bucket of the job's row count: every loop below is straight-line code, so each
+// k-step issues a fixed set of loads and the compiler's waits are exact.
+template <bool GLU, int NT>
+__device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nvalid, int expert, int ntile,
+                                       uint8_t (&lds_a0)[kAStage + kSStage], uint8_t (&lds_a1)[kAStage],
+                                       uint8_t (&lds_a2)[kAStage], uint8_t (&lds_a3)[kAStage]) {
+  constexpr int kADma = (NT * 16 * 12 + 255) / 256;  // 16-byte LDS-DMA chunks per thread per k-step
+  static_assert(kADma * 256 * 16 <= kAStage, "stage");
+  auto stage = [&](auto I_) -> uint8_t* {
+    constexpr int I = decltype(I_)::value % 4;
+    if constexpr (I == 0) return lds_a0;
+    else if constexpr (I == 1) return lds_a1;
+    else if constexpr (I == 2) return lds_a2;
+    else return lds_a3;
+  };
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int nl = lane & 15, q = lane >> 4;
+
+  const int K = a.K;
+  const uint32_t arow_bytes = (uint32_t)fp6_row_bytes(K), asrow_bytes = (uint32_t)fp6_scale_row_bytes(K);
+  auto a_row = [&](int j) -> int {  // A row of job slot j, -1 past the valid slots
+    if (j >= nvalid) return -1;
+    if (!a.routed || a.a_by_pos) return first + j;
+    return a.sorted_ids[first + j] / a.topk;
+  };
+
+  // ---- A stage by LDS-DMA: chunk t = tid + 256 i lands at LDS byte 16 t, i.e. position t % 12
+  // of staged row j = t / 12, and carries the row's global chunk whose rotated position that is.
+  uint32_t goff[kADma];
+#pragma unroll
+  for (int i = 0; i < kADma; ++i) {
+    const int t = tid + 256 * i, j = t / 12, pos = t % 12;
+    const int c = (pos + 12 - (j & 15) / 4) % 12;
+    const int r = j < NT * 16 ? a_row(j) : -1;
+    goff[i] = r >= 0 ? (uint32_t)r * arow_bytes + 16u * c : kOob;
+  }
+  uint32_t sgoff[kSDma];
+#pragma unroll
+  for (int i = 0; i < kSDma; ++i) {
+    const int t = tid + 256 * i, j = t >> 1, c = t & 1;
+    const int r = j < NT * 16 ? a_row(j) : -1;
+    sgoff[i] = r >= 0 ? (uint32_t)r * asrow_bytes + 16u * c : kOob;
+  }
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a.Aq, (uint32_t)a.a_rows * arow_bytes);
+  const __amdgpu_buffer_rsrc_t as_rs = make_rsrc(a.Aqs, (uint32_t)a.a_rows * asrow_bytes);
+
+  // ---- weights: wave rows, lane (nl, q) of B tile nf reads row rows(nf) + nl
+  const uint32_t kb2 = (uint32_t)K / 2, ks32 = (uint32_t)K / 32;
+  const uint32_t mat_bytes = (uint32_t)a.N * kb2, mat_scales = (uint32_t)a.N * ks32;
+  const __amdgpu_buffer_rsrc_t w_lo = make_rsrc(a.W + (size_t)expert * a.w_stride, mat_bytes);
+  const __amdgpu_buffer_rsrc_t s_lo = make_rsrc(a.S + (size_t)expert * a.s_stride, mat_scales);
+  const __amdgpu_buffer_rsrc_t w_hi = GLU ? make_rsrc(a.W2 + (size_t)expert * a.w_stride, mat_bytes) : w_lo;
+  const __amdgpu_buffer_rsrc_t s_hi = GLU ? make_rsrc(a.S2 + (size_t)expert * a.s_stride, mat_scales) : s_lo;
+  const int row0 = GLU ? ntile * 128 + wave * 32 : ntile * 256 + wave * 64;
+  uint32_t bvoff[4], svoff[4];
+#pragma unroll
+  for (int nf = 0; nf < 4; ++nf) {
+    const uint32_t row = (uint32_t)(row0 + 16 * (GLU ? (nf & 1) : nf) + nl);
+    bvoff[nf] = row * kb2 + 64u * q;
+    svoff[nf] = row * ks32 + 4u * q;
+  }
+
+  // A load that is not needed (past the last k-step or window) goes to a zero-size
+  // resource: it reads zeros without touching memory, and the load count stays fixed.
+  // The weight loads keep the default cache policy: the four k-steps of a window read
+  // interleaved 16-byte pieces of the same lines, which must survive in L2 between them.
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(a.W, 0u);
+  u32x4_t b[4][4];  // [k-step in window][B tile]
+  uint32_t sb[4], sbn[4];
+  auto load_b = [&](int w, int s, bool on) {  // 4 loads
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+      b[s][nf] = buf_load16(on ? ((GLU && nf >= 2) ? w_hi : w_lo) : none, bvoff[nf], (uint32_t)(256 * w + 16 * s));
+  };
+  auto load_sb = [&](int w, uint32_t* dst, bool on) {  // 4 loads
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+      dst[nf] = buf_load4(on ? ((GLU && nf >= 2) ? s_hi : s_lo) : none, svoff[nf], (uint32_t)(16 * w));
+  };
+  auto dma_a = [&](uint8_t* st, int ks, bool on) {  // kADma loads
+#pragma unroll
+    for (int i = 0; i < kADma; ++i)
+      dma16(on ? a_rs : none, st + wave * 1024 + i * 4096, goff[i], (uint32_t)(ks * kFp6StepBytes));
+  };
+  auto dma_s = [&](int w, bool on) {  // kSDma loads
+    uint8_t* st = lds_a0 + kAStage;
+#pragma unroll
+    for (int i = 0; i < kSDma; ++i)
+      dma16(on ? as_rs : none, st + wave * 1024 + i * 4096, sgoff[i], (uint32_t)(w * kFp6WindowScaleBytes));
+  };
+
+  f32x4_t acc[NT][4];
+#pragma unroll
+  for (int mf = 0; mf < NT; ++mf)
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // lane (nl, q) reads, per plane p, the 3 eight-byte units of its 24-byte piece
+  uint32_t aoff[2][3];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int gb = p * 96 + q * 24 + 8 * u;
+      aoff[p][u] = (uint32_t)(nl * kArow + a_chunk_pos(gb / 16, nl) * 16 + gb % 16);
+    }
+  uint32_t sA[NT][2];
+
+  auto read_a = [&](const uint8_t* st, int mf, i32x8_t* av) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint8_t* base = st + mf * 16 * kArow;
+      const uint2 x0 = *(const uint2*)(base + aoff[p][0]);
+      const uint2 x1 = *(const uint2*)(base + aoff[p][1]);
+      const uint2 x2 = *(const uint2*)(base + aoff[p][2]);
+      av[p] = i32x8_t{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, (int)x2.x, (int)x2.y, 0, 0};
+    }
+  };
+  // Tile mf's MFMAs run while tile mf+1's operands are read; the barriers per tile keep
+  // the compiler from hoisting all tiles' reads (12 tiles would need 144 registers).
+  // Two register sets, picked by tile parity, so no operand is copied.
+  auto compute = [&](auto S_, const uint8_t* st) {
+    constexpr int S = decltype(S_)::value;
+    i32x8_t av[2][2];  // [row tile parity][plane]
+    read_a(st, 0, av[0]);
+#pragma unroll
+    for (int mf = 0; mf < NT; ++mf) {
+      if (mf + 1 < NT) read_a(st, mf + 1, av[(mf + 1) & 1]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          const u32x4_t bw = b[S][nf];
+          const i32x8_t bv = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
+          acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mf & 1][p], bv, acc[mf][nf], 2, 4, S,
+                                                                          (int)sA[mf][p], S, (int)sb[nf]);
+        }
+      // The memory clobber pins the LDS reads (IR passes may move loads across the
+      // scheduling barrier, which touches no memory); the scheduling barrier then keeps
+      // the MFMAs between them.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Pipeline. K-step ks (window w = ks/4, step S = ks%4) uses A stage S. Each k-step
+  // issues, in order: at S == 1 the activation scales of window w+1 (kSDma loads into
+  // stage 0's scale area), the A stage of ks+3 (kADma loads into stage (S+3)%4, read by
+  // k-step ks-1), the MFMAs of ks, the weights of k-step ks+4 (4 loads) and at S == 0
+  // the weight scales of window w+1 (4). Before the barrier that ends k-step ks, the A
+  // stage of ks+1 (issued in k-step ks-2) must be complete, and with it everything
+  // issued before it; the loads issued after it may stay in flight.
+  const int nw = K >> 9;
+  const int nks = nw * 4;
+  constexpr int kStepLoads[4] = {kADma + 8, kSDma + kADma + 4, kADma + 4, kADma + 4};  // by S
+  constexpr int kStepTail[4] = {8, 4, 4, 4};  // loads of a k-step issued after its A stage
+  // Prologue: scales of window 0, A stage 0, then the weights of window 0 interleaved
+  // with A stages 1 and 2 so that, as in the steady state, tail(2) + loads(3) loads
+  // follow stage 1 and tail(3) follow stage 2: the first two k-steps then need no
+  // wait counts of their own (a runtime branch there would split the window body).
+  static_assert(kStepTail[2] + kStepLoads[3] == 8 + kADma && kStepTail[3] == 4, "prologue order");
+  dma_s(0, true);
+  dma_a(stage(ic<0>{}), 0, true);
+  load_b(0, 0, true);
+  load_b(0, 1, true);
+  load_sb(0, sb, true);
+  dma_a(stage(ic<1>{}), 1, nks > 1);
+  load_b(0, 2, true);
+  dma_a(stage(ic<2>{}), 2, nks > 2);
+  load_b(0, 3, true);
+  MOE_WAIT_VM_LGKM0(20 + 2 * kADma);  // scales 0 and stage 0 complete
+  ring_barrier();
+
+  for (int w = 0; w < nw; ++w) {
+    {
+      const uint8_t* ss = lds_a0 + kAStage + nl * kFp6WindowScaleBytes + q * 4;
+#pragma unroll
+      for (int mf = 0; mf < NT; ++mf)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) sA[mf][p] = *(const uint32_t*)(ss + mf * 16 * kFp6WindowScaleBytes + p * 16);
+    }
+    const bool more_w = w + 1 < nw;
+    auto step = [&](auto S_) {
+      constexpr int S = decltype(S_)::value;
+      const int ks = 4 * w + S;
+      if (S == 1) dma_s(w + 1, more_w);
+      dma_a(stage(ic<S + 3>{}), ks + 3, ks + 3 < nks);
+      compute(S_, stage(S_));
+      load_b(w + 1, S, more_w);
+      if (S == 0) load_sb(w + 1, sbn, more_w);
+      // loads issued after the A stage of ks+1: tail of ks-2, all of ks-1 and ks
+      MOE_WAIT_VM_LGKM0(kStepTail[(S + 2) % 4] + kStepLoads[(S + 3) % 4] + kStepLoads[S]);
+      ring_barrier();
+    };
+    step(ic<0>{});
+    step(ic<1>{});
+    step(ic<2>{});
+    step(ic<3>{});
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) sb[nf] = sbn[nf];
+  }
+  // the last k-steps issued zero-filling stage loads into the ring: drain them before reuse
+  MOE_WAIT_VM_LGKM0(0);
+  ring_barrier();
+
+  if (!GLU) {
+    const int col0 = row0;
+#pragma unroll
+    for (int mf = 0; mf < NT; ++mf) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * mf + 4 * q + r;
+        if (j < nvalid) {
+          float* o = a.outf + (size_t)(first + j) * a.ldo + col0 + nl;
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf) o[16 * nf] = acc[mf][nf][r];
+        }
+      }
+    }
+  } else {
+    // h tile through LDS, 48 rows per pass, then one thread per (row, group of 32)
+    float* hs = (float*)lds_a0;
+    const uint32_t orow_bytes = (uint32_t)fp6_row_bytes(a.N), osrow_bytes = (uint32_t)fp6_scale_row_bytes(a.N);
+#pragma unroll
+    for (int pass = 0; pass < (NT + kHTiles - 1) / kHTiles; ++pass) {
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < kHTiles; ++mt) {
+        const int mf = pass * kHTiles + mt;
+        if (mf < NT) {
+#pragma unroll
+          for (int nf = 0; nf < 2; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              hs[(16 * mt + 4 * q + r) * kHRow + wave * 32 + 16 * nf + nl] =
+                  glu_act(acc[mf][nf][r], acc[mf][nf + 2][r]);
+        }
+      }
+      __syncthreads();
+      const int jl = tid >> 2, g4 = tid & 3;
+      const int j = pass * kHTiles * 16 + jl;
+      if (jl < kHTiles * 16 && j < nvalid) {
+        float v[32];
+        const f32x4_t* src = (const f32x4_t*)(hs + jl * kHRow + 32 * g4);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const f32x4_t x = src[u];
+          v[4 * u] = x[0];
+          v[4 * u + 1] = x[1];
+          v[4 * u + 2] = x[2];
+          v[4 * u + 3] = x[3];
+        }
+        uint32_t hi[6], lo[6], s_hi, s_lo;
+        fp6_encode_group(v, hi, lo, s_hi, s_lo);
+        const int g = ntile * 4 + g4;
+        uint8_t* drow = a.outq + (size_t)(first + j) * orow_bytes;
+        uint2* dh = (uint2*)(drow + fp6_data_offset(g, 0));
+        uint2* dl = (uint2*)(drow + fp6_data_offset(g, 1));
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          dh[u] = make_uint2(hi[2 * u], hi[2 * u + 1]);
+          dl[u] = make_uint2(lo[2 * u], lo[2 * u + 1]);
+        }
+        uint8_t* srow = a.outqs + (size_t)(first + j) * osrow_bytes;
+        srow[fp6_scale_offset(g, 0)] = (uint8_t)s_hi;
+        srow[fp6_scale_offset(g, 1)] = (uint8_t)s_lo;
+      }
+    }
+  }
+}
+
+template <bool GLU>
+__global__ __launch_bounds__(256) void mx_mfma_kernel(MfmaArgs args) {
+  // stage 0 also holds the activation scales of its window (its k-step starts the window)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kAStage + kSStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a1[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a2[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a3[kAStage];
+
+  // ---- block -> (problem, job, column tile)
+  int nb0, nb1 = 0, nt0, nt1 = 1;
+  {
+    const MfmaProblem& p = args.p[0];
+    nt0 = p.N / (GLU ? 128 : 256);
+    nb0 = (p.routed ? *p.n_jobs : (p.M + kRows - 1) / kRows) * nt0;
+  }
+  if (args.nprob > 1) {
+    const MfmaProblem& p = args.p[1];
+    nt1 = p.N / (GLU ? 128 : 256);
+    nb1 = (p.routed ? *p.n_jobs : (p.M + kRows - 1) / kRows) * nt1;
+  }
+  const int total = nb0 + nb1;
+  const int per = (total + 7) >> 3;  // logical blocks per XCD (grid position mod 8)
+  const int lb = (int)blockIdx.x >> 3;
+  if (lb >= per) return;
+  const int L = ((int)blockIdx.x & 7) * per + lb;
+  if (L >= total) return;
+  const bool second = L >= nb0;
+  const MfmaProblem& a = args.p[second ? 1 : 0];
+  const int local = second ? L - nb0 : L;
+  const int nt = second ? nt1 : nt0;
+  const int job = local / nt, ntile = local % nt;
+  int first, nvalid, expert = 0;
+  if (a.routed) {
+    const int4 jb = a.jobs[job];
+    first = jb.x;
+    nvalid = jb.y;
+    expert = jb.z;
+  } else {
+    first = job * kRows;
+    nvalid = min(kRows, a.M - first);
+  }
+  const int nmf = (nvalid + 15) >> 4;
+  if (nmf <= 4)
+    mx_job<GLU, 4>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+  else if (nmf <= 8)
+    mx_job<GLU, 8>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+  else if (nmf <= 10)
+    mx_job<GLU, 10>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+  else
+    mx_job<GLU, kMF>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+}
+
+}  // namespace
+
+hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
+  if (a.nprob < 1 || a.nprob > 2) return hipErrorInvalidValue;
+  const bool glu = a.p[0].W2 != nullptr;
+  long long blocks = 0;
+  for (int i = 0; i < a.nprob; ++i) {
+    const MfmaProblem& p = a.p[i];
+    if ((p.W2 != nullptr) != glu || p.K % 512 || p.K <= 0) return hipErrorInvalidValue;
+    // GLU blocks cover 128 h columns and write whole FP6 windows of h; plain blocks cover 256 columns
+    if (glu ? (p.N % 512) : (p.N % 256)) return hipErrorInvalidValue;
+    // 32-bit byte offsets: activations, weights of one matrix, outputs
+    if (p.a_rows < 0 || (long long)p.a_rows * (long long)fp6_row_bytes(p.K) >= (1ll << 31) ||
+        (long long)p.N * p.K / 2 >= (1ll << 31) || (!p.routed && p.M > p.a_rows))
+      return hipErrorInvalidValue;
+    const long long jobs = p.routed ? p.max_jobs : (p.M + kRows - 1) / kRows;
+    blocks += jobs * (p.N / (glu ? 128 : 256));
+  }
+  if (blocks == 0) return hipSuccess;
+  const long long grid = (blocks + 7) / 8 * 8;
+  if (grid > 0x7fffffffll) return hipErrorInvalidValue;
+  if (glu)
+    hipLaunchKernelGGL(mx_mfma_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(mx_mfma_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+// Activation encoding for the scaled-MFMA contractions, and their work list.
+#include "common.h"
+#include "kernels.h"
+#include "mxfp6.h"
+
+namespace moe {
+
+namespace {
+
+// One thread per group of 32 values: 64 bytes in, 2 x 24 bytes and 2 scale bytes out.
+__global__ __launch_bounds__(256) void quant_fp6_kernel(const uint16_t* __restrict__ A, int lda, int rows, int K,
+                                                        uint8_t* __restrict__ data, uint8_t* __restrict__ scales) {
+  const int G = K >> 5;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)rows * G) return;
+  const int row = (int)(idx / G), g = (int)(idx % G);
+  const u32x4_t* src = (const u32x4_t*)(A + (size_t)row * lda + (size_t)g * 32);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t x = src[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * j + 2 * e] = bf16_bits_to_f32(x[e] & 0xffffu);
+      v[8 * j + 2 * e + 1] = bf16_bits_to_f32(x[e] >> 16);
+    }
+  }
+  uint32_t hi[6], lo[6], s_hi, s_lo;
+  fp6_encode_group(v, hi, lo, s_hi, s_lo);
+  uint8_t* drow = data + (size_t)row * fp6_row_bytes(K);
+  uint2* dh = (uint2*)(drow + fp6_data_offset(g, 0));
+  uint2* dl = (uint2*)(drow + fp6_data_offset(g, 1));
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    dh[j] = make_uint2(hi[2 * j], hi[2 * j + 1]);
+    dl[j] = make_uint2(lo[2 * j], lo[2 * j + 1]);
+  }
+  uint8_t* srow = scales + (size_t)row * fp6_scale_row_bytes(K);
+  srow[fp6_scale_offset(g, 0)] = (uint8_t)s_hi;
+  srow[fp6_scale_offset(g, 1)] = (uint8_t)s_lo;
+}
+
+// Single block: per-expert padded segment offsets (the align layout) and job counts,
+// scanned in expert order, then one job per chunk of at most spj valid slots.
+constexpr int kJobThreads = 1024;
+
+__global__ __launch_bounds__(kJobThreads) void mx_jobs_kernel(const int32_t* __restrict__ counts, int E, int B,
+                                                             int spj, int4* __restrict__ jobs,
+                                                             int32_t* __restrict__ n_jobs) {
+  __shared__ int s_pad[kJobThreads];
+  __shared__ int s_job[kJobThreads];
+  const int tid = threadIdx.x;
+  const int per = (E + kJobThreads - 1) / kJobThreads;  // experts per thread, contiguous
+  const int e0 = tid * per;
+  int pad = 0, nj = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = counts[e];
+    pad += (c + B - 1) / B * B;
+    nj += (c + spj - 1) / spj;
+  }
+  s_pad[tid] = pad;
+  s_job[tid] = nj;
+  __syncthreads();
+  // inclusive scan (Hillis-Steele), then shift to exclusive
+  for (int o = 1; o < kJobThreads; o <<= 1) {
+    const int a = tid >= o ? s_pad[tid - o] : 0;
+    const int b = tid >= o ? s_job[tid - o] : 0;
+    __syncthreads();
+    s_pad[tid] += a;
+    s_job[tid] += b;
+    __syncthreads();
+  }
+  int slot = s_pad[tid] - pad, job = s_job[tid] - nj;
+  if (tid == kJobThreads - 1) *n_jobs = s_job[tid];
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = counts[e];
+    for (int f = 0; f < c; f += spj) jobs[job++] = make_int4(slot + f, min(spj, c - f), e, 0);
+    slot += (c + B - 1) / B * B;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp6(const uint16_t* A, int lda, int rows, int K, uint8_t* data, uint8_t* scales,
+                            hipStream_t s) {
+  if (K % 512 || lda % 8 || rows < 0) return hipErrorInvalidValue;
+  const long long groups = (long long)rows * (K / 32);
+  if (groups == 0) return hipSuccess;
+  const long long blocks = (groups + 255) / 256;
+  if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_fp6_kernel, dim3((unsigned)blocks), dim3(256), 0, s, A, lda, rows, K, data, scales);
+  return hipGetLastError();
+}
+
+int mx_max_jobs(int pairs, int E, int slots_per_job) {
+  // sum_e ceil(c_e / spj) <= sum_e (c_e / spj) + #{e : c_e > 0}
+  return pairs / slots_per_job + (pairs < E ? pairs : E) + 1;
+}
+
+hipError_t launch_mx_jobs(const int32_t* counts, int E, int B, int slots_per_job, int4* jobs, int32_t* n_jobs,
+                          hipStream_t s) {
+  if (E < 1 || B < 1 || slots_per_job < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_jobs_kernel, dim3(1), dim3(kJobThreads), 0, s, counts, E, B, slots_per_job, jobs, n_jobs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -30,9 +30,10 @@ def _check(fn: str, rc: int) -> None:
 
 
 def make_dims(T: int, hidden: int, latent: int, n_experts: int, inter: int, shared_inter: int = 0,
-              align_block: int = 0, rms_eps: float = 1e-6, routed_scaling_factor: float = 1.0) -> MoeLatentDims:
+              align_block: int = 0, rms_eps: float = 1e-6, routed_scaling_factor: float = 1.0,
+              expert_path: int = 0) -> MoeLatentDims:
     return MoeLatentDims(ctypes.sizeof(MoeLatentDims), T, hidden, latent, n_experts, inter, shared_inter,
-                         align_block, rms_eps, routed_scaling_factor)
+                         align_block, rms_eps, routed_scaling_factor, expert_path)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "") -> Optional[int]:

@@ -63,16 +63,17 @@ class DeviceLayer:
             self.sh_packed = torch.from_numpy(sh[0]).to(dev)
             self.sh_scales = torch.from_numpy(sh[1]).to(dev)
 
-    def dims(self, T: int, align_block: int = 0):
+    def dims(self, T: int, align_block: int = 0, expert_path: int = 0):
         c = self.c
         return L.make_dims(T, c.hidden, c.latent, c.n_experts, c.inter, c.shared_inter, align_block, c.rms_eps,
-                           c.routed_scaling_factor)
+                           c.routed_scaling_factor, expert_path)
 
-    def run(self, x_bits: np.ndarray = None, x_dev: torch.Tensor = None, taps: bool = True, align_block: int = 0):
+    def run(self, x_bits: np.ndarray = None, x_dev: torch.Tensor = None, taps: bool = True, align_block: int = 0,
+            expert_path: int = 0):
         c = self.c
         x = to_dev_bf16(x_bits) if x_dev is None else x_dev
         T = x.shape[0]
-        dims = self.dims(T, align_block)
+        dims = self.dims(T, align_block, expert_path)
         ws = torch.empty(max(L.moe_latent_workspace_size(dims, c.topk), 256), dtype=torch.uint8, device=x.device)
         y = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=x.device)
         out = {}

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.moe_latent_abi_version() == 1
+    assert lib.moe_latent_abi_version() == 2
     for code in range(0, -7, -1):
         assert lib.moe_latent_strerror(code)
     assert lib.moe_latent_stage_count() == 9
@@ -43,7 +43,7 @@ def test_abi_version_and_strerror(lib):
 
 def _dims(**kw):
     base = dict(T=16, hidden=7168, latent=3584, n_experts=896, inter=3072, shared_inter=6144, align_block=0,
-                rms_eps=1e-6, routed_scaling_factor=1.0)
+                rms_eps=1e-6, routed_scaling_factor=1.0, expert_path=0)
     base.update(kw)
     d = _lib.MoeLatentDims(ctypes.sizeof(_lib.MoeLatentDims), *[base[f] for f, _ in _lib.MoeLatentDims._fields_[1:]])
     return d

@@ -29,13 +29,16 @@ def _harness():
     return gpu_harness
 
 
-def _run_small(c, align_block=0, dense=None, experts=None):
+PATH_STREAM, PATH_MFMA = 1, 2
+
+
+def _run_small(c, align_block=0, dense=None, experts=None, expert_path=0):
     H = _harness()
     d = li.build(c) if experts is None else experts
     dl = H.DeviceLayer(c, dense=dense if dense is not None else {k: d[k] for k in
                                                                   ("down", "up", "norm", "router", "select_bias")},
                        experts=(d["exp_packed"], d["exp_scales"]))
-    out = dl.run(d["x"], align_block=align_block)
+    out = dl.run(d["x"], align_block=align_block, expert_path=expert_path)
     ref = li.oracle_forward(c, {**d, **dl.host_dense}, align_block=out["B"])
     return out, ref, d
 
@@ -57,6 +60,50 @@ def test_small_layer_parity(name, kw):
     H = _harness()
     c = li.small_config(**kw)
     out, ref, _ = _run_small(c)
+    H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
+
+
+# The scaled-MFMA expert path: sizes multiples of 512, several K windows, experts split
+# into several jobs of at most 192 slots, ragged tails, dense shared rows over two jobs.
+MFMA_SMALL = [
+    ("two_windows", dict(T=96, hidden=1024, latent=1024, n_experts=8, topk=4, inter=1024, shared_inter=512)),
+    ("experts_over_192_slots_k_eq_E", dict(T=256, hidden=512, latent=512, n_experts=4, topk=4, inter=512,
+                                           shared_inter=512, norm=False)),
+    ("ragged_no_shared", dict(T=37, hidden=512, latent=512, n_experts=40, topk=6, inter=512, shared_inter=0)),
+    ("bias_rsf_three_windows", dict(T=200, hidden=512, latent=1536, n_experts=24, topk=5, inter=512,
+                                    shared_inter=1024, routed_scaling_factor=2.446, zipf_s=1.1, zipf_c=0.05)),
+]
+
+
+@pytest.mark.parametrize("name,kw", MFMA_SMALL, ids=[s[0] for s in MFMA_SMALL])
+def test_mfma_path_parity(name, kw):
+    H = _harness()
+    c = li.small_config(**kw)
+    out, ref, _ = _run_small(c, expert_path=PATH_MFMA)
+    H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
+
+
+def test_both_paths_on_one_input():
+    """The same layer through the streaming and the MFMA expert kernels: each within
+    the tolerance of the oracle."""
+    H = _harness()
+    c = li.small_config(T=64, hidden=512, latent=1024, n_experts=16, topk=4, inter=512, shared_inter=512)
+    d = li.build(c)
+    dl = H.DeviceLayer(c, dense={k: d[k] for k in ("down", "up", "norm", "router", "select_bias")},
+                       experts=(d["exp_packed"], d["exp_scales"]))
+    a = dl.run(d["x"], expert_path=PATH_STREAM)
+    b = dl.run(d["x"], expert_path=PATH_MFMA)
+    ref = li.oracle_forward(c, {**d, **dl.host_dense}, align_block=a["B"])
+    H.compare_layer(a, ref, c.T, c.topk, c.n_experts)
+    H.compare_layer(b, ref, c.T, c.topk, c.n_experts)
+
+
+def test_mfma_path_align_block_48():
+    """Jobs follow the expert segments of a B = 48 layout."""
+    H = _harness()
+    c = li.small_config(T=70, n_experts=9, topk=3, hidden=512, latent=512, inter=512, shared_inter=0)
+    out, ref, _ = _run_small(c, align_block=48, expert_path=PATH_MFMA)
+    assert out["B"] == 48
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
 
 
