@@ -62,6 +62,7 @@ struct Plan {
   size_t z, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
   size_t z_part, r_part, y_part;
   size_t zq, zqs, xq, xqs, hq, hqs, hsq, hsqs, jobs, n_jobs;  // mfma: FP6 activations and the job table
+  size_t wr3;      // T > 64: router weight split into three bf16 planes [E, 3H]
   size_t total;
 };
 
@@ -152,6 +153,7 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.hsqs = take(tq * p.Is / 16);
   p.jobs = take((size_t)p.max_jobs * 16);
   p.n_jobs = take(p.mfma ? 4 : 0);
+  p.wr3 = take(p.small ? 0 : (size_t)p.E * 3 * p.H * 2);
   p.total = o;
   return p;
 }
@@ -279,15 +281,16 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     g.seg[1] = {router->weight, p.E, 1, p.sr, at<float>(ws, p.r_part)};
     MOE_HIP(moe::launch_dense_gemv(g, s));
   } else {
-    moe::DenseArgs a{};
+    uint16_t* wr3 = at<uint16_t>(ws, p.wr3);
+    MOE_HIP(moe::launch_split3(router->weight, p.E, p.H, wr3, s));
+    moe::GemmArgs a{};
     a.A = (const uint16_t*)x;
     a.lda = p.H;
     a.M = p.T;
-    a.K = p.H;
     a.nseg = 2;
-    a.seg[0] = {down, p.L, 0, moe::kStoreBf16, z, p.L, nullptr, 0, nullptr, 0};
-    a.seg[1] = {router->weight, p.E, 1, moe::kStoreF32, logits, p.E, nullptr, 0, nullptr, 0};
-    MOE_HIP(moe::launch_dense(a, s));
+    a.seg[0] = {(const uint16_t*)down, p.L, p.H, p.H, moe::kStoreBf16, z, p.L, nullptr, 0, nullptr, 0};
+    a.seg[1] = {wr3, p.E, 3 * p.H, p.H, moe::kStoreF32, logits, p.E, nullptr, 0, nullptr, 0};
+    MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
   STAGE_MARK(1);
   // a2: (finish the split-K sums,) sigmoid, bias, top-k, weights
@@ -529,15 +532,14 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     MOE_HIP(moe::launch_finish_up(at<float>(ws, p.y_part), p.su, p.T, p.H, shared ? ys : nullptr, (uint16_t*)y,
                                   taps ? taps->y_routed : nullptr, s));
   } else {
-    moe::DenseArgs a{};
+    moe::GemmArgs a{};
     a.A = cn;
     a.lda = p.L;
     a.M = p.T;
-    a.K = p.L;
     a.nseg = 1;
-    a.seg[0] = {up, p.H, 0, moe::kAddStoreBf16, y, p.H, shared ? ys : nullptr, p.H,
+    a.seg[0] = {(const uint16_t*)up, p.H, p.L, p.L, moe::kAddStoreBf16, y, p.H, shared ? ys : nullptr, p.H,
                 taps ? taps->y_routed : nullptr, p.H};
-    MOE_HIP(moe::launch_dense(a, s));
+    MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
   STAGE_MARK(9);
 

@@ -1,0 +1,271 @@
+// Dense projections for batches of more than 64 tokens: C = A . W^T in bf16 MFMA.
+//
+// The layer's two dense matmuls (down-projection with the router logits, and the
+// up-projection; WASTE "Kimi K3, as released", section "Shape", and the K3
+// report review, "Stable LatentMoE") are plain contractions over K-contiguous
+// rows: A [M, K] activations, W [N, K] weights, both row-major.
+//
+// Tile: 128 x 128 outputs per block, 4 waves in 2 x 2, each 64 x 64 (4 x 4 MFMA
+// 16x16x32 bf16 tiles), K in steps of 64 (one 128-byte line per row). Operand
+// tiles go to LDS by LDS-DMA, full lines per row, into a ring of four stages
+// three k-steps ahead; each stage is its own LDS array with a compile-time index,
+// and the waits are explicit counts (every k-step issues the same 8 loads per
+// thread). The 16-byte chunks of a row are XOR-rotated by (row / 2) % 8, which
+// makes the MFMA fragment reads (16 rows x 16 bytes per lane group) bank-conflict
+// free.
+//
+// Grid order: logical tiles run M-tile major, N fastest, in contiguous ranges per
+// XCD (grid position mod 8), so the N tiles that share an A tile read it from
+// the same L2.
+//
+// fp32 weights (the router, fp32 on the K3 checkpoint) are first split exactly
+// into three bf16 planes hi + mid + lo (24 significand bits = 3 x 8) stored as
+// one [N, 3K] matrix; the contraction then runs over 3K with A's column k mod K,
+// which gives the fp32-weight product with fp32 accumulation.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kTile = kBM * kBK * 2;           // bytes of one operand tile in a stage
+constexpr int kGemmDma = 2 * kTile / 16 / 256;  // 16-byte LDS-DMA chunks per thread per k-step (A and W)
+static_assert(kGemmDma == 8, "");
+
+template <int I>
+using icg = std::integral_constant<int, I>;
+
+#define MOE_GEMM_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | ((((n) >> 4) & 3) << 14))
+
+__device__ __forceinline__ void gemm_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16g(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
+                                           0, 0);
+}
+
+// LDS position of 16-byte chunk c (0..7) of tile row r
+__host__ __device__ constexpr int g_pos(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[2 * kTile];
+  auto stage = [&](auto I_) -> uint8_t* {
+    constexpr int I = decltype(I_)::value % 4;
+    if constexpr (I == 0) return st0;
+    else if constexpr (I == 1) return st1;
+    else if constexpr (I == 2) return st2;
+    else return st3;
+  };
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nl = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- block -> (segment, M tile, N tile)
+  const int tm = (args.M + kBM - 1) / kBM;
+  const int tn0 = (args.seg[0].N + kBN - 1) / kBN;
+  const int tn1 = args.nseg > 1 ? (args.seg[1].N + kBN - 1) / kBN : 0;
+  const int tn = tn0 + tn1;
+  const int total = tm * tn;
+  const int per = (total + 7) >> 3;
+  const int lb = (int)blockIdx.x >> 3;
+  if (lb >= per) return;
+  const int L = ((int)blockIdx.x & 7) * per + lb;
+  if (L >= total) return;
+  const int mt = L / tn, nt = L % tn;
+  const bool second = nt >= tn0;
+  const GemmSeg& sg = args.seg[second ? 1 : 0];
+  const int m0 = mt * kBM, n0 = (second ? nt - tn0 : nt) * kBN;
+  const int K = sg.K, kwrap = sg.kwrap;
+
+  // ---- LDS-DMA of one k-step: chunk t = tid + 256 i; i < 4: A, else W; row t/8 of the
+  // tile (t taken mod 1024), LDS position t % 8, global chunk g_pos^-1 = same XOR
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, (uint32_t)args.M * (uint32_t)args.lda * 2u);
+  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(sg.W, 0u);
+  uint32_t goff[kGemmDma];
+#pragma unroll
+  for (int i = 0; i < kGemmDma; ++i) {
+    const int t = (tid + 256 * i) & 1023, r = t >> 3, pos = t & 7;
+    const int c = g_pos(pos, r);  // the XOR is its own inverse
+    if (i < 4) {
+      const int row = m0 + r;
+      goff[i] = row < args.M ? ((uint32_t)row * (uint32_t)args.lda + 8u * c) * 2u : kOob;
+    } else {
+      const int row = n0 + r;
+      goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
+    }
+  }
+  auto dma = [&](uint8_t* st, int ks, bool on) {  // kGemmDma loads
+    const uint32_t ka = (uint32_t)((ks * kBK) % kwrap) * 2u, kw = (uint32_t)(ks * kBK) * 2u;
+#pragma unroll
+    for (int i = 0; i < kGemmDma; ++i)
+      dma16g(on ? (i < 4 ? a_rs : w_rs) : none, st + (i < 4 ? 0 : kTile) + (i & 3) * 4096 + wave * 1024, goff[i],
+             i < 4 ? ka : kw);
+  };
+
+  // fragment reads: lane (nl, q) of A tile mi reads row 64 wm + 16 mi + nl, chunk 4 kk + q
+  uint32_t ard[2], brd[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    ard[kk] = (uint32_t)((wm * 64 + nl) * 128 + g_pos(4 * kk + q, nl) * 16);
+    brd[kk] = (uint32_t)(kTile + (wn * 64 + nl) * 128 + g_pos(4 * kk + q, nl) * 16);
+  }
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t* st) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4_t av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = *(const u32x4_t*)(st + ard[kk] + i * 16 * 128);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = *(const u32x4_t*)(st + brd[kk] + j * 16 * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ring: k-step ks reads stage ks % 4; it issues the loads of ks + 3 into the stage read
+  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x 8 loads follow it)
+  const int nks = K / kBK;  // a multiple of 4
+  dma(stage(icg<0>{}), 0, true);
+  dma(stage(icg<1>{}), 1, nks > 1);
+  dma(stage(icg<2>{}), 2, nks > 2);
+  MOE_GEMM_WAIT_VM_LGKM0(2 * kGemmDma);
+  gemm_barrier();
+  for (int k4 = 0; k4 < nks; k4 += 4) {
+    auto step = [&](auto S_) {
+      constexpr int S = decltype(S_)::value;
+      const int ks = k4 + S;
+      dma(stage(icg<S + 3>{}), ks + 3, ks + 3 < nks);
+      compute(stage(S_));
+      MOE_GEMM_WAIT_VM_LGKM0(2 * kGemmDma);
+      gemm_barrier();
+    };
+    step(icg<0>{});
+    step(icg<1>{});
+    step(icg<2>{});
+    step(icg<3>{});
+  }
+  // the last k-steps issued zero-filling loads into the ring: they must land before the
+  // block ends and its LDS goes to another block
+  MOE_GEMM_WAIT_VM_LGKM0(0);
+
+  // epilogue: lane holds D[m = 4q + r][n = nl] of each 16 x 16 tile. Rows past M and
+  // columns past N are skipped; all addend loads are issued before any store.
+  int rows[4][4];
+  bool colok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rows[i][r] = m0 + wm * 64 + 16 * i + 4 * q + r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) colok[j] = n0 + wn * 64 + 16 * j + nl < sg.N;
+  const int colb = n0 + wn * 64 + nl;
+  if (sg.mode == kAddStoreBf16) {
+    float add[4][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          add[i][r][j] = (sg.addend && rows[i][r] < args.M && colok[j])
+                             ? sg.addend[(size_t)rows[i][r] * sg.ld_add + colb + 16 * j]
+                             : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (rows[i][r] >= args.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!colok[j]) continue;
+          const float v = acc[i][j][r];
+          ((uint16_t*)sg.out)[(size_t)rows[i][r] * sg.ldo + colb + 16 * j] =
+              (uint16_t)f32_to_bf16_bits(v + add[i][r][j]);
+          if (sg.tap) sg.tap[(size_t)rows[i][r] * sg.ld_tap + colb + 16 * j] = v;
+        }
+      }
+  } else {
+    const bool f32 = sg.mode == kStoreF32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (rows[i][r] >= args.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!colok[j]) continue;
+          const size_t o = (size_t)rows[i][r] * sg.ldo + colb + 16 * j;
+          if (f32)
+            ((float*)sg.out)[o] = acc[i][j][r];
+          else
+            ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+        }
+      }
+  }
+}
+
+// fp32 [N, K] -> bf16 [N, 3K]: row n = hi(k) | mid(k) | lo(k), w = hi + mid + lo exactly
+__global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ W, int N, int K,
+                                                     uint16_t* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)N * K) return;
+  const int n = (int)(i / K), k = (int)(i % K);
+  const float f = W[i];
+  const uint32_t h = __float_as_uint(f) & 0xffff0000u;
+  const float r = f - __uint_as_float(h);
+  const uint32_t m = __float_as_uint(r) & 0xffff0000u;
+  const float l = r - __uint_as_float(m);
+  uint16_t* row = out + (size_t)n * 3 * K;
+  row[k] = (uint16_t)(h >> 16);
+  row[K + k] = (uint16_t)(m >> 16);
+  row[2 * K + k] = (uint16_t)(__float_as_uint(l) >> 16);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
+  if (a.nseg < 1 || a.nseg > 2 || a.M < 0 || a.lda % 8) return hipErrorInvalidValue;
+  long long tiles = 0;
+  const long long tm = (a.M + kBM - 1) / kBM;
+  for (int i = 0; i < a.nseg; ++i) {
+    const GemmSeg& g = a.seg[i];
+    if (g.K % (4 * kBK) || g.kwrap % kBK || g.kwrap > a.lda || g.K % g.kwrap || g.N <= 0) return hipErrorInvalidValue;
+    if ((long long)g.N * g.K * 2 >= (1ll << 31)) return hipErrorInvalidValue;
+    tiles += tm * ((g.N + kBN - 1) / kBN);
+  }
+  if ((long long)a.M * a.lda * 2 >= (1ll << 31)) return hipErrorInvalidValue;
+  if (tiles == 0) return hipSuccess;
+  const long long grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split3(const float* W, int N, int K, uint16_t* out, hipStream_t s) {
+  const long long n = (long long)N * K;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(split3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, W, N, K, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -36,6 +36,30 @@ struct DenseArgs {
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- dense projections, large batches
+// out = A . W^T per segment; A bf16 [M, lda]; W bf16 [N, K]; A's column for k is k mod kwrap
+// (kwrap = K, or the width of A when W holds three split planes of fp32 weights).
+struct GemmSeg {
+  const uint16_t* W;
+  int N, K, kwrap;      // K multiple of 256, kwrap multiple of 64
+  int mode;             // DenseOut
+  void* out;
+  int ldo;
+  const float* addend;  // kAddStoreBf16 only (may be null)
+  int ld_add;
+  float* tap;           // kAddStoreBf16 only, optional
+  int ld_tap;
+};
+struct GemmArgs {
+  const uint16_t* A;
+  int lda, M;
+  GemmSeg seg[2];
+  int nseg;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// fp32 [N, K] -> bf16 [N, 3K] rows hi | mid | lo with w = hi + mid + lo exactly
+hipError_t launch_split3(const float* W, int N, int K, uint16_t* out, hipStream_t s);
+
 // ---------------------------------------------------------------- decode-size dense projections
 // Split-K streaming GEMV for M <= 64 tokens: part[slice][m][n] = sum over the slice's K of A[m][k] W[n][k].
 struct GemvSeg {
