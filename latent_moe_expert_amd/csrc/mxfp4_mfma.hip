@@ -15,10 +15,12 @@
 // into the MFMA unchanged. The activations are the A operand in the FP6 E2M3
 // hi/lo encoding (mxfp6.h); hi and lo each take one MFMA at the FP4 rate.
 //
-// K order. Within a window of 16 groups (512 K values), k-step s gives lane
-// group q the group 4q + s. Then each lane's weight bytes for the window are one
-// 64-byte run of its row, and each lane's four scales are one aligned dword
-// (opsel s picks the byte), for weights and activations alike.
+// K order. K-step k gives lane group q the E8M0 group 4k + q, so one weight load
+// instruction covers 64 contiguous bytes of each of 16 rows. A lane's scales for
+// the four k-steps of a window (512 K values) are bytes q, 4+q, 8+q, 12+q of its
+// row's 16 window scale bytes; they are gathered once per window into one dword
+// (opsel s picks byte s). The activation encoding stores its scales in that
+// gathered order already.
 //
 // Dataflow per block (4 waves, 1 per SIMD). The A rows of a k-step (192 rows x
 // 192 bytes, gathered through the sorted token ids) go to LDS by LDS-DMA loads
@@ -56,9 +58,8 @@ constexpr int kAStage = kRows * kArow;      // bytes per A stage (sized for the 
 constexpr int kSDma = 2;                    // 16-byte scale chunks per thread per window
 constexpr int kSStage = kSDma * 256 * 16;
 constexpr int kHRow = 132;                  // floats per row of the GLU epilogue tile
-constexpr int kHTiles = 3;                  // row tiles per epilogue pass
 static_assert(kRows * 2 <= kSDma * 256, "scale chunks");
-static_assert(kHTiles * 16 * kHRow * 4 <= kAStage, "GLU epilogue tile must fit a stage");
+static_assert(64 * kHRow * 4 <= kAStage && kMF <= 12, "GLU epilogue: 64 rows of h per ring array, 3 arrays");
 static_assert(4 * kAStage + kSStage <= 160 * 1024, "LDS");
 
 template <int I>
@@ -80,10 +81,6 @@ __device__ __forceinline__ void ring_barrier() {
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff,
                                            0, 0);
-}
-
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
 }
 
 // LDS position of 16-byte chunk c of a staged row whose index within its 16-row tile is
@@ -151,9 +148,11 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
 #pragma unroll
   for (int nf = 0; nf < 4; ++nf) {
     const uint32_t row = (uint32_t)(row0 + 16 * (GLU ? (nf & 1) : nf) + nl);
-    bvoff[nf] = row * kb2 + 64u * q;
-    svoff[nf] = row * ks32 + 4u * q;
+    bvoff[nf] = row * kb2 + 16u * q;
+    svoff[nf] = row * ks32;
   }
+  // byte selector of v_perm_b32 gathering byte q of each of two dwords into the low half
+  const uint32_t qsel = 0x0c0c0000u | ((uint32_t)(4 + q) << 8) | (uint32_t)q;
 
   // A load that is not needed (past the last k-step or window) goes to a zero-size
   // resource: it reads zeros without touching memory, and the load count stays fixed.
@@ -161,16 +160,26 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   // interleaved 16-byte pieces of the same lines, which must survive in L2 between them.
   const __amdgpu_buffer_rsrc_t none = make_rsrc(a.W, 0u);
   u32x4_t b[4][4];  // [k-step in window][B tile]
-  uint32_t sb[4], sbn[4];
+  uint32_t sb[4];   // gathered scale dwords of the current window
+  u32x4_t sbn[4];   // the next window's 16 scale bytes per row
   auto load_b = [&](int w, int s, bool on) {  // 4 loads
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf)
-      b[s][nf] = buf_load16(on ? ((GLU && nf >= 2) ? w_hi : w_lo) : none, bvoff[nf], (uint32_t)(256 * w + 16 * s));
+      b[s][nf] = buf_load16(on ? ((GLU && nf >= 2) ? w_hi : w_lo) : none, bvoff[nf], (uint32_t)(256 * w + 64 * s));
   };
-  auto load_sb = [&](int w, uint32_t* dst, bool on) {  // 4 loads
+  auto load_sb = [&](int w, u32x4_t* dst, bool on) {  // 4 loads
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf)
-      dst[nf] = buf_load4(on ? ((GLU && nf >= 2) ? s_hi : s_lo) : none, svoff[nf], (uint32_t)(16 * w));
+      dst[nf] = buf_load16(on ? ((GLU && nf >= 2) ? s_hi : s_lo) : none, svoff[nf], (uint32_t)(16 * w));
+  };
+  // byte s of the result = byte q of dword s (the scale of group 4s + q)
+  auto gather_sb = [&](const u32x4_t* src) {
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+      const uint32_t lo = __builtin_amdgcn_perm(src[nf][1], src[nf][0], qsel);
+      const uint32_t hi = __builtin_amdgcn_perm(src[nf][3], src[nf][2], qsel);
+      sb[nf] = lo | (hi << 16);
+    }
   };
   auto dma_a = [&](uint8_t* st, int ks, bool on) {  // kADma loads
 #pragma unroll
@@ -199,6 +208,8 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
       const int gb = p * 96 + q * 24 + 8 * u;
       aoff[p][u] = (uint32_t)(nl * kArow + a_chunk_pos(gb / 16, nl) * 16 + gb % 16);
     }
+  // activation scale dwords of the window, read at its start: the scale area (in stage 0)
+  // receives the next window's scales from k-step 1 of the window on
   uint32_t sA[NT][2];
 
   auto read_a = [&](const uint8_t* st, int mf, i32x8_t* av) {
@@ -258,13 +269,14 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   dma_a(stage(ic<0>{}), 0, true);
   load_b(0, 0, true);
   load_b(0, 1, true);
-  load_sb(0, sb, true);
+  load_sb(0, sbn, true);
   dma_a(stage(ic<1>{}), 1, nks > 1);
   load_b(0, 2, true);
   dma_a(stage(ic<2>{}), 2, nks > 2);
   load_b(0, 3, true);
   MOE_WAIT_VM_LGKM0(20 + 2 * kADma);  // scales 0 and stage 0 complete
   ring_barrier();
+  gather_sb(sbn);
 
   for (int w = 0; w < nw; ++w) {
     {
@@ -291,8 +303,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
     step(ic<1>{});
     step(ic<2>{});
     step(ic<3>{});
-#pragma unroll
-    for (int nf = 0; nf < 4; ++nf) sb[nf] = sbn[nf];
+    gather_sb(sbn);
   }
   // the last k-steps issued zero-filling stage loads into the ring: drain them before reuse
   MOE_WAIT_VM_LGKM0(0);
@@ -313,30 +324,31 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
       }
     }
   } else {
-    // h tile through LDS, 48 rows per pass, then one thread per (row, group of 32)
-    float* hs = (float*)lds_a0;
+    // h tile through LDS in one pass (rows 64i.. in ring array i), then one thread per
+    // (row, group of 32 columns): all four waves' columns of a row form its 4 groups.
     const uint32_t orow_bytes = (uint32_t)fp6_row_bytes(a.N), osrow_bytes = (uint32_t)fp6_scale_row_bytes(a.N);
+    auto hrow = [&](int j) -> float* {  // j: row of the job (compile-time array choice when j's tile is)
+      uint8_t* base = (j < 64) ? lds_a0 : (j < 128 ? lds_a1 : lds_a2);
+      return (float*)base + (j & 63) * kHRow;
+    };
 #pragma unroll
-    for (int pass = 0; pass < (NT + kHTiles - 1) / kHTiles; ++pass) {
-      __syncthreads();
+    for (int mf = 0; mf < NT; ++mf) {
+      uint8_t* base = (mf < 4) ? lds_a0 : (mf < 8 ? lds_a1 : lds_a2);
 #pragma unroll
-      for (int mt = 0; mt < kHTiles; ++mt) {
-        const int mf = pass * kHTiles + mt;
-        if (mf < NT) {
+      for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
-          for (int nf = 0; nf < 2; ++nf)
+        for (int r = 0; r < 4; ++r)
+          ((float*)base)[((16 * mf + 4 * q + r) & 63) * kHRow + wave * 32 + 16 * nf + nl] =
+              glu_act(acc[mf][nf][r], acc[mf][nf + 2][r]);
+    }
+    __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              hs[(16 * mt + 4 * q + r) * kHRow + wave * 32 + 16 * nf + nl] =
-                  glu_act(acc[mf][nf][r], acc[mf][nf + 2][r]);
-        }
-      }
-      __syncthreads();
-      const int jl = tid >> 2, g4 = tid & 3;
-      const int j = pass * kHTiles * 16 + jl;
-      if (jl < kHTiles * 16 && j < nvalid) {
+    for (int i = 0; i < (NT * 64 + 255) / 256; ++i) {
+      const int t = tid + 256 * i;
+      const int j = t >> 2, g4 = t & 3;
+      if (j < NT * 16 && j < nvalid) {
         float v[32];
-        const f32x4_t* src = (const f32x4_t*)(hs + jl * kHRow + 32 * g4);
+        const f32x4_t* src = (const f32x4_t*)(hrow(j) + 32 * g4);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const f32x4_t x = src[u];

@@ -20,10 +20,11 @@
 // (little endian), which is the register layout the MFMA reads.
 //
 // Tensor layout (rows of K values, K a multiple of 512; a window is 16 groups):
-//   data   [row][K/128 steps][plane hi|lo][4][24 B]: step 4w+s, slot q holds group 16w + 4q + s
-//   scales [row][K/512 windows][plane hi|lo][16 B]: byte j is the scale of group 16w + j
-// so MFMA lane group q of k-step (w, s) finds its 24 bytes contiguously and its
-// scale as byte s of dword q of the window.
+//   data   [row][K/128 steps][plane hi|lo][4][24 B]: step k, slot q holds group 4k + q
+//   scales [row][K/512 windows][plane hi|lo][4][4 B]: window w, dword q, byte s is the
+//          scale of group 16w + 4s + q
+// so MFMA lane group q of k-step 4w + s finds its 24 bytes contiguously, and its
+// four scales of the window as one aligned dword (byte s for k-step s).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,27 +47,19 @@ __device__ __forceinline__ uint32_t fp6_scale_code(float amax, float& inv) {
 }
 
 // Round y (already divided by the scale) to E2M3: returns the 6-bit code and the
-// value of the code (in units of the scale).
+// value of the code (in units of the scale). Branch-free (lanes of a wave round
+// values of different binades): binade e = [t >= 2] + [t >= 4] has spacing 2^(e-3)
+// and code offset 8e.
 __device__ __forceinline__ uint32_t e2m3_round(float y, float& qv) {
   const float t = fminf(fabsf(y), 7.5f);
-  float r;
-  uint32_t c;
-  if (t < 2.f) {
-    r = rintf(t * 8.f);
-    c = (uint32_t)r;
-    r *= 0.125f;
-  } else if (t < 4.f) {
-    r = rintf(t * 4.f);
-    c = (uint32_t)r + 8u;
-    r *= 0.25f;
-  } else {
-    r = rintf(t * 2.f);
-    c = (uint32_t)r + 16u;
-    r *= 0.5f;
-  }
-  const bool neg = y < 0.f;
-  qv = neg ? -r : r;
-  return c | (neg ? 32u : 0u);
+  const bool b2 = t >= 2.f, b4 = t >= 4.f;
+  const float f = b4 ? 2.f : (b2 ? 4.f : 8.f);
+  const float inv = b4 ? 0.5f : (b2 ? 0.25f : 0.125f);
+  const uint32_t off = b4 ? 16u : (b2 ? 8u : 0u);
+  const float r = rintf(t * f);
+  const uint32_t sign = y < 0.f ? 0x80000000u : 0u;
+  qv = __uint_as_float(__float_as_uint(r * inv) | sign);
+  return ((uint32_t)r + off) | (sign >> 26);
 }
 
 // Pack 32 six-bit codes into 6 dwords (code i at bits [6i, 6i+6)).
@@ -112,11 +105,11 @@ __device__ __forceinline__ void fp6_encode_group(const float v[32], uint32_t hi[
 
 // Byte offsets of group g of a row inside the data and scale rows.
 __device__ __forceinline__ uint32_t fp6_data_offset(int g, int plane) {
-  const int w = g >> 4, q = (g >> 2) & 3, s = g & 3;
-  return (uint32_t)((4 * w + s) * kFp6StepBytes + plane * 96 + q * 24);
+  return (uint32_t)((g >> 2) * kFp6StepBytes + plane * 96 + (g & 3) * 24);
 }
 __device__ __forceinline__ uint32_t fp6_scale_offset(int g, int plane) {
-  return (uint32_t)((g >> 4) * kFp6WindowScaleBytes + plane * 16 + (g & 15));
+  const int w = g >> 4, s = (g >> 2) & 3, q = g & 3;
+  return (uint32_t)(w * kFp6WindowScaleBytes + plane * 16 + q * 4 + s);
 }
 
 }  // namespace moe
