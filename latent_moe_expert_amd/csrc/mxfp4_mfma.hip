@@ -27,9 +27,10 @@
 // (no registers), into a ring of four stages, three k-steps ahead of their use;
 // every wave reads all of them, one barrier per k-step. Each wave owns 64 weight
 // rows (GLU: 32 gate + the same 32 up rows) and loads them straight into MFMA
-// registers, one window ahead; weights are read once, so those loads are
-// non-temporal. Blocks of one job are adjacent in the grid order of one XCD, so
-// the job's activation rows are served from that XCD's L2.
+// registers, one window ahead (default cache policy: the four k-steps of a window
+// read the two halves of the same lines). Jobs are dealt to the XCDs round-robin
+// and the blocks of one job are adjacent in its XCD's order, so the job's
+// activation rows are served from that XCD's L2.
 //
 // Waits. vmcnt retires loads in issue order, so waiting for a stage also waits
 // for every load issued before it; the ring depth sets how old those loads are.
@@ -384,29 +385,31 @@ __global__ __launch_bounds__(256) void mx_mfma_kernel(MfmaArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a2[kAStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_a3[kAStage];
 
-  // ---- block -> (problem, job, column tile)
-  int nb0, nb1 = 0, nt0, nt1 = 1;
+  // ---- block -> (problem, job, column tile). Jobs are dealt to XCDs round-robin (job j
+  // to grid positions = j mod 8, which the hardware places on XCD j mod 8); inside an XCD
+  // the column tiles of a job are consecutive (the job's activation rows stay in that
+  // XCD's L2), and problem 0's jobs (the long dense rows) come before problem 1's.
+  const int xcd = (int)blockIdx.x & 7, lb = (int)blockIdx.x >> 3;
+  int nj0, nj1 = 0, nt0, nt1 = 1;
   {
     const MfmaProblem& p = args.p[0];
     nt0 = p.N / (GLU ? 128 : 256);
-    nb0 = (p.routed ? *p.n_jobs : (p.M + kRows - 1) / kRows) * nt0;
+    nj0 = p.routed ? *p.n_jobs : (p.M + kRows - 1) / kRows;
   }
   if (args.nprob > 1) {
     const MfmaProblem& p = args.p[1];
     nt1 = p.N / (GLU ? 128 : 256);
-    nb1 = (p.routed ? *p.n_jobs : (p.M + kRows - 1) / kRows) * nt1;
+    nj1 = p.routed ? *p.n_jobs : (p.M + kRows - 1) / kRows;
   }
-  const int total = nb0 + nb1;
-  const int per = (total + 7) >> 3;  // logical blocks per XCD (grid position mod 8)
-  const int lb = (int)blockIdx.x >> 3;
-  if (lb >= per) return;
-  const int L = ((int)blockIdx.x & 7) * per + lb;
-  if (L >= total) return;
-  const bool second = L >= nb0;
+  const int mine0 = nj0 > xcd ? (nj0 - xcd + 7) >> 3 : 0;  // jobs j = xcd + 8i of problem 0
+  const int mine1 = nj1 > xcd ? (nj1 - xcd + 7) >> 3 : 0;
+  const int b0 = mine0 * nt0;
+  if (lb >= b0 + mine1 * nt1) return;
+  const bool second = lb >= b0;
   const MfmaProblem& a = args.p[second ? 1 : 0];
-  const int local = second ? L - nb0 : L;
+  const int local = second ? lb - b0 : lb;
   const int nt = second ? nt1 : nt0;
-  const int job = local / nt, ntile = local % nt;
+  const int job = xcd + 8 * (local / nt), ntile = local % nt;
   int first, nvalid, expert = 0;
   if (a.routed) {
     const int4 jb = a.jobs[job];
@@ -444,10 +447,10 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
         (long long)p.N * p.K / 2 >= (1ll << 31) || (!p.routed && p.M > p.a_rows))
       return hipErrorInvalidValue;
     const long long jobs = p.routed ? p.max_jobs : (p.M + kRows - 1) / kRows;
-    blocks += jobs * (p.N / (glu ? 128 : 256));
+    blocks += (jobs + 7) / 8 * (p.N / (glu ? 128 : 256));  // per grid-position class (XCD)
   }
   if (blocks == 0) return hipSuccess;
-  const long long grid = (blocks + 7) / 8 * 8;
+  const long long grid = blocks * 8;
   if (grid > 0x7fffffffll) return hipErrorInvalidValue;
   if (glu)
     hipLaunchKernelGGL(mx_mfma_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
