@@ -6,7 +6,12 @@ up-projection) over one batch of seeded synthetic tokens with every input
 already resident in HBM. Default workload: one K3 layer at decode batch 16
 (hidden 7168, latent 3584, 896 MXFP4 experts with top-16, RMSNorm, 2 shared
 experts merged to a 6144-wide MXFP4 GLU). Four seeded token batches rotate so
-that consecutive steps touch different experts.
+that consecutive steps touch different experts. Its roofline is HBM bandwidth
+on the expert-weight bytes of the gate/up launch.
+
+The default run also times the same layer at an 8192-token prefill (two
+rotating batches) and reports it under "prefill", with the MXFP4 MFMA roofline
+of its gate/up launch (algorithmic flops over the FP4/FP6 dense MFMA peak).
 
 Prints one JSON line (rank 0). Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -25,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "latent-MoE layer tokens/s; % peak HBM GB/s (decode), % MXFP4 MFMA (prefill)"
 HBM_PEAK_GBS = 8000.0
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4/MXFP6 MFMA, MI355X
 
 
 def log(msg):
@@ -81,6 +87,8 @@ def main():
     ap.add_argument("--config", default="decode16", help="named workload (decode16, decode256, prefill8192)")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the secondary 8192-token prefill measurement of the default run")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the steps, run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -109,87 +117,123 @@ def main():
     xs = [to_dev_bf16(xs_bits[i * c.T:(i + 1) * c.T]) for i in range(4)]
     log(f"inputs resident in HBM in {time.time() - t0:.1f} s")
 
+    record = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L)
+    if not args.no_prefill and c.name == "decode16":
+        # the 8192-token prefill on the same resident layer (the scaled-MFMA expert path)
+        cp = gen.named_config("prefill8192")
+        xp_bits = gen.make_x(cp, 0, T=2 * cp.T)
+        xp = [to_dev_bf16(xp_bits[i * cp.T:(i + 1) * cp.T]) for i in range(2)]
+        record["prefill"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2, summary=True)
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
+    print(json.dumps(record), flush=True)
+
+
+def uses_mfma_path(c) -> bool:
+    """The library's automatic expert-path rule (MOE_PATH_AUTO in include/moe_latent.h)."""
+    sizes = all(v % 512 == 0 for v in (c.hidden, c.latent, c.inter, c.shared_inter))
+    return sizes and c.T * c.topk >= 32 * c.n_experts
+
+
+def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False):
+    """Time `steps` forwards of config c over `rotate` resident token batches; returns the
+    JSON record (or, with summary, the fields of a secondary measurement)."""
+    import torch
+    from workload import gen
     dims = dl.dims(c.T)
     ws = torch.empty(L.moe_latent_workspace_size(dims, c.topk), dtype=torch.uint8, device="cuda")
     y = torch.empty((c.T, c.hidden), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i):
-        L.moe_latent_forward(dims, xs[i % 4], dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales, dl.up,
+        L.moe_latent_forward(dims, xs[i % rotate], dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales, dl.up,
                              dl.sh_packed, dl.sh_scales, c.topk, y, ws, stream=stream)
 
     # distinct experts touched by each batch (routing taps, untimed)
     D = []
-    for i in range(4):
+    for i in range(rotate):
         ids = torch.empty((c.T, c.topk), dtype=torch.int32, device="cuda")
         L.moe_latent_forward_ex(dims, xs[i], dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales, dl.up,
                                 dl.sh_packed, dl.sh_scales, c.topk, y, ws, taps={"topk_ids": ids})
         torch.cuda.synchronize()
         D.append(len(np.unique(ids.cpu().numpy())))
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
     L.moe_latent_timing_enable(True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     L.moe_latent_timing_enable(False)
     stages, nf = L.moe_latent_timing_read()
+    del ws
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = c.T * args.steps / elapsed
+    ms_per_step = elapsed * 1e3 / steps
+    value = c.T * steps / elapsed
     stage_ms = {k: v / max(nf, 1) for k, v in stages.items()}
-
-    gu_per_expert = 2 * (c.inter * c.latent // 2 + c.inter * c.latent // 32)     # w1 + w3, packed + scales
-    dn_per_expert = c.latent * c.inter // 2 + c.latent * c.inter // 32
-    D_steps = [D[i % 4] for i in range(args.steps)]
-    D_mean = float(np.mean(D_steps))
+    D_mean = float(np.mean([D[i % rotate] for i in range(steps)]))
     pairs = c.T * c.topk
-    # algorithmic bytes of one gate/up launch (routed experts and, in the same launch, the
-    # shared experts' gate/up): each touched expert's w1|w3 once, the gathered latent rows
-    # once per pair, h written once per pair; the shared gate|up once, x once, hs written once
-    sh_gu = 2 * (c.shared_inter * c.hidden // 2 + c.shared_inter * c.hidden // 32) if c.shared_inter else 0
-    gu_bytes = (D_mean * gu_per_expert + pairs * c.latent * 2 + pairs * c.inter * 2
-                + sh_gu + (c.T * c.hidden * 2 + c.T * c.shared_inter * 2 if c.shared_inter else 0))
-    gu_ms = stage_ms["expert_gate_up"]
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    sh_bytes = gen.shared_record_bytes(c) + gen.shared_scale_bytes(c) if c.shared_inter else 0
-    exp_ms = stage_ms["expert_gate_up"] + stage_ms["expert_down"] + stage_ms["shared_gate_up"] + stage_ms["shared_down"]
-    exp_bytes = D_mean * (gu_per_expert + dn_per_expert) + sh_bytes
-    record = {
+    gu_ms, dn_ms = stage_ms["expert_gate_up"], stage_ms["expert_down"]
+    workload = (f"{c.name}: one K3 latent-MoE layer, T={c.T} tokens, hidden {c.hidden}, latent {c.latent}, "
+                f"{c.n_experts} MXFP4 experts top-{c.topk}, intermediate {c.inter}, RMSNorm={c.norm}, shared GLU "
+                f"{c.shared_inter}; weights MXFP4 (E2M1 + E8M0/32), activations bf16, fp32 accumulation")
+    if uses_mfma_path(c):
+        # algorithmic flops of the gate/up launch (routed pairs and shared rows, gate and up)
+        gu_flops = 4.0 * pairs * c.latent * c.inter + 4.0 * c.T * c.hidden * c.shared_inter
+        all_flops = 6.0 * pairs * c.latent * c.inter + 6.0 * c.T * c.hidden * c.shared_inter
+        tf = gu_flops / (gu_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "mx_mfma_kernel<GLU> (routed + shared MXFP4 gate/up + GLU, "
+                                                "scaled MFMA, FP6 hi/lo activations)",
+                    "achieved": round(tf, 1), "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 5)}
+        extra = {"expert_kernels_mfma_frac": round(all_flops / ((gu_ms + dn_ms) * 1e-3) / 1e12
+                                                   / MFMA_FP4_PEAK_TFLOPS, 4)}
+    else:
+        gu_per_expert = 2 * (c.inter * c.latent // 2 + c.inter * c.latent // 32)     # w1 + w3, packed + scales
+        dn_per_expert = c.latent * c.inter // 2 + c.latent * c.inter // 32
+        # algorithmic bytes of one gate/up launch (routed experts and, in the same launch, the
+        # shared experts' gate/up): each touched expert's w1|w3 once, the gathered latent rows
+        # once per pair, h written once per pair; the shared gate|up once, x once, hs written once
+        sh_gu = 2 * (c.shared_inter * c.hidden // 2 + c.shared_inter * c.hidden // 32) if c.shared_inter else 0
+        gu_bytes = (D_mean * gu_per_expert + pairs * c.latent * 2 + pairs * c.inter * 2
+                    + sh_gu + (c.T * c.hidden * 2 + c.T * c.shared_inter * 2 if c.shared_inter else 0))
+        achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+        sh_bytes = gen.shared_record_bytes(c) + gen.shared_scale_bytes(c) if c.shared_inter else 0
+        exp_bytes = D_mean * (gu_per_expert + dn_per_expert) + sh_bytes
+        roofline = {"bound": "hbm", "kernel": "mx_small_kernel<GLU> (routed + shared MXFP4 gate/up + GLU)",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
+                    "bytes_per_launch": int(gu_bytes), "avg_launch_ms": round(gu_ms, 5)}
+        extra = {"expert_kernels_hbm_frac": round(exp_bytes / ((gu_ms + dn_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if summary:
+        return {"config": {"workload": workload, "global_batch": c.T}, "value": round(value, 2), "unit": "tokens/s",
+                "steps": steps, "ms_per_step": round(ms_per_step, 4), "roofline": roofline, **extra,
+                "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}}
+    return {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{c.name}: one K3 latent-MoE layer, T={c.T} tokens, hidden {c.hidden}, latent "
-                               f"{c.latent}, {c.n_experts} MXFP4 experts top-{c.topk}, intermediate {c.inter}, "
-                               f"RMSNorm={c.norm}, shared GLU {c.shared_inter}; weights MXFP4 (E2M1 + E8M0/32), "
-                               f"activations bf16, fp32 accumulation",
-                   "global_batch": c.T, "parallelism": "none (1 GPU)",
+        "config": {"workload": workload, "global_batch": c.T, "parallelism": "none (1 GPU)",
                    "distinct_experts_per_step": D_mean},
-        "roofline": {"bound": "hbm", "kernel": "mx_small_kernel<GLU> (routed + shared MXFP4 gate/up + GLU)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
-                     "bytes_per_launch": int(gu_bytes), "avg_launch_ms": round(gu_ms, 5)},
-        "expert_kernels_hbm_frac": round(exp_bytes / (exp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        **extra,
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
     }
-    if not args.no_cpu_baseline:
-        record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
-    print(json.dumps(record), flush=True)
 
 
 if __name__ == "__main__":

@@ -26,11 +26,11 @@ constexpr int kMaxTopk = 64;
 constexpr int kMaxLatent = 8192;
 
 // ------------------------------------------------------------------ stage timing
-enum Stage { kProjRouter, kTopk, kAlign, kExpGateUp, kExpDown, kCombine, kShGateUp, kShDown, kUpProj, kNumStages };
-// the shared experts' contractions run inside the expert_gate_up / expert_down
-// launches (their stages stay in the list and measure ~0)
-const char* kStageNames[kNumStages] = {"proj_router", "topk", "align", "expert_gate_up", "expert_down",
-                                       "combine_norm", "shared_gate_up", "shared_down", "up_proj"};
+enum Stage { kProjRouter, kTopk, kAlign, kActEncode, kExpGateUp, kExpDown, kCombine, kUpProj, kNumStages };
+// act_encode: the MXFP6 encoding of the contraction inputs (MOE_PATH_MFMA; ~0 otherwise).
+// The shared experts' contractions run inside the expert_gate_up / expert_down launches.
+const char* kStageNames[kNumStages] = {"proj_router", "topk", "align", "act_encode", "expert_gate_up",
+                                       "expert_down", "combine_norm", "up_proj"};
 constexpr int kMaxTimed = 256;
 
 struct Timing {
@@ -339,6 +339,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     const int32_t* n_jobs = at<int32_t>(ws, p.n_jobs);
     MOE_HIP(moe::launch_quant_fp6(z, p.L, p.T, p.L, zq, zqs, s));
     if (shared) MOE_HIP(moe::launch_quant_fp6((const uint16_t*)x, p.H, p.T, p.H, xq, xqs, s));
+    STAGE_MARK(4);
     {
       moe::MfmaArgs m{};
       int n = 0;
@@ -382,7 +383,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
       m.nprob = n;
       MOE_HIP(moe::launch_mx_mfma(m, s));
     }
-    STAGE_MARK(4);
+    STAGE_MARK(5);
     {
       moe::MfmaArgs m{};
       int n = 0;
@@ -422,8 +423,9 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
       m.nprob = n;
       MOE_HIP(moe::launch_mx_mfma(m, s));
     }
-    STAGE_MARK(5);
+    STAGE_MARK(6);
   } else {
+  STAGE_MARK(4);  // no activation encoding on this path
   {
     moe::MxArgs m{};
     int n = 0;
@@ -468,7 +470,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     m.nprob = n;
     MOE_HIP(moe::launch_mx_small(m, s));
   }
-  STAGE_MARK(4);
+  STAGE_MARK(5);
   // a6 (and a10's down): plain contractions, shared blocks first
   {
     moe::MxArgs m{};
@@ -510,15 +512,12 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     m.nprob = n;
     MOE_HIP(moe::launch_mx_small(m, s));
   }
-  STAGE_MARK(5);
+  STAGE_MARK(6);
   }
   // a7 + a8: weighted combine and RMSNorm
   MOE_HIP(moe::launch_combine_norm(O, p.L, inv_pos, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
                                    taps ? taps->c : nullptr, cn, s));
-  STAGE_MARK(6);
-  // (the shared experts ran inside the two contraction launches above)
   STAGE_MARK(7);
-  STAGE_MARK(8);
   // a9: up-projection, plus the shared output, rounded to bf16
   if (p.small) {
     moe::GemvArgs g{};
@@ -541,7 +540,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
                 taps ? taps->y_routed : nullptr, p.H};
     MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
-  STAGE_MARK(9);
+  STAGE_MARK(8);
 
   if (taps) {
     int r;

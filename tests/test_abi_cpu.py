@@ -37,8 +37,8 @@ def test_abi_version_and_strerror(lib):
     assert lib.moe_latent_abi_version() == 2
     for code in range(0, -7, -1):
         assert lib.moe_latent_strerror(code)
-    assert lib.moe_latent_stage_count() == 9
-    assert lib.moe_latent_stage_name(3) == b"expert_gate_up"
+    assert lib.moe_latent_stage_count() == 8
+    assert lib.moe_latent_stage_name(4) == b"expert_gate_up"
 
 
 def _dims(**kw):
