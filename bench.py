@@ -37,11 +37,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_PROFILES = {"decode16": "mx_small_decode16_traffic.md", "prefill8192": "mx_mfma_prefill8192_traffic.md"}
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC summary,
     or None when that summary was taken on a different kernel source or workload."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "mx_small_decode16_traffic.md")
+    if workload not in TRAFFIC_PROFILES:
+        return None
+    path = os.path.join(ROOT, "profiles", TRAFFIC_PROFILES[workload])
     try:
         line = next(l for l in open(path) if l.startswith("traffic_record:"))
         rec = json.loads(line.split(":", 1)[1])
@@ -190,7 +195,7 @@ def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False):
         roofline = {"bound": "mfma", "kernel": "mx_mfma_kernel<GLU> (routed + shared MXFP4 gate/up + GLU, "
                                                 "scaled MFMA, FP6 hi/lo activations)",
                     "achieved": round(tf, 1), "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(c.name),
                     "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 5)}
         extra = {"expert_kernels_mfma_frac": round(all_flops / ((gu_ms + dn_ms) * 1e-3) / 1e12
                                                    / MFMA_FP4_PEAK_TFLOPS, 4)}
