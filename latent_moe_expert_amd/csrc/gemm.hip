@@ -14,9 +14,10 @@
 // makes the MFMA fragment reads (16 rows x 16 bytes per lane group) bank-conflict
 // free.
 //
-// Grid order: logical tiles run M-tile major, N fastest, in contiguous ranges per
-// XCD (grid position mod 8), so the N tiles that share an A tile read it from
-// the same L2.
+// Grid order: contiguous ranges of logical tiles per XCD (grid position mod 8);
+// logical tiles run in groups of 8 M tiles with M fastest, so the blocks an XCD
+// runs together share W tiles and reuse A tiles across N from its L2 (one M tile
+// at a time across all of N streamed the weights once per M tile).
 //
 // fp32 weights (the router, fp32 on the K3 checkpoint) are first split exactly
 // into three bf16 planes hi + mid + lo (24 significand bits = 3 x 8) stored as
@@ -32,6 +33,7 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kGM = 8;  // M tiles per group of the grid order
 constexpr int kTile = kBM * kBK * 2;           // bytes of one operand tile in a stage
 constexpr int kGemmDma = 2 * kTile / 16 / 256;  // 16-byte LDS-DMA chunks per thread per k-step (A and W)
 static_assert(kGemmDma == 8, "");
@@ -82,7 +84,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   if (lb >= per) return;
   const int L = ((int)blockIdx.x & 7) * per + lb;
   if (L >= total) return;
-  const int mt = L / tn, nt = L % tn;
+  // grouped order: groups of kGM M tiles, M fastest inside a group, so the blocks that run
+  // together on an XCD share their W tiles (and each A tile is reused across N in L2)
+  const int grp = L / (kGM * tn), rem = L % (kGM * tn);
+  const int gm = min(kGM, tm - grp * kGM);
+  const int mt = grp * kGM + rem % gm, nt = rem / gm;
   const bool second = nt >= tn0;
   const GemmSeg& sg = args.seg[second ? 1 : 0];
   const int m0 = mt * kBM, n0 = (second ? nt - tn0 : nt) * kBN;
