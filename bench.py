@@ -89,7 +89,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="decode16", help="named workload (decode16, decode256, prefill8192)")
+    ap.add_argument("--config", default="decode16",
+                    help="named workload (decode16, decode256, prefill8192, stack8x4096)")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
@@ -116,6 +117,10 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.copy_mb} MiB device copies")
         del src, dst
+    if c.n_layers > 1:
+        record = measure_stack(c, args.steps, args.warmup, L, DeviceLayer, to_dev_bf16)
+        print(json.dumps(record), flush=True)
+        return
     t0 = time.time()
     dl = DeviceLayer(c)
     xs_bits = gen.make_x(c, 0, T=4 * c.T)
@@ -132,6 +137,61 @@ def main():
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
     print(json.dumps(record), flush=True)
+
+
+def measure_stack(c, steps, warmup, L, DeviceLayer, to_dev_bf16):
+    """A stack of c.n_layers layers with distinct seeded weights, all resident in HBM; a step
+    runs the T tokens through every layer in turn (layer i's y is layer i+1's x)."""
+    import torch
+    from workload import gen
+    t0 = time.time()
+    layers = [DeviceLayer(c, layer=i) for i in range(c.n_layers)]
+    log(f"{c.n_layers} layers resident in HBM in {time.time() - t0:.1f} s")
+    x0 = to_dev_bf16(gen.make_x(c, 0))
+    dims = layers[0].dims(c.T)
+    ws = torch.empty(L.moe_latent_workspace_size(dims, c.topk), dtype=torch.uint8, device="cuda")
+    ys = [torch.empty((c.T, c.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        x = x0
+        for i, dl in enumerate(layers):
+            y = ys[i & 1]
+            L.moe_latent_forward(dims, x, dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales, dl.up,
+                                 dl.sh_packed, dl.sh_scales, c.topk, y, ws, stream=stream)
+            x = y
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    L.moe_latent_timing_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    L.moe_latent_timing_enable(False)
+    stages, nf = L.moe_latent_timing_read()
+    stage_ms = {k: v / max(nf, 1) for k, v in stages.items()}
+    pairs = c.T * c.topk
+    gu_ms = stage_ms["expert_gate_up"]
+    gu_flops = 4.0 * pairs * c.latent * c.inter + 4.0 * c.T * c.hidden * c.shared_inter
+    tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": round(c.T * steps / elapsed, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(elapsed * 1e3 / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{c.name}: {c.n_layers} K3 latent-MoE layers with distinct seeded weights, chained, "
+                               f"T={c.T} tokens, Zipf({c.zipf_s}) selection bias (amplitude {c.zipf_c}); one step "
+                               f"runs the tokens through all layers", "global_batch": c.T,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "mx_mfma_kernel<GLU> (per layer: routed + shared gate/up + GLU)",
+                     "achieved": round(tf, 1), "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": None, "flops_per_launch": gu_flops,
+                     "avg_launch_ms": round(gu_ms, 5)},
+        "layer_stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+    }
 
 
 def uses_mfma_path(c) -> bool:

@@ -280,3 +280,31 @@ def test_full_decode256():
 @pytest.mark.timeout(900)
 def test_full_prefill8192():
     _full_case("prefill8192", sample=[0, 4097, 8191])
+
+
+@pytest.mark.fullsize
+@pytest.mark.timeout(900)
+def test_full_stack_layer_zipf_hot_experts():
+    """Layer 0 of the 8-layer stack workload: T=4096 with the Zipf(1.1) selection bias, where
+    the hottest expert takes ~1155 of the 65536 pairs (about 16x the mean) and is split over
+    several MFMA jobs. Same weights as the decode workloads (layer 0), plus the bias."""
+    H = _harness()
+    c = gen.named_config("stack8x4096")
+    dl = _k3_layer()
+    dense = {**dl.host_dense, "select_bias": gen.make_dense(c)["select_bias"]}
+    x = gen.make_x(c)
+    saved = dl.bias
+    dl.bias = torch.from_numpy(dense["select_bias"]).cuda()
+    try:
+        out = dl.run(x)
+    finally:
+        dl.bias = saved
+    counts = out["counts"]
+    hot = int(np.argmax(counts))
+    assert counts[hot] > 192  # more than one job
+    hot_token = int(np.nonzero((out["topk_ids"] == hot).any(axis=1))[0][-1])
+    sample = sorted({0, 2047, 4095, hot_token})
+    ref = li.oracle_forward(c, {"x": x, **dense, "shared": gen.make_shared(c)}, experts=dl.oracle_experts(),
+                            align_block=out["B"], tokens=sample)
+    H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
+
