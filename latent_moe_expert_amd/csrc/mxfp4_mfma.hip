@@ -22,15 +22,17 @@
 // (opsel s picks byte s). The activation encoding stores its scales in that
 // gathered order already.
 //
-// Dataflow per block (4 waves, 1 per SIMD). The A rows of a k-step (192 rows x
+// Dataflow per block (8 waves, 2 per SIMD). The A rows of a k-step (192 rows x
 // 192 bytes, gathered through the sorted token ids) go to LDS by LDS-DMA loads
 // (no registers), into a ring of four stages, three k-steps ahead of their use;
-// every wave reads all of them, one barrier per k-step. Each wave owns 64 weight
-// rows (GLU: 32 gate + the same 32 up rows) and loads them straight into MFMA
+// every wave reads all of them, one barrier per k-step. Each wave owns 32 weight
+// rows (GLU: 16 gate + the same 16 up rows) and loads them straight into MFMA
 // registers, one window ahead (default cache policy: the four k-steps of a window
-// read the two halves of the same lines). Jobs are dealt to the XCDs round-robin
-// and the blocks of one job are adjacent in its XCD's order, so the job's
-// activation rows are served from that XCD's L2.
+// read the two halves of the same lines). Two waves per SIMD keep its MFMA pipe
+// fed while the other wave's memory instructions wait for the load pipeline; each
+// k-step's memory instructions are spread over its row tiles for the same reason.
+// Jobs are dealt to the XCDs round-robin and the blocks of one job are adjacent
+// in its XCD's order, so the job's activation rows are served from that XCD's L2.
 //
 // Waits. vmcnt retires loads in issue order, so waiting for a stage also waits
 // for every load issued before it; the ring depth sets how old those loads are.
@@ -52,19 +54,35 @@ namespace moe {
 
 namespace {
 
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kMF = kMfmaSlotsPerJob / 16;  // row tiles per job
 constexpr int kRows = kMfmaSlotsPerJob;     // 192
 constexpr int kArow = 192;                  // LDS bytes per staged row (12 chunks of 16 B, rotated)
-constexpr int kAStage = kRows * kArow;      // bytes per A stage (sized for the largest job)
-constexpr int kSDma = 2;                    // 16-byte scale chunks per thread per window
-constexpr int kSStage = kSDma * 256 * 16;
+constexpr int kADmaMax = (kRows * 12 + kThreads - 1) / kThreads;  // LDS-DMA loads per thread per stage
+constexpr int kAStage = kRows * kArow;                            // bytes per A stage
+// The last LDS-DMA round of a stage covers only part of the block; the waves past the
+// stage's end load zeros into a dummy area instead (same load count in every wave).
+constexpr int kADummy = kADmaMax * kThreads * 16 - kAStage;
+constexpr int kSDma = 1;                    // 16-byte scale chunks per thread per window
+constexpr int kSStage = kSDma * kThreads * 16;
 constexpr int kHRow = 132;                  // floats per row of the GLU epilogue tile
-static_assert(kRows * 2 <= kSDma * 256, "scale chunks");
-static_assert(64 * kHRow * 4 <= kAStage && kMF <= 12, "GLU epilogue: 64 rows of h per ring array, 3 arrays");
-static_assert(4 * kAStage + kSStage <= 160 * 1024, "LDS");
+constexpr int kHRowsPerArray = 48;          // rows of h per ring array in the GLU epilogue
+static_assert(kADummy >= 0 && kADummy % 1024 == 0 && kAStage % 1024 == 0, "A stage");
+static_assert(kRows * 2 <= kSDma * kThreads, "scale chunks");
+static_assert(kHRowsPerArray * kHRow * 4 <= kAStage && 4 * kHRowsPerArray >= kRows, "GLU epilogue tile");
+static_assert(4 * kAStage + kSStage + kADummy <= 160 * 1024, "LDS");
 
 template <int I>
 using ic = std::integral_constant<int, I>;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at 15:14)
 #define MOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | ((((n) >> 4) & 3) << 14))
@@ -85,9 +103,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wav
 }
 
 // LDS position of 16-byte chunk c of a staged row whose index within its 16-row tile is
-// nl: rotating the chunks by nl/4 makes the MFMA fragment reads (16 rows x 24 bytes per
-// lane group) bank-conflict free.
-__host__ __device__ constexpr int a_chunk_pos(int c, int nl) { return (c + nl / 4) % 12; }
+// nl. A lane group's operands are chunks 3q..3q+2 of its row: 16 bytes of hi, then 8 of
+// hi and 8 of lo, then 16 of lo; the 16 lanes of a group read the same chunk index of 16
+// rows. Rows are 12 chunks long, so unrotated rows 4 apart would share banks (64 banks
+// of 4 bytes: 16 chunks per bank cycle); rotating row nl by a_rot(nl) spreads each
+// 16-byte read over all 16 chunk slots of a bank cycle.
+__host__ __device__ constexpr int a_rot(int nl) { return ((nl >> 1) & 3) ^ ((nl >> 3) & 1); }
+__host__ __device__ constexpr int a_chunk_pos(int c, int nl) { return (c + a_rot(nl)) % 12; }
 
 // One job (at most NT row tiles of 16) against one column tile. NT is a compile-time
 // bucket of the job's row count: every loop below is straight-line code, so each
@@ -95,9 +117,10 @@ __host__ __device__ constexpr int a_chunk_pos(int c, int nl) { return (c + nl / 
 template <bool GLU, int NT>
 __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nvalid, int expert, int ntile,
                                        uint8_t (&lds_a0)[kAStage + kSStage], uint8_t (&lds_a1)[kAStage],
-                                       uint8_t (&lds_a2)[kAStage], uint8_t (&lds_a3)[kAStage]) {
-  constexpr int kADma = (NT * 16 * 12 + 255) / 256;  // 16-byte LDS-DMA chunks per thread per k-step
-  static_assert(kADma * 256 * 16 <= kAStage, "stage");
+                                       uint8_t (&lds_a2)[kAStage], uint8_t (&lds_a3)[kAStage],
+                                       uint8_t* lds_dummy) {
+  constexpr int kADma = (NT * 16 * 12 + kThreads - 1) / kThreads;  // LDS-DMA loads per thread per k-step
+  static_assert(kADma <= kADmaMax, "stage");
   auto stage = [&](auto I_) -> uint8_t* {
     constexpr int I = decltype(I_)::value % 4;
     if constexpr (I == 0) return lds_a0;
@@ -117,41 +140,44 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
     return a.sorted_ids[first + j] / a.topk;
   };
 
-  // ---- A stage by LDS-DMA: chunk t = tid + 256 i lands at LDS byte 16 t, i.e. position t % 12
+  // ---- A stage by LDS-DMA: chunk t = tid + 512 i lands at LDS byte 16 t, i.e. position t % 12
   // of staged row j = t / 12, and carries the row's global chunk whose rotated position that is.
   uint32_t goff[kADma];
 #pragma unroll
   for (int i = 0; i < kADma; ++i) {
-    const int t = tid + 256 * i, j = t / 12, pos = t % 12;
-    const int c = (pos + 12 - (j & 15) / 4) % 12;
+    const int t = tid + kThreads * i, j = t / 12, pos = t % 12;
+    const int c = (pos + 12 - a_rot(j & 15)) % 12;
     const int r = j < NT * 16 ? a_row(j) : -1;
     goff[i] = r >= 0 ? (uint32_t)r * arow_bytes + 16u * c : kOob;
   }
   uint32_t sgoff[kSDma];
 #pragma unroll
   for (int i = 0; i < kSDma; ++i) {
-    const int t = tid + 256 * i, j = t >> 1, c = t & 1;
+    const int t = tid + kThreads * i, j = t >> 1, c = t & 1;
     const int r = j < NT * 16 ? a_row(j) : -1;
     sgoff[i] = r >= 0 ? (uint32_t)r * asrow_bytes + 16u * c : kOob;
   }
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a.Aq, (uint32_t)a.a_rows * arow_bytes);
   const __amdgpu_buffer_rsrc_t as_rs = make_rsrc(a.Aqs, (uint32_t)a.a_rows * asrow_bytes);
 
-  // ---- weights: wave rows, lane (nl, q) of B tile nf reads row rows(nf) + nl
+  // ---- weights: two B tiles per wave, lane (nl, q) of tile nf reads row rows(nf) + nl.
+  // GLU: tile 0 = 16 gate rows, tile 1 = the same 16 up rows; plain: 32 consecutive rows.
   const uint32_t kb2 = (uint32_t)K / 2, ks32 = (uint32_t)K / 32;
   const uint32_t mat_bytes = (uint32_t)a.N * kb2, mat_scales = (uint32_t)a.N * ks32;
   const __amdgpu_buffer_rsrc_t w_lo = make_rsrc(a.W + (size_t)expert * a.w_stride, mat_bytes);
   const __amdgpu_buffer_rsrc_t s_lo = make_rsrc(a.S + (size_t)expert * a.s_stride, mat_scales);
   const __amdgpu_buffer_rsrc_t w_hi = GLU ? make_rsrc(a.W2 + (size_t)expert * a.w_stride, mat_bytes) : w_lo;
   const __amdgpu_buffer_rsrc_t s_hi = GLU ? make_rsrc(a.S2 + (size_t)expert * a.s_stride, mat_scales) : s_lo;
-  const int row0 = GLU ? ntile * 128 + wave * 32 : ntile * 256 + wave * 64;
-  uint32_t bvoff[4], svoff[4];
+  const int row0 = GLU ? ntile * 128 + wave * 16 : ntile * 256 + wave * 32;
+  uint32_t bvoff[2], svoff[2];
 #pragma unroll
-  for (int nf = 0; nf < 4; ++nf) {
-    const uint32_t row = (uint32_t)(row0 + 16 * (GLU ? (nf & 1) : nf) + nl);
+  for (int nf = 0; nf < 2; ++nf) {
+    const uint32_t row = (uint32_t)(row0 + (GLU ? 0 : 16 * nf) + nl);
     bvoff[nf] = row * kb2 + 16u * q;
     svoff[nf] = row * ks32;
   }
+  auto w_rs = [&](int nf) { return (GLU && nf == 1) ? w_hi : w_lo; };
+  auto s_rs = [&](int nf) { return (GLU && nf == 1) ? s_hi : s_lo; };
   // byte selector of v_perm_b32 gathering byte q of each of two dwords into the low half
   const uint32_t qsel = 0x0c0c0000u | ((uint32_t)(4 + q) << 8) | (uint32_t)q;
 
@@ -160,83 +186,92 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   // The weight loads keep the default cache policy: the four k-steps of a window read
   // interleaved 16-byte pieces of the same lines, which must survive in L2 between them.
   const __amdgpu_buffer_rsrc_t none = make_rsrc(a.W, 0u);
-  u32x4_t b[4][4];  // [k-step in window][B tile]
-  uint32_t sb[4];   // gathered scale dwords of the current window
-  u32x4_t sbn[4];   // the next window's 16 scale bytes per row
-  auto load_b = [&](int w, int s, bool on) {  // 4 loads
+  u32x4_t b[4][2];  // [k-step in window][B tile]
+  uint32_t sb[2];   // gathered scale dwords of the current window
+  u32x4_t sbn[2];   // the next window's 16 scale bytes per row
+  auto load_b = [&](int w, int s, bool on) {  // 2 loads
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf)
-      b[s][nf] = buf_load16(on ? ((GLU && nf >= 2) ? w_hi : w_lo) : none, bvoff[nf], (uint32_t)(256 * w + 64 * s));
+    for (int nf = 0; nf < 2; ++nf)
+      b[s][nf] = buf_load16(on ? w_rs(nf) : none, bvoff[nf], (uint32_t)(256 * w + 64 * s));
   };
-  auto load_sb = [&](int w, u32x4_t* dst, bool on) {  // 4 loads
+  auto load_sb = [&](int w, bool on) {  // 2 loads
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf)
-      dst[nf] = buf_load16(on ? ((GLU && nf >= 2) ? s_hi : s_lo) : none, svoff[nf], (uint32_t)(16 * w));
+    for (int nf = 0; nf < 2; ++nf) sbn[nf] = buf_load16(on ? s_rs(nf) : none, svoff[nf], (uint32_t)(16 * w));
   };
   // byte s of the result = byte q of dword s (the scale of group 4s + q)
-  auto gather_sb = [&](const u32x4_t* src) {
+  auto gather_sb = [&]() {
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const uint32_t lo = __builtin_amdgcn_perm(src[nf][1], src[nf][0], qsel);
-      const uint32_t hi = __builtin_amdgcn_perm(src[nf][3], src[nf][2], qsel);
+    for (int nf = 0; nf < 2; ++nf) {
+      const uint32_t lo = __builtin_amdgcn_perm(sbn[nf][1], sbn[nf][0], qsel);
+      const uint32_t hi = __builtin_amdgcn_perm(sbn[nf][3], sbn[nf][2], qsel);
       sb[nf] = lo | (hi << 16);
     }
   };
+  // LDS-DMA round i of this wave: 1 KB at byte i * 8192 + wave * 1024 of the stage, or of the
+  // dummy area past the stage's end (those lanes carry no row: their goff is out of range)
+  auto a_dst_of = [&](uint8_t* st, int i) -> uint8_t* {
+    const int o = i * (kThreads * 16) + wave * 1024;
+    return (i + 1) * (kThreads * 16) <= kAStage || o < kAStage ? st + o : lds_dummy + (o - kAStage);
+  };
   auto dma_a = [&](uint8_t* st, int ks, bool on) {  // kADma loads
 #pragma unroll
-    for (int i = 0; i < kADma; ++i)
-      dma16(on ? a_rs : none, st + wave * 1024 + i * 4096, goff[i], (uint32_t)(ks * kFp6StepBytes));
+    for (int i = 0; i < kADma; ++i) dma16(on ? a_rs : none, a_dst_of(st, i), goff[i], (uint32_t)(ks * kFp6StepBytes));
   };
   auto dma_s = [&](int w, bool on) {  // kSDma loads
-    uint8_t* st = lds_a0 + kAStage;
 #pragma unroll
     for (int i = 0; i < kSDma; ++i)
-      dma16(on ? as_rs : none, st + wave * 1024 + i * 4096, sgoff[i], (uint32_t)(w * kFp6WindowScaleBytes));
+      dma16(on ? as_rs : none, lds_a0 + kAStage + wave * 1024 + i * (kThreads * 16), sgoff[i],
+            (uint32_t)(w * kFp6WindowScaleBytes));
   };
 
-  f32x4_t acc[NT][4];
+  // Each accumulator starts from its own opaque zero: with one shared constant as the
+  // loop-entry value of every accumulator, the register allocator renames MFMA results
+  // and copies them back on every iteration.
+  f32x4_t acc[NT][2];
 #pragma unroll
   for (int mf = 0; mf < NT; ++mf)
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // lane (nl, q) reads, per plane p, the 3 eight-byte units of its 24-byte piece
-  uint32_t aoff[2][3];
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int gb = p * 96 + q * 24 + 8 * u;
-      aoff[p][u] = (uint32_t)(nl * kArow + a_chunk_pos(gb / 16, nl) * 16 + gb % 16);
+    for (int nf = 0; nf < 2; ++nf) {
+      acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[mf][nf]));
     }
+
+  // lane (nl, q) reads the 48 bytes of its group (hi then lo plane) as chunks 3q..3q+2
+  uint32_t aoff[3];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) aoff[u] = (uint32_t)(nl * kArow + a_chunk_pos(3 * q + u, nl) * 16);
   // activation scale dwords of the window, read at its start: the scale area (in stage 0)
   // receives the next window's scales from k-step 1 of the window on
   uint32_t sA[NT][2];
 
+  // Four reads per tile: the middle chunk is read as two halves, so each operand is one
+  // 16-byte and one 8-byte read straight into its registers (the empty asm keeps the two
+  // halves from being merged into one read whose halves would then be copied).
   auto read_a = [&](const uint8_t* st, int mf, i32x8_t* av) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint8_t* base = st + mf * 16 * kArow;
-      const uint2 x0 = *(const uint2*)(base + aoff[p][0]);
-      const uint2 x1 = *(const uint2*)(base + aoff[p][1]);
-      const uint2 x2 = *(const uint2*)(base + aoff[p][2]);
-      av[p] = i32x8_t{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, (int)x2.x, (int)x2.y, 0, 0};
-    }
+    const uint8_t* base = st + mf * 16 * kArow;
+    const i32x4_t x0 = *(const i32x4_t*)(base + aoff[0]);
+    const int2 h1 = *(const int2*)(base + aoff[1]);
+    asm volatile("" ::: "memory");
+    const int2 l1 = *(const int2*)(base + aoff[1] + 8);
+    const i32x4_t x2 = *(const i32x4_t*)(base + aoff[2]);
+    av[0] = i32x8_t{x0[0], x0[1], x0[2], x0[3], h1.x, h1.y, 0, 0};
+    av[1] = i32x8_t{l1.x, l1.y, x2[0], x2[1], x2[2], x2[3], 0, 0};
   };
   // Tile mf's MFMAs run while tile mf+1's operands are read; the barriers per tile keep
-  // the compiler from hoisting all tiles' reads (12 tiles would need 144 registers).
-  // Two register sets, picked by tile parity, so no operand is copied.
-  auto compute = [&](auto S_, const uint8_t* st) {
+  // the compiler from hoisting all tiles' reads. Two register sets, picked by tile parity,
+  // so no operand is copied. mem(mf) issues the memory operations assigned to tile mf.
+  auto compute = [&](auto S_, const uint8_t* st, auto&& mem) {
     constexpr int S = decltype(S_)::value;
     i32x8_t av[2][2];  // [row tile parity][plane]
     read_a(st, 0, av[0]);
-#pragma unroll
-    for (int mf = 0; mf < NT; ++mf) {
-      if (mf + 1 < NT) read_a(st, mf + 1, av[(mf + 1) & 1]);
+    static_for<0, NT>([&](auto MF) {
+      constexpr int mf = decltype(MF)::value;
+      if constexpr (mf + 1 < NT) read_a(st, mf + 1, av[(mf + 1) & 1]);
+      mem(MF);
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
+        for (int nf = 0; nf < 2; ++nf) {
           const u32x4_t bw = b[S][nf];
           const i32x8_t bv = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
           acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mf & 1][p], bv, acc[mf][nf], 2, 4, S,
@@ -247,37 +282,37 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
       // the MFMAs between them.
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
 
   // Pipeline. K-step ks (window w = ks/4, step S = ks%4) uses A stage S. Each k-step
   // issues, in order: at S == 1 the activation scales of window w+1 (kSDma loads into
   // stage 0's scale area), the A stage of ks+3 (kADma loads into stage (S+3)%4, read by
-  // k-step ks-1), the MFMAs of ks, the weights of k-step ks+4 (4 loads) and at S == 0
-  // the weight scales of window w+1 (4). Before the barrier that ends k-step ks, the A
-  // stage of ks+1 (issued in k-step ks-2) must be complete, and with it everything
-  // issued before it; the loads issued after it may stay in flight.
+  // k-step ks-1), the weights of k-step (S+3)%4 (2 loads: window w at S == 0, else w+1;
+  // those registers were last read by the previous k-step) and at S == 0 the weight
+  // scales of window w+1 (2). Before the barrier that ends k-step ks, the A stage of ks+1
+  // (issued in k-step ks-2) must be complete, and with it everything issued before it;
+  // the loads issued after it may stay in flight (the compiler waits for the weight
+  // registers where they are read).
   const int nw = K >> 9;
   const int nks = nw * 4;
-  constexpr int kStepLoads[4] = {kADma + 8, kSDma + kADma + 4, kADma + 4, kADma + 4};  // by S
-  constexpr int kStepTail[4] = {8, 4, 4, 4};  // loads of a k-step issued after its A stage
-  // Prologue: scales of window 0, A stage 0, then the weights of window 0 interleaved
-  // with A stages 1 and 2 so that, as in the steady state, tail(2) + loads(3) loads
-  // follow stage 1 and tail(3) follow stage 2: the first two k-steps then need no
-  // wait counts of their own (a runtime branch there would split the window body).
-  static_assert(kStepTail[2] + kStepLoads[3] == 8 + kADma && kStepTail[3] == 4, "prologue order");
+  constexpr int kStepLoads[4] = {kADma + 4, kSDma + kADma + 2, kADma + 2, kADma + 2};  // by S
+  constexpr int kStepTail[4] = {4, 2, 2, 2};  // loads of a k-step issued after its A stage
+  // Prologue: scales of window 0, A stage 0, the weights of k-steps 0-2 of window 0 and
+  // their scales, interleaved with A stages 1 and 2 so that at most tail(2) + loads(3)
+  // loads follow stage 1 and tail(3) follow stage 2, as the first waits assume.
   dma_s(0, true);
   dma_a(stage(ic<0>{}), 0, true);
   load_b(0, 0, true);
   load_b(0, 1, true);
-  load_sb(0, sbn, true);
+  load_sb(0, true);
   dma_a(stage(ic<1>{}), 1, nks > 1);
   load_b(0, 2, true);
   dma_a(stage(ic<2>{}), 2, nks > 2);
-  load_b(0, 3, true);
-  MOE_WAIT_VM_LGKM0(20 + 2 * kADma);  // scales 0 and stage 0 complete
+  static_assert(2 + kADma <= kStepTail[2] + kStepLoads[3] && 0 <= kStepTail[3], "prologue order");
+  MOE_WAIT_VM_LGKM0(8 + 2 * kADma);  // scales 0 and stage 0 complete
   ring_barrier();
-  gather_sb(sbn);
+  gather_sb();
 
   for (int w = 0; w < nw; ++w) {
     {
@@ -291,11 +326,34 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
     auto step = [&](auto S_) {
       constexpr int S = decltype(S_)::value;
       const int ks = 4 * w + S;
-      if (S == 1) dma_s(w + 1, more_w);
-      dma_a(stage(ic<S + 3>{}), ks + 3, ks + 3 < nks);
-      compute(S_, stage(S_));
-      load_b(w + 1, S, more_w);
-      if (S == 0) load_sb(w + 1, sbn, more_w);
+      constexpr int nS = S == 1 ? kSDma : 0;
+      constexpr int nOps = nS + kADma + 2 + (S == 0 ? 2 : 0);
+      constexpr int per = (nOps + NT - 1) / NT;
+      constexpr int bs = (S + 3) % 4;
+      const int bw_win = S == 0 ? w : w + 1;
+      const bool b_on = S == 0 ? true : more_w;
+      uint8_t* const a_dst = stage(ic<S + 3>{});
+      const bool a_on = ks + 3 < nks;
+      auto mem = [&](auto MF) {
+        constexpr int mf = decltype(MF)::value;
+        static_for<mf * per, (mf + 1) * per < nOps ? (mf + 1) * per : nOps>([&](auto O) {
+          constexpr int o = decltype(O)::value;
+          if constexpr (o < nS) {
+            dma16(more_w ? as_rs : none, lds_a0 + kAStage + wave * 1024 + o * (kThreads * 16), sgoff[o],
+                  (uint32_t)((w + 1) * kFp6WindowScaleBytes));
+          } else if constexpr (o < nS + kADma) {
+            constexpr int i = o - nS;
+            dma16(a_on ? a_rs : none, a_dst_of(a_dst, i), goff[i], (uint32_t)((ks + 3) * kFp6StepBytes));
+          } else if constexpr (o < nS + kADma + 2) {
+            constexpr int nf = o - nS - kADma;
+            b[bs][nf] = buf_load16(b_on ? w_rs(nf) : none, bvoff[nf], (uint32_t)(256 * bw_win + 64 * bs));
+          } else {
+            constexpr int nf = o - nS - kADma - 2;
+            sbn[nf] = buf_load16(more_w ? s_rs(nf) : none, svoff[nf], (uint32_t)(16 * (w + 1)));
+          }
+        });
+      };
+      compute(S_, stage(S_), mem);
       // loads issued after the A stage of ks+1: tail of ks-2, all of ks-1 and ks
       MOE_WAIT_VM_LGKM0(kStepTail[(S + 2) % 4] + kStepLoads[(S + 3) % 4] + kStepLoads[S]);
       ring_barrier();
@@ -304,7 +362,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
     step(ic<1>{});
     step(ic<2>{});
     step(ic<3>{});
-    gather_sb(sbn);
+    gather_sb();
   }
   // the last k-steps issued zero-filling stage loads into the ring: drain them before reuse
   MOE_WAIT_VM_LGKM0(0);
@@ -320,32 +378,27 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
         if (j < nvalid) {
           float* o = a.outf + (size_t)(first + j) * a.ldo + col0 + nl;
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) o[16 * nf] = acc[mf][nf][r];
+          for (int nf = 0; nf < 2; ++nf) o[16 * nf] = acc[mf][nf][r];
         }
       }
     }
   } else {
-    // h tile through LDS in one pass (rows 64i.. in ring array i), then one thread per
-    // (row, group of 32 columns): all four waves' columns of a row form its 4 groups.
+    // h tile through LDS in one pass (rows 48i.. in ring array i), then one thread per
+    // (row, group of 32 columns): the eight waves' 16 columns of a row form its 4 groups.
     const uint32_t orow_bytes = (uint32_t)fp6_row_bytes(a.N), osrow_bytes = (uint32_t)fp6_scale_row_bytes(a.N);
-    auto hrow = [&](int j) -> float* {  // j: row of the job (compile-time array choice when j's tile is)
-      uint8_t* base = (j < 64) ? lds_a0 : (j < 128 ? lds_a1 : lds_a2);
-      return (float*)base + (j & 63) * kHRow;
+    auto hrow = [&](int j) -> float* {
+      const int arr = j / kHRowsPerArray;
+      uint8_t* base = arr == 0 ? lds_a0 : (arr == 1 ? lds_a1 : (arr == 2 ? lds_a2 : lds_a3));
+      return (float*)base + (j - arr * kHRowsPerArray) * kHRow;
     };
 #pragma unroll
-    for (int mf = 0; mf < NT; ++mf) {
-      uint8_t* base = (mf < 4) ? lds_a0 : (mf < 8 ? lds_a1 : lds_a2);
+    for (int mf = 0; mf < NT; ++mf)
 #pragma unroll
-      for (int nf = 0; nf < 2; ++nf)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ((float*)base)[((16 * mf + 4 * q + r) & 63) * kHRow + wave * 32 + 16 * nf + nl] =
-              glu_act(acc[mf][nf][r], acc[mf][nf + 2][r]);
-    }
+      for (int r = 0; r < 4; ++r) hrow(16 * mf + 4 * q + r)[wave * 16 + nl] = glu_act(acc[mf][0][r], acc[mf][1][r]);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < (NT * 64 + 255) / 256; ++i) {
-      const int t = tid + 256 * i;
+    for (int i = 0; i < (NT * 64 + kThreads - 1) / kThreads; ++i) {
+      const int t = tid + kThreads * i;
       const int j = t >> 2, g4 = t & 3;
       if (j < NT * 16 && j < nvalid) {
         float v[32];
@@ -378,12 +431,13 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
 }
 
 template <bool GLU>
-__global__ __launch_bounds__(256) void mx_mfma_kernel(MfmaArgs args) {
+__global__ __launch_bounds__(kThreads) void mx_mfma_kernel(MfmaArgs args) {
   // stage 0 also holds the activation scales of its window (its k-step starts the window)
   __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kAStage + kSStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_a1[kAStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_a2[kAStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds_a3[kAStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_dummy[kADummy > 0 ? kADummy : 16];
 
   // ---- block -> (problem, job, column tile). Jobs are dealt to XCDs round-robin (job j
   // to grid positions = j mod 8, which the hardware places on XCD j mod 8); inside an XCD
@@ -422,13 +476,13 @@ __global__ __launch_bounds__(256) void mx_mfma_kernel(MfmaArgs args) {
   }
   const int nmf = (nvalid + 15) >> 4;
   if (nmf <= 4)
-    mx_job<GLU, 4>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+    mx_job<GLU, 4>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else if (nmf <= 8)
-    mx_job<GLU, 8>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+    mx_job<GLU, 8>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else if (nmf <= 10)
-    mx_job<GLU, 10>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+    mx_job<GLU, 10>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else
-    mx_job<GLU, kMF>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3);
+    mx_job<GLU, kMF>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
 }
 
 }  // namespace
@@ -453,9 +507,9 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
   const long long grid = blocks * 8;
   if (grid > 0x7fffffffll) return hipErrorInvalidValue;
   if (glu)
-    hipLaunchKernelGGL(mx_mfma_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mx_mfma_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(mx_mfma_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mx_mfma_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

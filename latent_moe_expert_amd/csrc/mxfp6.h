@@ -9,7 +9,7 @@
 //
 // Scale rule (OCP MX v1.0, section 6.3): X = 2^(floor(log2(amax)) - 2), where
 // 2 is the exponent of E2M3's largest normal (7.5 = 1.875 * 2^2); codes round to
-// nearest even and saturate at 7.5.
+// nearest even and saturate at 7.5 (gfx950's scaled conversion instructions do both).
 //
 // E2M3 code (6 bits): sign (bit 5), exponent (bits 4:3, bias 1), mantissa (2:0):
 // exponent 0 -> m/8, else (1 + m/8) * 2^(e-1). Magnitude codes are monotonic, so
@@ -20,92 +20,77 @@
 // (little endian), which is the register layout the MFMA reads.
 //
 // Tensor layout (rows of K values, K a multiple of 512; a window is 16 groups):
-//   data   [row][K/128 steps][plane hi|lo][4][24 B]: step k, slot q holds group 4k + q
+//   data   [row][K/128 steps][4][plane hi|lo][24 B]: step k, slot q holds group 4k + q
 //   scales [row][K/512 windows][plane hi|lo][4][4 B]: window w, dword q, byte s is the
 //          scale of group 16w + 4s + q
-// so MFMA lane group q of k-step 4w + s finds its 24 bytes contiguously, and its
-// four scales of the window as one aligned dword (byte s for k-step s).
+// so MFMA lane group q of k-step 4w + s finds both planes of its group as 48
+// contiguous, 16-byte aligned bytes (three 16-byte reads fill the two operands),
+// and its four scales of the window as one aligned dword (byte s for k-step s).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
 
-constexpr int kFp6StepBytes = 192;   // one k-step (128 values) of one row: hi 96 B + lo 96 B
+constexpr int kFp6StepBytes = 192;   // one k-step (128 values) of one row: 4 groups x (hi 24 B + lo 24 B)
 constexpr int kFp6WindowScaleBytes = 32;
 
 __host__ __device__ constexpr size_t fp6_row_bytes(int K) { return (size_t)K * 3 / 2; }
 __host__ __device__ constexpr size_t fp6_scale_row_bytes(int K) { return (size_t)K / 16; }
 
-// Scale code (E8M0) of a group with max magnitude `amax`, and 1/X as fp32.
-__device__ __forceinline__ uint32_t fp6_scale_code(float amax, float& inv) {
+typedef __attribute__((ext_vector_type(16))) float fp6_f32x16_t;
+typedef __attribute__((ext_vector_type(32))) float fp6_f32x32_t;
+typedef __attribute__((ext_vector_type(6))) unsigned fp6_u32x6_t;
+
+// Scale code (E8M0) of a group with max magnitude `amax`: 2^(floor(log2 amax) - 2), at
+// least 2^-126 (code 1) so that the scale is a normal float (a group whose magnitudes are
+// all below 2^-125 is encoded on the 2^-126 grid).
+__device__ __forceinline__ uint32_t fp6_scale_code(float amax) {
   const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);  // biased exponent, 0 for zero/subnormal
-  int code = e - 2;                                           // 2^(floor(log2 amax) - 2), biased
-  code = code < 0 ? 0 : code;                                 // amax < 2^-125: values quantize at 2^-127
-  inv = __uint_as_float((uint32_t)(254 - code) << 23);        // exact power of two, code <= 253
-  return (uint32_t)code;
+  const int code = e - 2;
+  return (uint32_t)(code < 1 ? 1 : code);
 }
+__device__ __forceinline__ float e8m0_value(uint32_t code) { return __uint_as_float(code << 23); }  // code >= 1
 
-// Round y (already divided by the scale) to E2M3: returns the 6-bit code and the
-// value of the code (in units of the scale). Branch-free (lanes of a wave round
-// values of different binades): binade e = [t >= 2] + [t >= 4] has spacing 2^(e-3)
-// and code offset 8e.
-__device__ __forceinline__ uint32_t e2m3_round(float y, float& qv) {
-  const float t = fminf(fabsf(y), 7.5f);
-  const bool b2 = t >= 2.f, b4 = t >= 4.f;
-  const float f = b4 ? 2.f : (b2 ? 4.f : 8.f);
-  const float inv = b4 ? 0.5f : (b2 ? 0.25f : 0.125f);
-  const uint32_t off = b4 ? 16u : (b2 ? 8u : 0u);
-  const float r = rintf(t * f);
-  const uint32_t sign = y < 0.f ? 0x80000000u : 0u;
-  qv = __uint_as_float(__float_as_uint(r * inv) | sign);
-  return ((uint32_t)r + off) | (sign >> 26);
-}
-
-// Pack 32 six-bit codes into 6 dwords (code i at bits [6i, 6i+6)).
-__device__ __forceinline__ void pack_fp6x32(const uint32_t c[32], uint32_t w[6]) {
-#pragma unroll
-  for (int j = 0; j < 6; ++j) w[j] = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int bit = 6 * i, wi = bit >> 5, sh = bit & 31;
-    w[wi] |= c[i] << sh;
-    if (sh > 26) w[wi + 1] |= c[i] >> (32 - sh);
-  }
-}
-
-// Encode one group of 32 values into hi and lo planes (6 dwords each) and their scale codes.
+// Encode one group of 32 values into hi and lo planes (6 dwords each) and their scale
+// codes. v_cvt_scalef32_2xpk16_fp6_f32 rounds x / scale to E2M3 (nearest even, saturating
+// at 7.5) and packs src0[j] at code position 2j and src1[j] at 2j + 1;
+// v_cvt_scalef32_pk32_f32_fp6 returns code value * scale in position order. Feeding the
+// even- and odd-indexed values puts value i at position i.
 __device__ __forceinline__ void fp6_encode_group(const float v[32], uint32_t hi[6], uint32_t lo[6], uint32_t& s_hi,
                                                  uint32_t& s_lo) {
+  fp6_f32x16_t ev, od;
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  float inv;
-  s_hi = fp6_scale_code(amax, inv);
-  const float x_hi = __uint_as_float(s_hi ? (s_hi << 23) : 0x00400000u);  // 2^(s_hi - 127)
-  uint32_t c[32];
-  float r[32];
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = v[2 * i];
+    od[i] = v[2 * i + 1];
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  s_hi = fp6_scale_code(amax);
+  const float x_hi = e8m0_value(s_hi);
+  const fp6_u32x6_t h = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, x_hi);
+  const fp6_f32x32_t q = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h, x_hi);
   float ramax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float qv;
-    c[i] = e2m3_round(v[i] * inv, qv);
-    r[i] = v[i] - qv * x_hi;  // exact: qv * x_hi and v[i] are within a factor of two or qv = 0
-    ramax = fmaxf(ramax, fabsf(r[i]));
+  for (int i = 0; i < 16; ++i) {
+    // exact: v and its hi value are within a factor of two of each other, or the hi value is 0
+    ev[i] = v[2 * i] - q[2 * i];
+    od[i] = v[2 * i + 1] - q[2 * i + 1];
+    ramax = fmaxf(ramax, fmaxf(fabsf(ev[i]), fabsf(od[i])));
   }
-  pack_fp6x32(c, hi);
-  s_lo = fp6_scale_code(ramax, inv);
+  s_lo = fp6_scale_code(ramax);
+  const fp6_u32x6_t l = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, e8m0_value(s_lo));
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float qv;
-    c[i] = e2m3_round(r[i] * inv, qv);
+  for (int j = 0; j < 6; ++j) {
+    hi[j] = h[j];
+    lo[j] = l[j];
   }
-  pack_fp6x32(c, lo);
 }
 
 // Byte offsets of group g of a row inside the data and scale rows.
 __device__ __forceinline__ uint32_t fp6_data_offset(int g, int plane) {
-  return (uint32_t)((g >> 2) * kFp6StepBytes + plane * 96 + (g & 3) * 24);
+  return (uint32_t)((g >> 2) * kFp6StepBytes + (g & 3) * 48 + plane * 24);
 }
 __device__ __forceinline__ uint32_t fp6_scale_offset(int g, int plane) {
   const int w = g >> 4, s = (g >> 2) & 3, q = g & 3;

@@ -64,10 +64,10 @@ def test_small_layer_parity(name, kw):
 
 
 # The scaled-MFMA expert path: sizes multiples of 512, several K windows, experts split
-# into several jobs of at most 192 slots, ragged tails, dense shared rows over two jobs.
+# into several jobs of at most 160 slots, ragged tails, dense shared rows over two jobs.
 MFMA_SMALL = [
     ("two_windows", dict(T=96, hidden=1024, latent=1024, n_experts=8, topk=4, inter=1024, shared_inter=512)),
-    ("experts_over_192_slots_k_eq_E", dict(T=256, hidden=512, latent=512, n_experts=4, topk=4, inter=512,
+    ("experts_over_160_slots_k_eq_E", dict(T=256, hidden=512, latent=512, n_experts=4, topk=4, inter=512,
                                            shared_inter=512, norm=False)),
     ("ragged_no_shared", dict(T=37, hidden=512, latent=512, n_experts=40, topk=6, inter=512, shared_inter=0)),
     ("bias_rsf_three_windows", dict(T=200, hidden=512, latent=1536, n_experts=24, topk=5, inter=512,
@@ -301,7 +301,7 @@ def test_full_stack_layer_zipf_hot_experts():
         dl.bias = saved
     counts = out["counts"]
     hot = int(np.argmax(counts))
-    assert counts[hot] > 192  # more than one job
+    assert counts[hot] > 160  # more than one job
     hot_token = int(np.nonzero((out["topk_ids"] == hot).any(axis=1))[0][-1])
     sample = sorted({0, 2047, 4095, hot_token})
     ref = li.oracle_forward(c, {"x": x, **dense, "shared": gen.make_shared(c)}, experts=dl.oracle_experts(),
