@@ -298,19 +298,26 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   const int nks = nw * 4;
   constexpr int kStepLoads[4] = {kADma + 4, kSDma + kADma + 2, kADma + 2, kADma + 2};  // by S
   constexpr int kStepTail[4] = {4, 2, 2, 2};  // loads of a k-step issued after its A stage
-  // Prologue: scales of window 0, A stage 0, the weights of k-steps 0-2 of window 0 and
-  // their scales, interleaved with A stages 1 and 2 so that at most tail(2) + loads(3)
-  // loads follow stage 1 and tail(3) follow stage 2, as the first waits assume.
+  // Prologue: the weight scales of window 0, then the loads of k-steps -3, -2, -1 in the
+  // order those k-steps issue them (S = 1, 2, 3): the activation scales of window 0, A stage
+  // 0 and the weights of k-step 0, A stage 1 and the weights of k-step 1, A stage 2 and the
+  // weights of k-step 2. The waits at the ends of k-steps 0 and 1 then count exactly the
+  // loads issued after stages 1 and 2, as in every later k-step (a wait that allows more
+  // outstanding loads than were issued after the stage would not cover the stage).
+  load_sb(0, true);
   dma_s(0, true);
   dma_a(stage(ic<0>{}), 0, true);
   load_b(0, 0, true);
-  load_b(0, 1, true);
-  load_sb(0, true);
   dma_a(stage(ic<1>{}), 1, nks > 1);
-  load_b(0, 2, true);
+  load_b(0, 1, true);
   dma_a(stage(ic<2>{}), 2, nks > 2);
-  static_assert(2 + kADma <= kStepTail[2] + kStepLoads[3] && 0 <= kStepTail[3], "prologue order");
-  MOE_WAIT_VM_LGKM0(8 + 2 * kADma);  // scales 0 and stage 0 complete
+  load_b(0, 2, true);
+  static_assert(kStepTail[1] == 2 && kStepTail[2] == 2 && kStepTail[3] == 2 && kStepLoads[2] == kADma + 2 &&
+                    kStepLoads[3] == kADma + 2,
+                "prologue order");
+  // stage 0 and the scales before it complete: the loads after it are those of k-steps -2 and
+  // -1 and the weights of k-step 0
+  MOE_WAIT_VM_LGKM0(kStepTail[1] + kStepLoads[2] + kStepLoads[3]);
   ring_barrier();
   gather_sb();
 

@@ -64,7 +64,7 @@ def test_small_layer_parity(name, kw):
 
 
 # The scaled-MFMA expert path: sizes multiples of 512, several K windows, experts split
-# into several jobs of at most 160 slots, ragged tails, dense shared rows over two jobs.
+# into several jobs of at most 192 slots, ragged tails, dense shared rows over two jobs.
 MFMA_SMALL = [
     ("two_windows", dict(T=96, hidden=1024, latent=1024, n_experts=8, topk=4, inter=1024, shared_inter=512)),
     ("experts_over_160_slots_k_eq_E", dict(T=256, hidden=512, latent=512, n_experts=4, topk=4, inter=512,
@@ -72,6 +72,9 @@ MFMA_SMALL = [
     ("ragged_no_shared", dict(T=37, hidden=512, latent=512, n_experts=40, topk=6, inter=512, shared_inter=0)),
     ("bias_rsf_three_windows", dict(T=200, hidden=512, latent=1536, n_experts=24, topk=5, inter=512,
                                     shared_inter=1024, routed_scaling_factor=2.446, zipf_s=1.1, zipf_c=0.05)),
+    # about 128 slots per expert: jobs of 5 to 12 row tiles (every row-count bucket)
+    ("jobs_of_5_to_12_tiles", dict(T=512, hidden=512, latent=512, n_experts=8, topk=2, inter=512,
+                                   shared_inter=512)),
 ]
 
 
