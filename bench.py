@@ -227,13 +227,23 @@ def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False):
         step(i)
     torch.cuda.synchronize()
 
-    L.moe_latent_timing_enable(True)
+    # The timed steps run uninstrumented: an event between two launches on the stream
+    # costs a gap of several microseconds on the GPU.
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+
+    # The same steps again with the library's stage events (HIP events recorded on the
+    # launch stream at every stage boundary): per-stage times and the kernel durations of
+    # the roofline. They include the event gaps, so they read slightly long.
+    L.moe_latent_timing_enable(True)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
     L.moe_latent_timing_enable(False)
     stages, nf = L.moe_latent_timing_read()
     del ws
