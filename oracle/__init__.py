@@ -24,6 +24,10 @@ float64 from exactly upcast inputs (bf16 and MXFP4 values are exact in fp64):
                      plus the full-width shared experts (WASTE page, "Port
                      status" table row "latent MoE"; K3 report review,
                      section "Stable LatentMoE")
+  mxfp8              MXFP8 activations of the routed experts (E4M3 elements,
+                     one E8M0 scale per 32), the deployment numerics of the K3
+                     report review (quantization-aware training section);
+                     layer.forward(act="mxfp8") uses them
   brute              a pure-Python scalar twin of the whole layer for tiny
                      sizes, written independently (bit-field decoding, explicit
                      loops) and used only as a cross-check.
@@ -34,5 +38,5 @@ Readings where the pages are silent are listed in the module docstrings of
 Parity status: every function here is pinned by the CPU tests (pages' facts,
 closed forms, invariants, brute force); none is "parity unpinned".
 """
-from . import numerics, mxfp4, layer  # noqa: F401
+from . import numerics, mxfp4, mxfp8, layer  # noqa: F401
 from .layer import forward, route, align, rmsnorm, silu  # noqa: F401

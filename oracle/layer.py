@@ -45,6 +45,7 @@ from typing import Callable, Optional, Sequence
 
 import numpy as np
 
+from . import mxfp8
 from .mxfp4 import decode_glu_record
 from .numerics import bf16_to_f64, f64_to_bf16
 
@@ -159,16 +160,22 @@ def _expert_source(experts) -> Callable[[int], tuple]:
     return lambda e: (packed[e], scales[e])
 
 
-def expert_ffn(z_rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """One routed expert on latent rows: (SiLU(z W1^T) * (z W3^T)) W2^T."""
-    return glu(z_rows @ w1.T, z_rows @ w3.T) @ w2.T
+def expert_ffn(z_rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray, act: str = "bf16") -> np.ndarray:
+    """One routed expert on latent rows: (SiLU(z W1^T) * (z W3^T)) W2^T.
+
+    act="mxfp8": the expert's inputs are MXFP8 (mxfp8.py): z_rows are expected already
+    quantized, and the GLU output is quantized before w2."""
+    h = glu(z_rows @ w1.T, z_rows @ w3.T)
+    if act == "mxfp8":
+        h = mxfp8.quantize(h)
+    return h @ w2.T
 
 
 def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.ndarray],
             router_w: np.ndarray, select_bias: Optional[np.ndarray], experts,
             up_bits: np.ndarray, shared: Optional[tuple], k: int, *,
             inter: int, shared_inter: int = 0, rms_eps: float = 1e-6, rsf: float = 1.0,
-            align_block: int = 16, tokens: Optional[Sequence[int]] = None) -> dict:
+            align_block: int = 16, tokens: Optional[Sequence[int]] = None, act: str = "bf16") -> dict:
     """Evaluate the layer.
 
     x_bits bf16 [T, H]; down_bits bf16 [L, H]; norm_bits bf16 [L] or None;
@@ -179,7 +186,14 @@ def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.nd
 
     Routing and align cover all T tokens. Per-token results (z, O, c, c_norm,
     y_routed, y_shared, y) are computed for `tokens` (default: all), in that
-    order."""
+    order.
+
+    act="bf16" (default): the routed experts read the latent and the GLU output as
+    they are. act="mxfp8": they read MXFP8 activations (mxfp8.py), the latent
+    rounded to bf16 and then quantized, the GLU output quantized before w2; the
+    shared experts, projections and router are unchanged."""
+    if act not in ("bf16", "mxfp8"):
+        raise ValueError("act must be 'bf16' or 'mxfp8'")
     X = bf16_to_f64(x_bits)
     T, H = X.shape
     Wd = bf16_to_f64(down_bits)
@@ -197,12 +211,13 @@ def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.nd
     # routed experts: each expert decoded once, applied to its rows
     get = _expert_source(experts)
     ids_s = r["ids"][toks]
+    z_in = mxfp8.quantize(bf16_to_f64(f64_to_bf16(z))) if act == "mxfp8" else z
     O = np.zeros((len(toks), k, L))
     for e in np.unique(ids_s):
         rows, slots = np.nonzero(ids_s == e)
         p, s = get(int(e))
         w1, w3, w2 = decode_glu_record(p, s, L, inter)
-        O[rows, slots] = expert_ffn(z[rows], w1, w3, w2)
+        O[rows, slots] = expert_ffn(z_in[rows], w1, w3, w2, act)
 
     w_s = r["weights"][toks]
     c = np.einsum("tj,tjl->tl", w_s, O)                    # weighted combine over slots

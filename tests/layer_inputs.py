@@ -32,13 +32,13 @@ def build(c, layer=0, experts=True):
     return d
 
 
-def oracle_forward(c, d, tokens=None, align_block=16, experts=None):
+def oracle_forward(c, d, tokens=None, align_block=16, experts=None, act="bf16"):
     from oracle import layer
     ex = (d["exp_packed"], d["exp_scales"]) if experts is None else experts
     return layer.forward(d["x"], d["down"], d["norm"], d["router"], d["select_bias"], ex,
                          d["up"], d["shared"], c.topk, inter=c.inter, shared_inter=c.shared_inter,
                          rms_eps=c.rms_eps, rsf=c.routed_scaling_factor, align_block=align_block,
-                         tokens=tokens)
+                         tokens=tokens, act=act)
 
 
 def encode_mxfp4(values, scale_codes):
