@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "latent-MoE layer tokens/s; % peak HBM GB/s (decode), % MXFP4 MFMA (prefill)"
 HBM_PEAK_GBS = 8000.0
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4/MXFP6 MFMA, MI355X
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA (an MXFP8 x MXFP4 product runs at this rate)
 
 
 def log(msg):
@@ -128,12 +129,19 @@ def main():
     log(f"inputs resident in HBM in {time.time() - t0:.1f} s")
 
     record = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L)
+    if c.name == "decode16":
+        # the same decode with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
+        record["decode_mxfp8"] = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L, summary=True,
+                                         act_format=1)
     if not args.no_prefill and c.name == "decode16":
         # the 8192-token prefill on the same resident layer (the scaled-MFMA expert path)
         cp = gen.named_config("prefill8192")
         xp_bits = gen.make_x(cp, 0, T=2 * cp.T)
         xp = [to_dev_bf16(xp_bits[i * cp.T:(i + 1) * cp.T]) for i in range(2)]
         record["prefill"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2, summary=True)
+        # the same prefill with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
+        record["prefill_mxfp8"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2,
+                                          summary=True, act_format=1)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
     print(json.dumps(record), flush=True)
@@ -200,12 +208,13 @@ def uses_mfma_path(c) -> bool:
     return sizes and c.T * c.topk >= 32 * c.n_experts
 
 
-def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False):
+def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False, act_format=0):
     """Time `steps` forwards of config c over `rotate` resident token batches; returns the
-    JSON record (or, with summary, the fields of a secondary measurement)."""
+    JSON record (or, with summary, the fields of a secondary measurement). act_format 1:
+    MXFP8 activations of the routed experts."""
     import torch
     from workload import gen
-    dims = dl.dims(c.T)
+    dims = dl.dims(c.T, act_format=act_format)
     ws = torch.empty(L.moe_latent_workspace_size(dims, c.topk), dtype=torch.uint8, device="cuda")
     y = torch.empty((c.T, c.hidden), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
@@ -256,19 +265,23 @@ def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False):
     gu_ms, dn_ms = stage_ms["expert_gate_up"], stage_ms["expert_down"]
     workload = (f"{c.name}: one K3 latent-MoE layer, T={c.T} tokens, hidden {c.hidden}, latent {c.latent}, "
                 f"{c.n_experts} MXFP4 experts top-{c.topk}, intermediate {c.inter}, RMSNorm={c.norm}, shared GLU "
-                f"{c.shared_inter}; weights MXFP4 (E2M1 + E8M0/32), activations bf16, fp32 accumulation")
+                f"{c.shared_inter}; weights MXFP4 (E2M1 + E8M0/32), activations "
+                + ("of the routed experts MXFP8 (E4M3 + E8M0/32), others bf16" if act_format else "bf16")
+                + ", fp32 accumulation")
     if uses_mfma_path(c):
         # algorithmic flops of the gate/up launch (routed pairs and shared rows, gate and up)
         gu_flops = 4.0 * pairs * c.latent * c.inter + 4.0 * c.T * c.hidden * c.shared_inter
         all_flops = 6.0 * pairs * c.latent * c.inter + 6.0 * c.T * c.hidden * c.shared_inter
         tf = gu_flops / (gu_ms * 1e-3) / 1e12
+        peak = MFMA_FP8_PEAK_TFLOPS if act_format else MFMA_FP4_PEAK_TFLOPS
+        fmt = ("MXFP8 routed activations (FP8 x FP4 rate), FP6 hi/lo shared" if act_format
+               else "FP6 hi/lo activations")
         roofline = {"bound": "mfma", "kernel": "mx_mfma_kernel<GLU> (routed + shared MXFP4 gate/up + GLU, "
-                                                "scaled MFMA, FP6 hi/lo activations)",
-                    "achieved": round(tf, 1), "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(c.name),
+                                                f"scaled MFMA, {fmt})",
+                    "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tf / peak, 4), "traffic": None if act_format else measured_traffic(c.name),
                     "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 5)}
-        extra = {"expert_kernels_mfma_frac": round(all_flops / ((gu_ms + dn_ms) * 1e-3) / 1e12
-                                                   / MFMA_FP4_PEAK_TFLOPS, 4)}
+        extra = {"expert_kernels_mfma_frac": round(all_flops / ((gu_ms + dn_ms) * 1e-3) / 1e12 / peak, 4)}
     else:
         gu_per_expert = 2 * (c.inter * c.latent // 2 + c.inter * c.latent // 32)     # w1 + w3, packed + scales
         dn_per_expert = c.latent * c.inter // 2 + c.latent * c.inter // 32

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 2
+#define MOE_LATENT_ABI_VERSION 3
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, negative or inconsistent size */
@@ -60,6 +60,20 @@ extern "C" {
 #define MOE_PATH_STREAM 1
 #define MOE_PATH_MFMA 2
 
+/* Activation format of the routed experts (moe_latent_dims.act_format).
+ *   MOE_ACT_BF16: the experts read the bf16 latent and the bf16-precision GLU
+ *     output (the MFMA path's hi/lo MXFP6 encoding keeps about 8 significant
+ *     bits of them).
+ *   MOE_ACT_MXFP8: both expert inputs are MXFP8 -- E4M3 elements, one E8M0
+ *     scale 2^(floor(log2 amax) - 8) per 32 consecutive values of a row,
+ *     round to nearest even, saturation at 448 (OCP Microscaling v1.0) -- the
+ *     deployment numerics the K3 report review describes in its
+ *     quantization-aware training section (MXFP4 weights, MXFP8 activations).
+ *     The shared experts, projections and router keep their precision; the
+ *     z tap reports the latent before quantization. */
+#define MOE_ACT_BF16 0
+#define MOE_ACT_MXFP8 1
+
 /* Layer sizes. Limits checked by every call (else MOE_EUNSUPPORTED):
  * hidden, latent, inter, shared_inter multiples of 256 (512 for MOE_PATH_MFMA);
  * 1 <= n_experts <= 4096; latent <= 8192; align_block 0 (library choice, 16) or
@@ -77,6 +91,7 @@ typedef struct moe_latent_dims {
   float rms_eps;               /* RMSNorm epsilon (1e-6) */
   float routed_scaling_factor; /* 1.0 for K3 */
   int32_t expert_path;         /* MOE_PATH_* */
+  int32_t act_format;          /* MOE_ACT_* */
 } moe_latent_dims;
 
 /* Router (WASTE page, "Shape" router row and "Against the technical report"). */
@@ -186,8 +201,22 @@ int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts
                          size_t scratch_bytes, void* stream);
 
 /*
+ * The MXFP8 rounding that MOE_ACT_MXFP8 applies to the routed experts' inputs
+ * (K3 report review, quantization-aware training section; element and scale
+ * rules of OCP Microscaling v1.0 as stated at MOE_ACT_MXFP8): y = the MXFP8
+ * value of x per block of 32 consecutive values of a row, stored back in bf16.
+ *   x, y   bf16 [rows, K] device, 16-byte aligned; y may equal x (in place),
+ *          other overlaps are MOE_EALIAS
+ *   K      multiple of 32; rows >= 0 (0 enqueues nothing)
+ * Results are exact, down to magnitudes of 2^-126 (below that the bf16 store
+ * rounds). Each element's rounding decision is taken on the exact quotient
+ * x / 2^s, so it matches any exact evaluation bit for bit.
+ */
+int moe_mxfp8_round(const void* x, int rows, int K, void* y, void* stream);
+
+/*
  * Stage timing for measurement. While enabled, moe_latent_forward records HIP
- * events around each stage on its stream (at most 4096 forwards are kept).
+ * events around each stage on its stream (at most 256 forwards are kept).
  * moe_latent_timing_read synchronises on the recorded events and returns, per
  * stage, the summed milliseconds and the number of forwards recorded; it then
  * clears the record. Stage names: moe_latent_stage_name(i), i < stage count.

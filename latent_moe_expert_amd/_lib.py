@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_latent.so")
 
 MOE_OK = 0
 PATH_AUTO, PATH_STREAM, PATH_MFMA = 0, 1, 2
+ACT_BF16, ACT_MXFP8 = 0, 1
 ERRORS = {-1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EALIAS", -4: "MOE_EWORKSPACE", -5: "MOE_EHIP",
           -6: "MOE_EABI"}
 
@@ -17,7 +18,8 @@ class MoeLatentDims(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("T", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("latent", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("align_block", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("routed_scaling_factor", ctypes.c_float), ("expert_path", ctypes.c_int32)]
+                ("routed_scaling_factor", ctypes.c_float), ("expert_path", ctypes.c_int32),
+                ("act_format", ctypes.c_int32)]
 
 
 class MoeRouter(ctypes.Structure):
@@ -38,7 +40,8 @@ class MoeLatentTaps(ctypes.Structure):
 
 EXPORTS = ["moe_latent_abi_version", "moe_latent_strerror", "moe_latent_last_hip_error",
            "moe_latent_workspace_size", "moe_latent_align_layout", "moe_latent_forward", "moe_latent_forward_ex",
-           "moe_route", "moe_align_workspace_size", "moe_align_block_size", "moe_latent_timing_enable",
+           "moe_route", "moe_align_workspace_size", "moe_align_block_size", "moe_mxfp8_round",
+           "moe_latent_timing_enable",
            "moe_latent_stage_count", "moe_latent_stage_name", "moe_latent_timing_read"]
 
 _lib = None
@@ -68,6 +71,7 @@ def load() -> ctypes.CDLL:
         "moe_route": ([D, P, ctypes.POINTER(MoeRouter), I, P, P, P, P], I),
         "moe_align_workspace_size": ([I, I, I, ctypes.POINTER(SZ)], I),
         "moe_align_block_size": ([P, I, I, I, I, P, P, P, P, P, P, SZ, P], I),
+        "moe_mxfp8_round": ([P, I, I, P, P], I),
         "moe_latent_timing_enable": ([I], I),
         "moe_latent_stage_count": ([], I),
         "moe_latent_stage_name": ([I], ctypes.c_char_p),

@@ -27,7 +27,8 @@ constexpr int kMaxLatent = 8192;
 
 // ------------------------------------------------------------------ stage timing
 enum Stage { kProjRouter, kTopk, kAlign, kActEncode, kExpGateUp, kExpDown, kCombine, kUpProj, kNumStages };
-// act_encode: the MXFP6 encoding of the contraction inputs (MOE_PATH_MFMA; ~0 otherwise).
+// act_encode: the MXFP6 or MXFP8 encoding of the contraction inputs (MOE_PATH_MFMA), or
+// the MXFP8 rounding of z (MOE_PATH_STREAM with MOE_ACT_MXFP8); ~0 otherwise.
 // The shared experts' contractions run inside the expert_gate_up / expert_down launches.
 const char* kStageNames[kNumStages] = {"proj_router", "topk", "align", "act_encode", "expert_gate_up",
                                        "expert_down", "combine_norm", "up_proj"};
@@ -57,9 +58,10 @@ struct Plan {
   int T, H, L, E, I, Is, k, B, cap, pairs;
   bool small;      // T <= 64: split-K streaming projections
   bool mfma;       // expert contractions on the scaled MFMA (MOE_PATH_MFMA)
+  bool fp8;        // MXFP8 activations of the routed experts (MOE_ACT_MXFP8)
   int max_jobs;    // mfma: capacity of the job table
   int sz, sr, su;  // K slices of the down-projection, the router and the up-projection
-  size_t z, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
+  size_t z, z8, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
   size_t z_part, r_part, y_part;
   size_t zq, zqs, xq, xqs, hq, hqs, hsq, hsqs, jobs, n_jobs;  // mfma: FP6 activations and the job table
   size_t wr3;      // T > 64: router weight split into three bf16 planes [E, 3H]
@@ -88,6 +90,7 @@ int check_dims(const moe_latent_dims* d, int topk) {
   if (d->n_experts > kMaxExperts || topk > kMaxTopk || d->latent > kMaxLatent) return MOE_EUNSUPPORTED;
   if (d->align_block % 16) return MOE_EUNSUPPORTED;
   if (d->expert_path < MOE_PATH_AUTO || d->expert_path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_MXFP8) return MOE_EINVAL;
   if (d->expert_path == MOE_PATH_MFMA && !mfma_sizes_ok(d)) return MOE_EUNSUPPORTED;
   if ((long long)d->T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
   // activation tensors the kernels index with 32-bit byte offsets stay below 2 GiB
@@ -113,6 +116,7 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.small = p.T <= 64;
   p.mfma = d->expert_path == MOE_PATH_MFMA ||
            (d->expert_path == MOE_PATH_AUTO && mfma_sizes_ok(d) && (long long)p.pairs >= 32ll * p.E);
+  p.fp8 = d->act_format == MOE_ACT_MXFP8;
   p.max_jobs = p.mfma ? moe::mx_max_jobs(p.pairs, p.E, moe::kMfmaSlotsPerJob) : 0;
   p.sz = slices(p.H, 2);
   p.sr = slices(p.H, 4);
@@ -124,6 +128,7 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
     return at;
   };
   p.z = take((size_t)p.T * p.L * 2);
+  p.z8 = take(p.fp8 && !p.mfma ? (size_t)p.T * p.L * 2 : 0);  // stream: the MXFP8 values of z, bf16
   p.logits = take((size_t)p.T * p.E * 4);
   p.ids = take((size_t)p.pairs * 4);
   p.w = take((size_t)p.pairs * 4);
@@ -337,7 +342,10 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     uint8_t* hsqs = at<uint8_t>(ws, p.hsqs);
     const int4* jobs = at<int4>(ws, p.jobs);
     const int32_t* n_jobs = at<int32_t>(ws, p.n_jobs);
-    MOE_HIP(moe::launch_quant_fp6(z, p.L, p.T, p.L, zq, zqs, s));
+    if (p.fp8)
+      MOE_HIP(moe::launch_quant_fp8(z, p.L, p.T, p.L, zq, zqs, s));
+    else
+      MOE_HIP(moe::launch_quant_fp6(z, p.L, p.T, p.L, zq, zqs, s));
     if (shared) MOE_HIP(moe::launch_quant_fp6((const uint16_t*)x, p.H, p.T, p.H, xq, xqs, s));
     STAGE_MARK(4);
     {
@@ -360,6 +368,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
         g.outqs = hsqs;
       }
       moe::MfmaProblem& g = m.p[n++];
+      g.fp8 = p.fp8;
       g.Aq = zq;
       g.Aqs = zqs;
       g.a_rows = p.T;
@@ -402,6 +411,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
         dn.ldo = p.H;
       }
       moe::MfmaProblem& g = m.p[n++];
+      g.fp8 = p.fp8;
       g.Aq = hq;
       g.Aqs = hqs;
       g.a_rows = p.cap;
@@ -425,7 +435,13 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     }
     STAGE_MARK(6);
   } else {
-  STAGE_MARK(4);  // no activation encoding on this path
+  const uint16_t* z_in = z;
+  if (p.fp8) {  // the MXFP8 values of z; the GLU epilogue rounds h the same way
+    uint16_t* z8 = at<uint16_t>(ws, p.z8);
+    MOE_HIP(moe::launch_qdq_fp8(z, p.L, p.T, p.L, z8, p.L, s));
+    z_in = z8;
+  }
+  STAGE_MARK(4);
   {
     moe::MxArgs m{};
     int n = 0;
@@ -446,7 +462,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
       g.ldo = p.Is;
     }
     moe::MxProblem& g = m.p[n++];
-    g.A = z;
+    g.A = z_in;
     g.lda = p.L;
     g.routed = 1;
     g.a_by_pos = 0;
@@ -467,6 +483,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     g.K = p.L;
     g.out = h;
     g.ldo = p.I;
+    g.out_fp8 = p.fp8;
     m.nprob = n;
     MOE_HIP(moe::launch_mx_small(m, s));
   }
@@ -619,6 +636,16 @@ int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts
   if (scratch_bytes < moe::align_scratch_bytes(T, n_experts) || (!scratch && scratch_bytes)) return MOE_EWORKSPACE;
   MOE_HIP(moe::launch_align(topk_ids, T, topk, n_experts, block, counts, sorted_ids, expert_ids, num_post, inv_pos,
                             scratch, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_mxfp8_round(const void* x, int rows, int K, void* y, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15)) return MOE_EINVAL;
+  const size_t bytes = (size_t)rows * K * 2;
+  if (x != y && overlap(x, bytes, y, bytes)) return MOE_EALIAS;
+  MOE_HIP(moe::launch_qdq_fp8((const uint16_t*)x, K, rows, K, (uint16_t*)y, K, (hipStream_t)stream));
   return MOE_OK;
 }
 

@@ -128,6 +128,7 @@ struct MxProblem {
   // output: GLU -> bf16 [rows, ldo] = act(gate) * up; plain -> f32 [rows, ldo]
   void* out;
   int ldo;
+  int out_fp8;                // GLU: h rounded to its MXFP8 value per 32 columns before the bf16 store
 };
 
 // Up to two problems of the same kind (both GLU or both plain) in one launch;
@@ -144,6 +145,15 @@ hipError_t launch_mx_small(const MxArgs& a, hipStream_t s);
 hipError_t launch_quant_fp6(const uint16_t* A, int lda, int rows, int K, uint8_t* data, uint8_t* scales,
                             hipStream_t s);
 
+// ---------------------------------------------------------------- MXFP8 activations (mxfp8.h)
+// out = the MXFP8 value of in, per 32 consecutive values of a row, stored as bf16 (exact
+// down to 2^-126); rows x K with K % 32 == 0; in and out may be the same buffer.
+hipError_t launch_qdq_fp8(const uint16_t* in, int ld_in, int rows, int K, uint16_t* out, int ld_out,
+                          hipStream_t s);
+// bf16 [rows, lda] -> MXFP8 tensor (E4M3 codes [rows, K], scales [rows, K/32], layout in mxfp8.h); K % 512 == 0
+hipError_t launch_quant_fp8(const uint16_t* A, int lda, int rows, int K, uint8_t* data, uint8_t* scales,
+                            hipStream_t s);
+
 // Work list of the grouped MFMA contraction: one job per chunk of at most `slots_per_job`
 // token slots of one expert, in the expert-sorted layout with block B.
 // jobs[j] = {first slot, valid slots, expert, 0}; *n_jobs = number of jobs.
@@ -151,10 +161,11 @@ int mx_max_jobs(int pairs, int E, int slots_per_job);
 hipError_t launch_mx_jobs(const int32_t* counts, int E, int B, int slots_per_job, int4* jobs, int32_t* n_jobs,
                           hipStream_t s);
 
-// Grouped MXFP4 contraction on the scaled MFMA: A = FP6 hi/lo activations, B = MXFP4 weights.
+// Grouped MXFP4 contraction on the scaled MFMA: A = FP6 hi/lo or MXFP8 activations, B = MXFP4 weights.
 struct MfmaProblem {
-  const uint8_t* Aq;          // FP6 data of the A rows (row stride 1.5*K bytes)
-  const uint8_t* Aqs;         // FP6 scales (row stride K/16 bytes)
+  int fp8;                    // 0: A (and a GLU's h) in FP6 hi/lo (mxfp6.h); 1: in MXFP8 (mxfp8.h)
+  const uint8_t* Aq;          // A data (row stride 1.5*K bytes FP6, K bytes FP8)
+  const uint8_t* Aqs;         // A scales (row stride K/16 bytes FP6, K/32 bytes FP8)
   int a_rows;                 // rows of the A tensor (bounds its buffer resources)
   int routed;                 // 1: jobs from the table below; 0: dense rows 0..M-1
   int a_by_pos;               // routed: A row = slot position; else sorted_ids[slot] / topk
@@ -170,7 +181,7 @@ struct MfmaProblem {
   const uint8_t* S2;
   size_t w_stride, s_stride;
   int N, K;                   // GLU: N = h width, multiple of 512; plain: N multiple of 256; K multiple of 512
-  uint8_t* outq;              // GLU: FP6 h rows (routed: slot position, dense: row), width N
+  uint8_t* outq;              // GLU: h rows in A's format (routed: slot position, dense: row), width N
   uint8_t* outqs;
   float* outf;                // plain: fp32 [row, ldo] (routed: slot position)
   int ldo;

@@ -12,8 +12,10 @@
 // group q = lane/16 owns K block q) and one E8M0 scale for them. The weights are
 // the B operand straight from their shipped layout: a lane's 32 weights are one
 // E8M0 group, 16 bytes of a row, so the MXFP4 bytes and their scale bytes go
-// into the MFMA unchanged. The activations are the A operand in the FP6 E2M3
-// hi/lo encoding (mxfp6.h); hi and lo each take one MFMA at the FP4 rate.
+// into the MFMA unchanged. The activations are the A operand, per problem either
+// in the FP6 E2M3 hi/lo encoding (mxfp6.h; hi and lo each take one MFMA at the
+// FP4 rate) or, with MXFP8 activations, as E4M3 codes (mxfp8.h; one MFMA at the
+// FP8 rate, two thirds of the bytes per k-step).
 //
 // K order. K-step k gives lane group q the E8M0 group 4k + q, so one weight load
 // instruction covers 64 contiguous bytes of each of 16 rows. A lane's scales for
@@ -23,7 +25,7 @@
 // gathered order already.
 //
 // Dataflow per block (8 waves, 2 per SIMD). The A rows of a k-step (192 rows x
-// 192 bytes, gathered through the sorted token ids) go to LDS by LDS-DMA loads
+// 192 bytes FP6 or 128 FP8, gathered through the sorted token ids) go to LDS by LDS-DMA loads
 // (no registers), into a ring of four stages, three k-steps ahead of their use;
 // every wave reads all of them, one barrier per k-step. Each wave owns 32 weight
 // rows (GLU: 16 gate + the same 16 up rows) and loads them straight into MFMA
@@ -42,13 +44,14 @@
 // the target of the loads in flight.
 //
 // Epilogue. Plain: fp32 rows at the job's slot positions. GLU: h = act(gate)*up
-// goes through LDS and is written directly in the FP6 hi/lo encoding that the
-// down contraction reads.
+// goes through LDS and is written directly in the encoding (FP6 hi/lo or MXFP8)
+// that the down contraction reads.
 #include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
 #include "mxfp6.h"
+#include "mxfp8.h"
 
 namespace moe {
 
@@ -58,18 +61,41 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMF = kMfmaSlotsPerJob / 16;  // row tiles per job
 constexpr int kRows = kMfmaSlotsPerJob;     // 192
-constexpr int kArow = 192;                  // LDS bytes per staged row (12 chunks of 16 B, rotated)
-constexpr int kADmaMax = (kRows * 12 + kThreads - 1) / kThreads;  // LDS-DMA loads per thread per stage
-constexpr int kAStage = kRows * kArow;                            // bytes per A stage
-// The last LDS-DMA round of a stage covers only part of the block; the waves past the
-// stage's end load zeros into a dummy area instead (same load count in every wave).
-constexpr int kADummy = kADmaMax * kThreads * 16 - kAStage;
+
+// Activation formats of the A operand. Per row and k-step (128 K values): FP6 hi/lo takes
+// 12 chunks of 16 bytes (two planes of 4 x 24 bytes), MXFP8 8 chunks (4 x 32 bytes); per
+// row and window (512 K values) their scales take 32 and 16 bytes.
+template <bool FP8>
+struct AFmt {
+  static constexpr int kChunks = FP8 ? 8 : 12;         // 16-byte chunks per row per k-step
+  static constexpr int kArow = kChunks * 16;           // LDS bytes per staged row
+  static constexpr int kStep = FP8 ? 128 : kFp6StepBytes;
+  static constexpr int kWinScale = FP8 ? kFp8WindowScaleBytes : kFp6WindowScaleBytes;
+  static constexpr int kSChunks = kWinScale / 16;      // 16-byte scale chunks per row per window
+  static constexpr int kPlanes = FP8 ? 1 : 2;          // MFMAs per (row tile, B tile, k-step)
+  static constexpr int kAStage = kRows * kArow;        // bytes per A stage
+  static constexpr int kADmaMax = (kRows * kChunks + kThreads - 1) / kThreads;
+  // the last LDS-DMA round of a stage may cover only part of the block; the waves past
+  // the stage's end load zeros into a dummy area instead (same load count in every wave)
+  static constexpr int kADummy = kADmaMax * kThreads * 16 - kAStage;
+  __host__ __device__ static size_t row_bytes(int K) { return FP8 ? fp8_row_bytes(K) : fp6_row_bytes(K); }
+  __host__ __device__ static size_t scale_row_bytes(int K) {
+    return FP8 ? fp8_scale_row_bytes(K) : fp6_scale_row_bytes(K);
+  }
+};
+using F6 = AFmt<false>;
+using F8 = AFmt<true>;
+// the kernel's LDS is laid out for FP6 hi/lo, the larger format
+constexpr int kAStage = F6::kAStage;
 constexpr int kSDma = 1;                    // 16-byte scale chunks per thread per window
 constexpr int kSStage = kSDma * kThreads * 16;
+constexpr int kADummy = F6::kADummy;
 constexpr int kHRow = 132;                  // floats per row of the GLU epilogue tile
 constexpr int kHRowsPerArray = 48;          // rows of h per ring array in the GLU epilogue
-static_assert(kADummy >= 0 && kADummy % 1024 == 0 && kAStage % 1024 == 0, "A stage");
-static_assert(kRows * 2 <= kSDma * kThreads, "scale chunks");
+static_assert(F6::kADummy >= 0 && F6::kADummy % 1024 == 0 && F6::kAStage % 1024 == 0, "A stage");
+static_assert(F8::kADummy == 0 && F8::kAStage % 1024 == 0 && F8::kAStage + kSStage <= kAStage + kSStage,
+              "FP8 stage inside the FP6 arrays");
+static_assert(kRows * F6::kSChunks <= kSDma * kThreads && kRows * F8::kSChunks <= kSDma * kThreads, "scale chunks");
 static_assert(kHRowsPerArray * kHRow * 4 <= kAStage && 4 * kHRowsPerArray >= kRows, "GLU epilogue tile");
 static_assert(4 * kAStage + kSStage + kADummy <= 160 * 1024, "LDS");
 
@@ -103,24 +129,34 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wav
 }
 
 // LDS position of 16-byte chunk c of a staged row whose index within its 16-row tile is
-// nl. A lane group's operands are chunks 3q..3q+2 of its row: 16 bytes of hi, then 8 of
-// hi and 8 of lo, then 16 of lo; the 16 lanes of a group read the same chunk index of 16
-// rows. Rows are 12 chunks long, so unrotated rows 4 apart would share banks (64 banks
-// of 4 bytes: 16 chunks per bank cycle); rotating row nl by a_rot(nl) spreads each
-// 16-byte read over all 16 chunk slots of a bank cycle.
-__host__ __device__ constexpr int a_rot(int nl) { return ((nl >> 1) & 3) ^ ((nl >> 3) & 1); }
-__host__ __device__ constexpr int a_chunk_pos(int c, int nl) { return (c + a_rot(nl)) % 12; }
+// nl. The 16 lanes of a lane group read the same chunk index of 16 rows (64 banks of 4
+// bytes: 16 chunk slots per bank cycle), so each row is rotated to spread such a read
+// over all 16 slots.
+// FP6: a lane group's operands are chunks 3q..3q+2 (16 bytes of hi, then 8 of hi and 8
+// of lo, then 16 of lo); rows are 12 chunks long, so unrotated rows 4 apart would share
+// slots. FP8: chunks q and 4+q; rows are 8 chunks long, so rows 2 apart would.
+template <bool FP8>
+__host__ __device__ constexpr int a_rot(int nl) {
+  return FP8 ? ((nl >> 1) & 7) : (((nl >> 1) & 3) ^ ((nl >> 3) & 1));
+}
+template <bool FP8>
+__host__ __device__ constexpr int a_chunk_pos(int c, int nl) {
+  return (c + a_rot<FP8>(nl)) % AFmt<FP8>::kChunks;
+}
 
 // One job (at most NT row tiles of 16) against one column tile. NT is a compile-time
 // bucket of the job's row count: every loop below is straight-line code, so each
 // k-step issues a fixed set of loads and the compiler's waits are exact.
-template <bool GLU, int NT>
+template <bool GLU, int NT, bool FP8>
 __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nvalid, int expert, int ntile,
                                        uint8_t (&lds_a0)[kAStage + kSStage], uint8_t (&lds_a1)[kAStage],
                                        uint8_t (&lds_a2)[kAStage], uint8_t (&lds_a3)[kAStage],
                                        uint8_t* lds_dummy) {
-  constexpr int kADma = (NT * 16 * 12 + kThreads - 1) / kThreads;  // LDS-DMA loads per thread per k-step
-  static_assert(kADma <= kADmaMax, "stage");
+  using Fm = AFmt<FP8>;
+  constexpr int kADma = (NT * 16 * Fm::kChunks + kThreads - 1) / kThreads;  // LDS-DMA loads per thread per k-step
+  static_assert(kADma <= Fm::kADmaMax, "stage");
+  constexpr int kArow = Fm::kArow;
+  constexpr int kFStage = Fm::kAStage;  // A bytes of a stage; the window's scales follow stage 0's
   auto stage = [&](auto I_) -> uint8_t* {
     constexpr int I = decltype(I_)::value % 4;
     if constexpr (I == 0) return lds_a0;
@@ -133,27 +169,29 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   const int nl = lane & 15, q = lane >> 4;
 
   const int K = a.K;
-  const uint32_t arow_bytes = (uint32_t)fp6_row_bytes(K), asrow_bytes = (uint32_t)fp6_scale_row_bytes(K);
+  const uint32_t arow_bytes = (uint32_t)Fm::row_bytes(K), asrow_bytes = (uint32_t)Fm::scale_row_bytes(K);
   auto a_row = [&](int j) -> int {  // A row of job slot j, -1 past the valid slots
     if (j >= nvalid) return -1;
     if (!a.routed || a.a_by_pos) return first + j;
     return a.sorted_ids[first + j] / a.topk;
   };
 
-  // ---- A stage by LDS-DMA: chunk t = tid + 512 i lands at LDS byte 16 t, i.e. position t % 12
-  // of staged row j = t / 12, and carries the row's global chunk whose rotated position that is.
+  // ---- A stage by LDS-DMA: chunk t = tid + 512 i lands at LDS byte 16 t, i.e. position
+  // t % kChunks of staged row j = t / kChunks, and carries the row's global chunk whose
+  // rotated position that is.
+  constexpr int kCh = Fm::kChunks;
   uint32_t goff[kADma];
 #pragma unroll
   for (int i = 0; i < kADma; ++i) {
-    const int t = tid + kThreads * i, j = t / 12, pos = t % 12;
-    const int c = (pos + 12 - a_rot(j & 15)) % 12;
+    const int t = tid + kThreads * i, j = t / kCh, pos = t % kCh;
+    const int c = (pos + kCh - a_rot<FP8>(j & 15)) % kCh;
     const int r = j < NT * 16 ? a_row(j) : -1;
     goff[i] = r >= 0 ? (uint32_t)r * arow_bytes + 16u * c : kOob;
   }
   uint32_t sgoff[kSDma];
 #pragma unroll
   for (int i = 0; i < kSDma; ++i) {
-    const int t = tid + kThreads * i, j = t >> 1, c = t & 1;
+    const int t = tid + kThreads * i, j = t / Fm::kSChunks, c = t % Fm::kSChunks;
     const int r = j < NT * 16 ? a_row(j) : -1;
     sgoff[i] = r >= 0 ? (uint32_t)r * asrow_bytes + 16u * c : kOob;
   }
@@ -211,17 +249,17 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   // dummy area past the stage's end (those lanes carry no row: their goff is out of range)
   auto a_dst_of = [&](uint8_t* st, int i) -> uint8_t* {
     const int o = i * (kThreads * 16) + wave * 1024;
-    return (i + 1) * (kThreads * 16) <= kAStage || o < kAStage ? st + o : lds_dummy + (o - kAStage);
+    return (i + 1) * (kThreads * 16) <= kFStage || o < kFStage ? st + o : lds_dummy + (o - kFStage);
   };
   auto dma_a = [&](uint8_t* st, int ks, bool on) {  // kADma loads
 #pragma unroll
-    for (int i = 0; i < kADma; ++i) dma16(on ? a_rs : none, a_dst_of(st, i), goff[i], (uint32_t)(ks * kFp6StepBytes));
+    for (int i = 0; i < kADma; ++i) dma16(on ? a_rs : none, a_dst_of(st, i), goff[i], (uint32_t)(ks * Fm::kStep));
   };
   auto dma_s = [&](int w, bool on) {  // kSDma loads
 #pragma unroll
     for (int i = 0; i < kSDma; ++i)
-      dma16(on ? as_rs : none, lds_a0 + kAStage + wave * 1024 + i * (kThreads * 16), sgoff[i],
-            (uint32_t)(w * kFp6WindowScaleBytes));
+      dma16(on ? as_rs : none, lds_a0 + kFStage + wave * 1024 + i * (kThreads * 16), sgoff[i],
+            (uint32_t)(w * Fm::kWinScale));
   };
 
   // Each accumulator starts from its own opaque zero: with one shared constant as the
@@ -236,19 +274,35 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
       asm volatile("" : "+a"(acc[mf][nf]));
     }
 
-  // lane (nl, q) reads the 48 bytes of its group (hi then lo plane) as chunks 3q..3q+2
-  uint32_t aoff[3];
+  // FP6: lane (nl, q) reads its group as chunks 3q .. 3q+2 (48 bytes, hi then lo plane).
+  // FP8: an FP8 operand register's first 16 bytes hold K 16q .. 16q+15 of the k-step and
+  // its last 16 bytes K 64+16q .. 64+16q+15, while K block b (32b .. 32b+31) is scaled by
+  // lane group b's scale; lane group q therefore reads chunks q and 4+q, and group
+  // 4k + q's scale stays with lane group q.
+  constexpr int kRd = FP8 ? 2 : 3;
+  uint32_t aoff[kRd];
 #pragma unroll
-  for (int u = 0; u < 3; ++u) aoff[u] = (uint32_t)(nl * kArow + a_chunk_pos(3 * q + u, nl) * 16);
+  for (int u = 0; u < kRd; ++u) {
+    const int c = FP8 ? q + 4 * u : 3 * q + u;
+    aoff[u] = (uint32_t)(nl * kArow + a_chunk_pos<FP8>(c, nl) * 16);
+  }
   // activation scale dwords of the window, read at its start: the scale area (in stage 0)
   // receives the next window's scales from k-step 1 of the window on
-  uint32_t sA[NT][2];
+  constexpr int kP = Fm::kPlanes;
+  uint32_t sA[NT][kP];
 
-  // Four reads per tile: the middle chunk is read as two halves, so each operand is one
-  // 16-byte and one 8-byte read straight into its registers (the empty asm keeps the two
-  // halves from being merged into one read whose halves would then be copied).
+  // FP6: four reads per tile: the middle chunk is read as two halves, so each operand is
+  // one 16-byte and one 8-byte read straight into its registers (the empty asm keeps the
+  // two halves from being merged into one read whose halves would then be copied).
+  // FP8: two 16-byte reads, the operand's two halves.
   auto read_a = [&](const uint8_t* st, int mf, i32x8_t* av) {
     const uint8_t* base = st + mf * 16 * kArow;
+    if constexpr (FP8) {
+      const i32x4_t x0 = *(const i32x4_t*)(base + aoff[0]);
+      const i32x4_t x1 = *(const i32x4_t*)(base + aoff[1]);
+      av[0] = i32x8_t{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      return;
+    }
     const i32x4_t x0 = *(const i32x4_t*)(base + aoff[0]);
     const int2 h1 = *(const int2*)(base + aoff[1]);
     asm volatile("" ::: "memory");
@@ -262,20 +316,21 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   // so no operand is copied. mem(mf) issues the memory operations assigned to tile mf.
   auto compute = [&](auto S_, const uint8_t* st, auto&& mem) {
     constexpr int S = decltype(S_)::value;
-    i32x8_t av[2][2];  // [row tile parity][plane]
+    i32x8_t av[2][kP];  // [row tile parity][plane]
     read_a(st, 0, av[0]);
     static_for<0, NT>([&](auto MF) {
       constexpr int mf = decltype(MF)::value;
       if constexpr (mf + 1 < NT) read_a(st, mf + 1, av[(mf + 1) & 1]);
       mem(MF);
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < kP; ++p)
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf) {
           const u32x4_t bw = b[S][nf];
           const i32x8_t bv = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
-          acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mf & 1][p], bv, acc[mf][nf], 2, 4, S,
-                                                                          (int)sA[mf][p], S, (int)sb[nf]);
+          // A format: 0 = FP8 E4M3, 2 = FP6 E2M3; B format 4 = FP4 E2M1
+          acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              av[mf & 1][p], bv, acc[mf][nf], FP8 ? 0 : 2, 4, S, (int)sA[mf][p], S, (int)sb[nf]);
         }
       // The memory clobber pins the LDS reads (IR passes may move loads across the
       // scheduling barrier, which touches no memory); the scheduling barrier then keeps
@@ -323,11 +378,11 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
 
   for (int w = 0; w < nw; ++w) {
     {
-      const uint8_t* ss = lds_a0 + kAStage + nl * kFp6WindowScaleBytes + q * 4;
+      const uint8_t* ss = lds_a0 + kFStage + nl * Fm::kWinScale + q * 4;
 #pragma unroll
       for (int mf = 0; mf < NT; ++mf)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) sA[mf][p] = *(const uint32_t*)(ss + mf * 16 * kFp6WindowScaleBytes + p * 16);
+        for (int p = 0; p < kP; ++p) sA[mf][p] = *(const uint32_t*)(ss + mf * 16 * Fm::kWinScale + p * 16);
     }
     const bool more_w = w + 1 < nw;
     auto step = [&](auto S_) {
@@ -346,11 +401,11 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
         static_for<mf * per, (mf + 1) * per < nOps ? (mf + 1) * per : nOps>([&](auto O) {
           constexpr int o = decltype(O)::value;
           if constexpr (o < nS) {
-            dma16(more_w ? as_rs : none, lds_a0 + kAStage + wave * 1024 + o * (kThreads * 16), sgoff[o],
-                  (uint32_t)((w + 1) * kFp6WindowScaleBytes));
+            dma16(more_w ? as_rs : none, lds_a0 + kFStage + wave * 1024 + o * (kThreads * 16), sgoff[o],
+                  (uint32_t)((w + 1) * Fm::kWinScale));
           } else if constexpr (o < nS + kADma) {
             constexpr int i = o - nS;
-            dma16(a_on ? a_rs : none, a_dst_of(a_dst, i), goff[i], (uint32_t)((ks + 3) * kFp6StepBytes));
+            dma16(a_on ? a_rs : none, a_dst_of(a_dst, i), goff[i], (uint32_t)((ks + 3) * Fm::kStep));
           } else if constexpr (o < nS + kADma + 2) {
             constexpr int nf = o - nS - kADma;
             b[bs][nf] = buf_load16(b_on ? w_rs(nf) : none, bvoff[nf], (uint32_t)(256 * bw_win + 64 * bs));
@@ -392,7 +447,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   } else {
     // h tile through LDS in one pass (rows 48i.. in ring array i), then one thread per
     // (row, group of 32 columns): the eight waves' 16 columns of a row form its 4 groups.
-    const uint32_t orow_bytes = (uint32_t)fp6_row_bytes(a.N), osrow_bytes = (uint32_t)fp6_scale_row_bytes(a.N);
+    const uint32_t orow_bytes = (uint32_t)Fm::row_bytes(a.N), osrow_bytes = (uint32_t)Fm::scale_row_bytes(a.N);
     auto hrow = [&](int j) -> float* {
       const int arr = j / kHRowsPerArray;
       uint8_t* base = arr == 0 ? lds_a0 : (arr == 1 ? lds_a1 : (arr == 2 ? lds_a2 : lds_a3));
@@ -418,9 +473,18 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
           v[4 * u + 2] = x[2];
           v[4 * u + 3] = x[3];
         }
+        const int g = ntile * 4 + g4;
+        if constexpr (FP8) {
+          uint32_t codes[8], sc;
+          mxfp8_encode_group(v, codes, sc);
+          u32x4_t* d = (u32x4_t*)(a.outq + (size_t)(first + j) * orow_bytes + (size_t)g * 32);
+          d[0] = u32x4_t{codes[0], codes[1], codes[2], codes[3]};
+          d[1] = u32x4_t{codes[4], codes[5], codes[6], codes[7]};
+          a.outqs[(size_t)(first + j) * osrow_bytes + fp8_scale_offset(g)] = (uint8_t)sc;
+          continue;
+        }
         uint32_t hi[6], lo[6], s_hi, s_lo;
         fp6_encode_group(v, hi, lo, s_hi, s_lo);
-        const int g = ntile * 4 + g4;
         uint8_t* drow = a.outq + (size_t)(first + j) * orow_bytes;
         uint2* dh = (uint2*)(drow + fp6_data_offset(g, 0));
         uint2* dl = (uint2*)(drow + fp6_data_offset(g, 1));
@@ -437,7 +501,12 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   }
 }
 
-template <bool GLU>
+// Activation formats of a launch's problems: every problem FP6 hi/lo, every problem MXFP8,
+// or problem 0 FP6 and problem 1 MXFP8 (the shared experts next to MXFP8 routed experts).
+// Each combination is its own kernel, so a kernel holds only the job code it runs.
+enum LaunchFormats { kAllFp6 = 0, kAllFp8 = 1, kFp6ThenFp8 = 2 };
+
+template <bool GLU, int FMTS>
 __global__ __launch_bounds__(kThreads) void mx_mfma_kernel(MfmaArgs args) {
   // stage 0 also holds the activation scales of its window (its k-step starts the window)
   __shared__ __attribute__((aligned(16))) uint8_t lds_a0[kAStage + kSStage];
@@ -482,14 +551,25 @@ __global__ __launch_bounds__(kThreads) void mx_mfma_kernel(MfmaArgs args) {
     nvalid = min(kRows, a.M - first);
   }
   const int nmf = (nvalid + 15) >> 4;
+  const bool fp8 = FMTS == kAllFp8 || (FMTS == kFp6ThenFp8 && second);
+  if (FMTS != kAllFp6 && fp8) {
+    if (nmf <= 4)
+      mx_job<GLU, 4, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    else if (nmf <= 8)
+      mx_job<GLU, 8, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    else
+      mx_job<GLU, kMF, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    return;
+  }
+  if constexpr (FMTS == kAllFp8) return;
   if (nmf <= 4)
-    mx_job<GLU, 4>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    mx_job<GLU, 4, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else if (nmf <= 8)
-    mx_job<GLU, 8>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    mx_job<GLU, 8, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else if (nmf <= 10)
-    mx_job<GLU, 10>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    mx_job<GLU, 10, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else
-    mx_job<GLU, kMF>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    mx_job<GLU, kMF, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
 }
 
 }  // namespace
@@ -504,7 +584,8 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
     // GLU blocks cover 128 h columns and write whole FP6 windows of h; plain blocks cover 256 columns
     if (glu ? (p.N % 512) : (p.N % 256)) return hipErrorInvalidValue;
     // 32-bit byte offsets: activations, weights of one matrix, outputs
-    if (p.a_rows < 0 || (long long)p.a_rows * (long long)fp6_row_bytes(p.K) >= (1ll << 31) ||
+    const long long a_row_bytes = p.fp8 ? (long long)fp8_row_bytes(p.K) : (long long)fp6_row_bytes(p.K);
+    if (p.a_rows < 0 || (long long)p.a_rows * a_row_bytes >= (1ll << 31) ||
         (long long)p.N * p.K / 2 >= (1ll << 31) || (!p.routed && p.M > p.a_rows))
       return hipErrorInvalidValue;
     const long long jobs = p.routed ? p.max_jobs : (p.M + kRows - 1) / kRows;
@@ -513,10 +594,23 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const long long grid = blocks * 8;
   if (grid > 0x7fffffffll) return hipErrorInvalidValue;
-  if (glu)
-    hipLaunchKernelGGL(mx_mfma_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  int fmts;
+  if (a.nprob == 1 || a.p[0].fp8 == a.p[1].fp8)
+    fmts = a.p[0].fp8 ? kAllFp8 : kAllFp6;
+  else if (!a.p[0].fp8)
+    fmts = kFp6ThenFp8;
   else
-    hipLaunchKernelGGL(mx_mfma_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    return hipErrorInvalidValue;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a); };
+  if (glu) {
+    if (fmts == kAllFp6) go(mx_mfma_kernel<true, kAllFp6>);
+    else if (fmts == kAllFp8) go(mx_mfma_kernel<true, kAllFp8>);
+    else go(mx_mfma_kernel<true, kFp6ThenFp8>);
+  } else {
+    if (fmts == kAllFp6) go(mx_mfma_kernel<false, kAllFp6>);
+    else if (fmts == kAllFp8) go(mx_mfma_kernel<false, kAllFp8>);
+    else go(mx_mfma_kernel<false, kFp6ThenFp8>);
+  }
   return hipGetLastError();
 }
 

@@ -28,9 +28,12 @@
 // both operands, so no reordering of K is visible in the result).
 //
 // GLU variant: the epilogue applies act(gate) * up in registers and writes
-// bf16 h; the plain variant (w2, or the shared down) writes fp32.
+// bf16 h (with MXFP8 activations: each row's 32 columns of a wave are one
+// block, rounded to their MXFP8 values first); the plain variant (w2, or the
+// shared down) writes fp32.
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8.h"
 
 namespace moe {
 
@@ -199,20 +202,36 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     opos[r] = pos;
     valid[r] = a.routed ? (a.sorted_ids[pos] < a.pairs) : (pos < a.M);
   }
-  constexpr int kOutTiles = GLU ? 2 : 4;
+  if (GLU) {
+    // a wave's 32 columns of a row are one MXFP8 group: lanes 16q..16q+15 (tiles 0 and 1) of row 4q + r
+    float hv[2][4];
 #pragma unroll
-  for (int t = 0; t < kOutTiles; ++t) {
-    const int col = col0 + t * 16 + nl;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (!valid[r]) continue;
-      if (GLU) {
-        const float hv = glu_act(acc[t][r], acc[t + 2][r]);
-        ((uint16_t*)a.out)[(size_t)opos[r] * a.ldo + col] = (uint16_t)f32_to_bf16_bits(hv);
-      } else {
-        ((float*)a.out)[(size_t)opos[r] * a.ldo + col] = acc[t][r];
+      for (int r = 0; r < 4; ++r) hv[t][r] = glu_act(acc[t][r], acc[t + 2][r]);
+    if (a.out_fp8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = fmaxf(fabsf(hv[0][r]), fabsf(hv[1][r]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        const int sx = mxfp8_scale_exp(m);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) hv[t][r] = ldexpf(e4m3_round(ldexpf(hv[t][r], -sx)), sx);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (valid[r])
+          ((uint16_t*)a.out)[(size_t)opos[r] * a.ldo + col0 + t * 16 + nl] = (uint16_t)f32_to_bf16_bits(hv[t][r]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (valid[r]) ((float*)a.out)[(size_t)opos[r] * a.ldo + col0 + t * 16 + nl] = acc[t][r];
   }
 }
 

@@ -1,7 +1,8 @@
-// Activation encoding for the scaled-MFMA contractions, and their work list.
+// Activation encodings (MXFP6 hi/lo, MXFP8) for the expert contractions, and their work list.
 #include "common.h"
 #include "kernels.h"
 #include "mxfp6.h"
+#include "mxfp8.h"
 
 namespace moe {
 
@@ -38,6 +39,61 @@ __global__ __launch_bounds__(256) void quant_fp6_kernel(const uint16_t* __restri
   uint8_t* srow = scales + (size_t)row * fp6_scale_row_bytes(K);
   srow[fp6_scale_offset(g, 0)] = (uint8_t)s_hi;
   srow[fp6_scale_offset(g, 1)] = (uint8_t)s_lo;
+}
+
+__device__ __forceinline__ void load_bf16x32(const uint16_t* p, float v[32]) {
+  const u32x4_t* src = (const u32x4_t*)p;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t x = src[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * j + 2 * e] = bf16_bits_to_f32(x[e] & 0xffffu);
+      v[8 * j + 2 * e + 1] = bf16_bits_to_f32(x[e] >> 16);
+    }
+  }
+}
+
+// One thread per group of 32 values: the MXFP8 value of each, back in bf16.
+__global__ __launch_bounds__(256) void qdq_fp8_kernel(const uint16_t* in, int ld_in, int rows, int K, uint16_t* out,
+                                                      int ld_out) {
+  const int G = K >> 5;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)rows * G) return;
+  const int row = (int)(idx / G), g = (int)(idx % G);
+  float v[32];
+  load_bf16x32(in + (size_t)row * ld_in + (size_t)g * 32, v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int s = mxfp8_scale_exp(amax);
+  u32x4_t* dst = (u32x4_t*)(out + (size_t)row * ld_out + (size_t)g * 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4_t x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[e] = pack_bf16x2(ldexpf(e4m3_round(ldexpf(v[8 * j + 2 * e], -s)), s),
+                         ldexpf(e4m3_round(ldexpf(v[8 * j + 2 * e + 1], -s)), s));
+    dst[j] = x;
+  }
+}
+
+// One thread per group of 32 values: 64 bytes in, 32 code bytes and 1 scale byte out.
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ A, int lda, int rows, int K,
+                                                        uint8_t* __restrict__ data, uint8_t* __restrict__ scales) {
+  const int G = K >> 5;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)rows * G) return;
+  const int row = (int)(idx / G), g = (int)(idx % G);
+  float v[32];
+  load_bf16x32(A + (size_t)row * lda + (size_t)g * 32, v);
+  uint32_t codes[8], sc;
+  mxfp8_encode_group(v, codes, sc);
+  u32x4_t* d = (u32x4_t*)(data + (size_t)row * fp8_row_bytes(K) + (size_t)g * 32);
+  d[0] = u32x4_t{codes[0], codes[1], codes[2], codes[3]};
+  d[1] = u32x4_t{codes[4], codes[5], codes[6], codes[7]};
+  scales[(size_t)row * fp8_scale_row_bytes(K) + fp8_scale_offset(g)] = (uint8_t)sc;
 }
 
 // Single block: per-expert padded segment offsets (the align layout) and job counts,
@@ -93,6 +149,28 @@ hipError_t launch_quant_fp6(const uint16_t* A, int lda, int rows, int K, uint8_t
   const long long blocks = (groups + 255) / 256;
   if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_fp6_kernel, dim3((unsigned)blocks), dim3(256), 0, s, A, lda, rows, K, data, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_qdq_fp8(const uint16_t* in, int ld_in, int rows, int K, uint16_t* out, int ld_out,
+                          hipStream_t s) {
+  if (K % 32 || K < 0 || ld_in % 8 || ld_out % 8 || ld_in < K || ld_out < K || rows < 0) return hipErrorInvalidValue;
+  const long long groups = (long long)rows * (K / 32);
+  if (groups == 0) return hipSuccess;
+  const long long blocks = (groups + 255) / 256;
+  if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qdq_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, in, ld_in, rows, K, out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const uint16_t* A, int lda, int rows, int K, uint8_t* data, uint8_t* scales,
+                            hipStream_t s) {
+  if (K % 512 || lda % 8 || lda < K || rows < 0) return hipErrorInvalidValue;
+  const long long groups = (long long)rows * (K / 32);
+  if (groups == 0) return hipSuccess;
+  const long long blocks = (groups + 255) / 256;
+  if (blocks > 0x7fffffffll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, A, lda, rows, K, data, scales);
   return hipGetLastError();
 }
 

@@ -31,9 +31,9 @@ def _check(fn: str, rc: int) -> None:
 
 def make_dims(T: int, hidden: int, latent: int, n_experts: int, inter: int, shared_inter: int = 0,
               align_block: int = 0, rms_eps: float = 1e-6, routed_scaling_factor: float = 1.0,
-              expert_path: int = 0) -> MoeLatentDims:
+              expert_path: int = 0, act_format: int = 0) -> MoeLatentDims:
     return MoeLatentDims(ctypes.sizeof(MoeLatentDims), T, hidden, latent, n_experts, inter, shared_inter,
-                         align_block, rms_eps, routed_scaling_factor, expert_path)
+                         align_block, rms_eps, routed_scaling_factor, expert_path, act_format)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "") -> Optional[int]:
@@ -136,6 +136,15 @@ def moe_align_block_size(topk_ids, T: int, topk: int, n_experts: int, block: int
                                   _ptr(scratch, torch.uint8, "scratch"), 0 if scratch is None else scratch.numel(),
                                   _stream(stream))
     _check("moe_align_block_size", rc)
+
+
+def moe_mxfp8_round(x, y, stream=None) -> None:
+    """y = MXFP8 value of x (bf16 [rows, K], K % 32 == 0); y may be x."""
+    if x.dim() != 2 or tuple(y.shape) != tuple(x.shape):
+        raise ValueError("x and y: the same [rows, K] shape")
+    rc = _lib.load().moe_mxfp8_round(_ptr(x, _BF16, "x"), x.shape[0], x.shape[1], _ptr(y, _BF16, "y"),
+                                     _stream(stream))
+    _check("moe_mxfp8_round", rc)
 
 
 def moe_latent_timing_enable(on: bool) -> None:

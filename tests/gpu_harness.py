@@ -63,17 +63,17 @@ class DeviceLayer:
             self.sh_packed = torch.from_numpy(sh[0]).to(dev)
             self.sh_scales = torch.from_numpy(sh[1]).to(dev)
 
-    def dims(self, T: int, align_block: int = 0, expert_path: int = 0):
+    def dims(self, T: int, align_block: int = 0, expert_path: int = 0, act_format: int = 0):
         c = self.c
         return L.make_dims(T, c.hidden, c.latent, c.n_experts, c.inter, c.shared_inter, align_block, c.rms_eps,
-                           c.routed_scaling_factor, expert_path)
+                           c.routed_scaling_factor, expert_path, act_format)
 
     def run(self, x_bits: np.ndarray = None, x_dev: torch.Tensor = None, taps: bool = True, align_block: int = 0,
-            expert_path: int = 0):
+            expert_path: int = 0, act_format: int = 0):
         c = self.c
         x = to_dev_bf16(x_bits) if x_dev is None else x_dev
         T = x.shape[0]
-        dims = self.dims(T, align_block, expert_path)
+        dims = self.dims(T, align_block, expert_path, act_format)
         ws = torch.empty(max(L.moe_latent_workspace_size(dims, c.topk), 256), dtype=torch.uint8, device=x.device)
         y = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=x.device)
         out = {}
@@ -110,6 +110,17 @@ class DeviceLayer:
     def oracle_experts(self):
         """Expert source for the oracle: regenerate expert e from its seeded stream."""
         return lambda e: gen.make_expert(self.c, self.layer, e)
+
+
+_K3 = {}
+
+
+def k3_layer() -> DeviceLayer:
+    """Layer 0 of the K3 workloads (shared by the decode and prefill configs): 896 experts
+    on the GPU (15.7 GB), uploaded once per test session."""
+    if "layer" not in _K3:
+        _K3["layer"] = DeviceLayer(gen.named_config("decode16"))
+    return _K3["layer"]
 
 
 def maxrel(a, b) -> float:

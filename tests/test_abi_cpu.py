@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.moe_latent_abi_version() == 2
+    assert lib.moe_latent_abi_version() == 3
     for code in range(0, -7, -1):
         assert lib.moe_latent_strerror(code)
     assert lib.moe_latent_stage_count() == 8
@@ -43,7 +43,7 @@ def test_abi_version_and_strerror(lib):
 
 def _dims(**kw):
     base = dict(T=16, hidden=7168, latent=3584, n_experts=896, inter=3072, shared_inter=6144, align_block=0,
-                rms_eps=1e-6, routed_scaling_factor=1.0, expert_path=0)
+                rms_eps=1e-6, routed_scaling_factor=1.0, expert_path=0, act_format=0)
     base.update(kw)
     d = _lib.MoeLatentDims(ctypes.sizeof(_lib.MoeLatentDims), *[base[f] for f, _ in _lib.MoeLatentDims._fields_[1:]])
     return d
@@ -69,6 +69,7 @@ def test_workspace_size_and_layout(lib):
     (dict(n_experts=5000), 16, -2), (dict(T=200000), 16, -2),
     (dict(align_block=24), 16, -2), (dict(T=-1), 16, -1), (dict(n_experts=8), 9, -1),
     (dict(), 0, -1), (dict(), 65, -2), (dict(rms_eps=-1.0), 16, -1),
+    (dict(act_format=2), 16, -1), (dict(act_format=-1), 16, -1),
 ])
 def test_dims_validation(lib, kw, k, code):
     rc, _ = _ws(lib, _dims(**kw), k)
@@ -120,3 +121,18 @@ def test_timing_read_when_empty(lib):
     arr = (ctypes.c_float * 9)()
     nf = ctypes.c_int(-1)
     assert lib.moe_latent_timing_read(arr, ctypes.byref(nf)) == 0 and nf.value == 0
+
+
+def test_mxfp8_round_argument_errors(lib):
+    P, Q = 0x100000, 0x900000
+    assert lib.moe_mxfp8_round(P, -1, 64, Q, None) == -1
+    assert lib.moe_mxfp8_round(P, 4, 48, Q, None) == -1      # K not a multiple of 32
+    assert lib.moe_mxfp8_round(P, 4, 0, Q, None) == -1
+    assert lib.moe_mxfp8_round(None, 4, 64, Q, None) == -1
+    assert lib.moe_mxfp8_round(P + 8, 4, 64, Q, None) == -1  # not 16-byte aligned
+    assert lib.moe_mxfp8_round(P, 4, 64, P + 64, None) == -3  # partial overlap
+    assert lib.moe_mxfp8_round(None, 0, 64, None, None) == 0  # nothing to do, nothing enqueued
+
+
+def test_forward_rejects_unknown_act_format(lib):
+    assert _forward(lib, _dims(act_format=7)) == -1

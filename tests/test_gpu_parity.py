@@ -236,22 +236,10 @@ def test_tiny_named_config_full_width():
 
 # ------------------------------------------------------------------ full K3 layer sizes
 
-_K3 = {}
-
-
-def _k3_layer():
-    """Layer 0 of the K3 workloads (shared by the decode and prefill configs): 896 experts
-    on the GPU (15.7 GB), uploaded once per test session."""
-    H = _harness()
-    if "layer" not in _K3:
-        _K3["layer"] = H.DeviceLayer(gen.named_config("decode16"))
-    return _K3["layer"]
-
-
 def _full_case(name, sample):
     H = _harness()
     c = gen.named_config(name)
-    dl = _k3_layer()
+    dl = H.k3_layer()
     dense = dl.host_dense
     if c.router_dist != "normal":   # decode256: uniform router, same experts
         dense = {**dense, "router": gen.make_dense(c)["router"]}
@@ -293,7 +281,7 @@ def test_full_stack_layer_zipf_hot_experts():
     several MFMA jobs. Same weights as the decode workloads (layer 0), plus the bias."""
     H = _harness()
     c = gen.named_config("stack8x4096")
-    dl = _k3_layer()
+    dl = H.k3_layer()
     dense = {**dl.host_dense, "select_bias": gen.make_dense(c)["select_bias"]}
     x = gen.make_x(c)
     saved = dl.bias
