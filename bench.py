@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the secondary 8192-token prefill measurement of the default run")
+    ap.add_argument("--no-mxfp8", action="store_true",
+                    help="skip the secondary measurements with MXFP8 routed-expert activations")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the steps, run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -129,7 +131,7 @@ def main():
     log(f"inputs resident in HBM in {time.time() - t0:.1f} s")
 
     record = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L)
-    if c.name == "decode16":
+    if c.name == "decode16" and not args.no_mxfp8:
         # the same decode with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
         record["decode_mxfp8"] = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L, summary=True,
                                          act_format=1)
@@ -140,8 +142,9 @@ def main():
         xp = [to_dev_bf16(xp_bits[i * cp.T:(i + 1) * cp.T]) for i in range(2)]
         record["prefill"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2, summary=True)
         # the same prefill with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
-        record["prefill_mxfp8"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2,
-                                          summary=True, act_format=1)
+        if not args.no_mxfp8:
+            record["prefill_mxfp8"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2,
+                                              summary=True, act_format=1)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
     print(json.dumps(record), flush=True)
