@@ -299,7 +299,8 @@ def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False, act_fo
         exp_bytes = D_mean * (gu_per_expert + dn_per_expert) + sh_bytes
         roofline = {"bound": "hbm", "kernel": "mx_small_kernel<GLU> (routed + shared MXFP4 gate/up + GLU)",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None if act_format else measured_traffic(c.name),
                     "bytes_per_launch": int(gu_bytes), "avg_launch_ms": round(gu_ms, 5)}
         extra = {"expert_kernels_hbm_frac": round(exp_bytes / ((gu_ms + dn_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if summary:

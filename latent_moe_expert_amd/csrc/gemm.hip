@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kGM = 8;  // M tiles per group of the grid order
+constexpr int kLargeM = 2048;  // from this many rows on, the 256 x 256 tile
 constexpr int kTile = kBM * kBK * 2;           // bytes of one operand tile in a stage
 constexpr int kGemmDma = 2 * kTile / 16 / 256;  // 16-byte LDS-DMA chunks per thread per k-step (A and W)
 static_assert(kGemmDma == 8, "");
@@ -47,6 +48,14 @@ __device__ __forceinline__ void gemm_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Keeps the loads issued before it ahead of the LDS reads and MFMAs that follow: left to
+// itself the scheduler sinks the next stage's LDS-DMA loads below the current stage's
+// compute, and the wait at the end of the k-step then finds them all still in flight.
+__device__ __forceinline__ void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void dma16g(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff, uint32_t soff) {
@@ -162,6 +171,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
       constexpr int S = decltype(S_)::value;
       const int ks = k4 + S;
       dma(stage(icg<S + 3>{}), ks + 3, ks + 3 < nks);
+      issue_fence();
       compute(stage(S_));
       MOE_GEMM_WAIT_VM_LGKM0(2 * kGemmDma);
       gemm_barrier();
@@ -231,6 +241,175 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   }
 }
 
+// ---- Large batches: 256 x 256 outputs per block, 8 waves (2 per SIMD) in 2 x 4, each
+// 128 x 64 (8 x 4 MFMA tiles). Per 64 K the block moves 64 KB for 8.4 MFLOP, half the
+// bytes per flop of the 128 x 128 tile, whose four waves (one per SIMD) need more load
+// bandwidth per compute unit than the memory path gives. K goes in steps of 32 (64 bytes
+// of every row) through a ring of four 32 KB stages, three k-steps ahead, so 96 KB stay in
+// flight per compute unit. Tiles are dealt to the XCDs round-robin (tile = grid position),
+// the segment with the longer K first, and inside a segment in groups of 8 M tiles with M
+// fastest, so one XCD holds the tiles of one M residue class and reuses their A rows
+// across N from its L2.
+constexpr int kBM2 = 256, kBN2 = 256, kBK2 = 32;
+constexpr int kTile2 = kBM2 * kBK2 * 2;            // 16 KB: one operand tile of a stage
+constexpr int kDma2 = 2 * kTile2 / 16 / 512;       // 16-byte LDS-DMA chunks per thread per k-step
+static_assert(kDma2 == 4, "");
+
+// LDS position of 16-byte chunk c (0..3) of a 64-byte tile row r: rows 4 apart share a bank
+// cycle, so the chunk is XOR-rotated by (r / 4) % 4
+__host__ __device__ constexpr int g_pos2(int c, int r) { return c ^ ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[2 * kTile2];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[2 * kTile2];
+  __shared__ __attribute__((aligned(16))) uint8_t sa2[2 * kTile2];
+  __shared__ __attribute__((aligned(16))) uint8_t sa3[2 * kTile2];
+  auto stage = [&](auto I_) -> uint8_t* {
+    constexpr int I = decltype(I_)::value % 4;
+    if constexpr (I == 0) return sa0;
+    else if constexpr (I == 1) return sa1;
+    else if constexpr (I == 2) return sa2;
+    else return sa3;
+  };
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nl = lane & 15, q = lane >> 4;
+  const int wm = wave >> 2, wn = wave & 3;
+
+  // ---- block -> (segment, M tile, N tile)
+  const int tm = (args.M + kBM2 - 1) / kBM2;
+  const int f = (args.nseg > 1 && args.seg[1].K > args.seg[0].K) ? 1 : 0;  // longer K first
+  const int tnf = (args.seg[f].N + kBN2 - 1) / kBN2;
+  const int tno = args.nseg > 1 ? (args.seg[1 - f].N + kBN2 - 1) / kBN2 : 0;
+  int L = (int)blockIdx.x;
+  if (L >= tm * (tnf + tno)) return;
+  const bool first = L < tm * tnf;
+  if (!first) L -= tm * tnf;
+  const int tn = first ? tnf : tno;
+  const int grp = L / (kGM * tn), rem = L % (kGM * tn);
+  const int gm = min(kGM, tm - grp * kGM);
+  const int mt = grp * kGM + rem % gm, nt = rem / gm;
+  const GemmSeg& sg = args.seg[first ? f : 1 - f];
+  const int m0 = mt * kBM2, n0 = nt * kBN2;
+  const int K = sg.K, kwrap = sg.kwrap;
+
+  // ---- LDS-DMA of one k-step: load i < 2 carries A chunk t = tid + 512 i, else W chunk
+  // t = tid + 512 (i - 2); chunk t is row t / 4 of its tile at LDS position t % 4
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, (uint32_t)args.M * (uint32_t)args.lda * 2u);
+  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(sg.W, 0u);
+  uint32_t goff[kDma2];
+#pragma unroll
+  for (int i = 0; i < kDma2; ++i) {
+    const int t = tid + 512 * (i & 1), r = t >> 2, pos = t & 3;
+    const int c = g_pos2(pos, r);  // the XOR is its own inverse
+    if (i < 2) {
+      const int row = m0 + r;
+      goff[i] = row < args.M ? ((uint32_t)row * (uint32_t)args.lda + 8u * c) * 2u : kOob;
+    } else {
+      const int row = n0 + r;
+      goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
+    }
+  }
+  auto dma = [&](uint8_t* st, int ks, bool on) {  // kDma2 loads
+    const uint32_t ka = (uint32_t)((ks * kBK2) % kwrap) * 2u, kw = (uint32_t)(ks * kBK2) * 2u;
+#pragma unroll
+    for (int i = 0; i < kDma2; ++i)
+      dma16g(on ? (i < 2 ? a_rs : w_rs) : none, st + (i < 2 ? 0 : kTile2) + (i & 1) * 8192 + wave * 1024, goff[i],
+             i < 2 ? ka : kw);
+  };
+
+  // fragment reads: lane (nl, q) of A tile mi reads row 128 wm + 16 mi + nl, chunk q
+  const uint32_t ard = (uint32_t)((wm * 128 + nl) * 64 + g_pos2(q, nl) * 16);
+  const uint32_t brd = (uint32_t)(kTile2 + (wn * 64 + nl) * 64 + g_pos2(q, nl) * 16);
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[i][j]));
+    }
+
+  auto compute = [&](const uint8_t* st) {
+    u32x4_t bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = *(const u32x4_t*)(st + brd + j * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t av = *(const u32x4_t*)(st + ard + i * 16 * 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ring: k-step ks reads stage ks % 4; it issues the loads of ks + 3 into the stage read
+  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x kDma2 loads follow it)
+  const int nks = K / kBK2;  // a multiple of 8
+  dma(stage(icg<0>{}), 0, true);
+  dma(stage(icg<1>{}), 1, true);
+  dma(stage(icg<2>{}), 2, true);
+  MOE_GEMM_WAIT_VM_LGKM0(2 * kDma2);
+  gemm_barrier();
+  for (int k4 = 0; k4 < nks; k4 += 4) {
+    auto step = [&](auto S_) {
+      constexpr int S = decltype(S_)::value;
+      const int ks = k4 + S;
+      dma(stage(icg<S + 3>{}), ks + 3, ks + 3 < nks);
+      issue_fence();
+      compute(stage(S_));
+      MOE_GEMM_WAIT_VM_LGKM0(2 * kDma2);
+      gemm_barrier();
+    };
+    step(icg<0>{});
+    step(icg<1>{});
+    step(icg<2>{});
+    step(icg<3>{});
+  }
+  // the last k-steps issued zero-filling loads into the ring: they must land before the
+  // block ends and its LDS goes to another block
+  MOE_GEMM_WAIT_VM_LGKM0(0);
+
+  // epilogue: lane holds D[m = 4q + r][n = nl] of each 16 x 16 tile; rows past M and
+  // columns past N are skipped
+  bool colok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) colok[j] = n0 + wn * 64 + 16 * j + nl < sg.N;
+  const int colb = n0 + wn * 64 + nl;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float add[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * 128 + 16 * i + 4 * q + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        add[r][j] = (sg.mode == kAddStoreBf16 && sg.addend && row < args.M && colok[j])
+                        ? sg.addend[(size_t)row * sg.ld_add + colb + 16 * j]
+                        : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + wm * 128 + 16 * i + 4 * q + r;
+      if (row >= args.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!colok[j]) continue;
+        const float v = acc[i][j][r];
+        const size_t o = (size_t)row * sg.ldo + colb + 16 * j;
+        if (sg.mode == kAddStoreBf16) {
+          ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(v + add[r][j]);
+          if (sg.tap) sg.tap[(size_t)row * sg.ld_tap + colb + 16 * j] = v;
+        } else if (sg.mode == kStoreF32) {
+          ((float*)sg.out)[o] = v;
+        } else {
+          ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
 // fp32 [N, K] -> bf16 [N, 3K]: row n = hi(k) | mid(k) | lo(k), w = hi + mid + lo exactly
 __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ W, int N, int K,
                                                      uint16_t* __restrict__ out) {
@@ -262,6 +441,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   }
   if ((long long)a.M * a.lda * 2 >= (1ll << 31)) return hipErrorInvalidValue;
   if (tiles == 0) return hipSuccess;
+  if (a.M >= kLargeM) {  // enough 256 x 256 tiles to fill the chip
+    long long tiles2 = 0;
+    for (int i = 0; i < a.nseg; ++i) tiles2 += (long long)((a.M + kBM2 - 1) / kBM2) * ((a.seg[i].N + kBN2 - 1) / kBN2);
+    hipLaunchKernelGGL(gemm256_kernel, dim3((unsigned)tiles2), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   const long long grid = (tiles + 7) / 8 * 8;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -120,6 +120,16 @@ def test_align_block_multiple_of_16(B):
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
 
 
+def test_dense_projections_256_tiles_all_rows():
+    """T = 2100 tokens take the 256 x 256 dense-projection tiles (M >= 2048): a ragged last
+    M tile (52 rows), a partial router N tile (40 of 256 rows, K = 3 x hidden), the
+    up-projection with the shared addend; every token compared."""
+    H = _harness()
+    c = li.small_config(T=2100, hidden=1024, latent=768, n_experts=40, topk=3, inter=256, shared_inter=256)
+    out, ref, _ = _run_small(c)
+    H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
+
+
 def test_k_equals_E_dense_equivalence():
     H = _harness()
     c = li.small_config(T=9, n_experts=6, topk=6, hidden=256, latent=256, inter=256, shared_inter=0, norm=False)
