@@ -89,7 +89,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode16",
                     help="named workload (decode16, decode256, prefill8192, stack8x4096)")
     ap.add_argument("--cpu-tokens", type=int, default=2)

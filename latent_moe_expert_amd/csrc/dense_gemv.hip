@@ -29,22 +29,18 @@ __device__ __forceinline__ void split3x2(float f0, float f1, uint32_t& hi, uint3
   lo = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xffff0000u);
 }
 
-template <int MT>
-__global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int blocks0, int bands0, int bands1) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][64 * 128];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nl = lane & 15, q = lane >> 4;
-  const bool second = (int)blockIdx.x >= blocks0;
-  const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
-  const GemvSeg& sg = args.seg[second ? 1 : 0];
-  const int bands = second ? bands1 : bands0;
-  const int band = local % bands, slice = local / bands;
-  const int row0 = (band * 4 + wave) * 64;
-  if (row0 >= sg.N) return;  // wave-uniform; no block barrier in this kernel
-  uint8_t* lds = lds_all[wave];
+// Steps of a slice run in blocks of kRun straight-line steps through a ring of three register
+// stages. Every step issues its loads (a step past the slice reads zeros from a zero-size
+// resource), so no load sits under a branch and the compiler's waits count exactly the loads
+// in flight; a branch or a loop back edge between a load and its use makes it wait for all.
+constexpr int kRun = 8;
 
-  const bool F32 = sg.w_f32 != 0;                     // block-uniform weight format
-  const int kEs = F32 ? 4 : 2;                        // bytes per weight
+template <int MT, bool F32>
+__device__ __forceinline__ void gemv_body(const GemvArgs& args, const GemvSeg& sg, int slice, int row0, int wave,
+                                          uint8_t* lds) {
+  const int lane = threadIdx.x & 63;
+  const int nl = lane & 15, q = lane >> 4;
+  constexpr int kEs = F32 ? 4 : 2;                    // bytes per weight
   const int K = args.K;
   const uint32_t rowb = (uint32_t)K * kEs;            // bytes per weight row
   const int nsteps = (int)(rowb / 128);               // 128 bytes of every row per step
@@ -52,6 +48,7 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int bloc
   const int s0 = slice * per, s1 = min(nsteps, s0 + per);
   const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * rowb);
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, 0x7fffffffu);
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(sg.W, 0u);
 
   uint32_t goff[8], wlds[8];
 #pragma unroll
@@ -83,17 +80,19 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int bloc
     u32x4_t w[8];
     u32x4_t x[MT][2];
   };
-  auto issue = [&](Stage& st, int s) {
+  auto issue = [&](Stage& st, int s) {  // step s, or zeros past the slice
+    const bool on = s < s1;
     const uint32_t kb = (uint32_t)s * 128;
 #pragma unroll
-    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16(w_rs, goff[l] + kb);
+    for (int l = 0; l < 8; ++l) st.w[l] = buf_load16(on ? w_rs : none, goff[l] + kb);
     const uint32_t kelem = kb / kEs;  // first K index of the step
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         if (h == 0 || !F32)
-          st.x[mt][h] = buf_load16(a_rs, aoff[mt] == 0x80000000u ? aoff[mt] : aoff[mt] + (kelem + h * 32) * 2);
+          st.x[mt][h] = buf_load16(on ? a_rs : none,
+                                   aoff[mt] == 0x80000000u ? aoff[mt] : aoff[mt] + (kelem + h * 32) * 2);
   };
   auto consume = [&](const Stage& st) {
 #pragma unroll
@@ -129,17 +128,24 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int bloc
     }
   };
 
-  if (s0 < s1) {
-    Stage st0, st1;
-    issue(st0, s0);
-    int s = s0;
-    for (; s + 2 <= s1; s += 2) {
-      issue(st1, s + 1);
-      consume(st0);
-      if (s + 2 < s1) issue(st0, s + 2);
-      consume(st1);
+  // the fences keep each step's loads ahead of the previous step's compute (the scheduler
+  // would otherwise sink them and wait for everything in flight)
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int b = s0; b < s1; b += kRun) {
+    Stage st[3];
+    issue(st[0], b);
+    issue(st[1], b + 1);
+    fence();
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      if (i + 2 < kRun) issue(st[(i + 2) % 3], b + i + 2);
+      fence();
+      consume(st[i % 3]);
+      fence();
     }
-    if (s < s1) consume(st0);
   }
 
   // partial sums of this slice: lane holds D[m = 4q + r][n = nl] of each tile
@@ -155,6 +161,24 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int bloc
         if (m < args.M && n < sg.N) part[(size_t)m * sg.N + n] = acc[mt][t][r];
       }
     }
+}
+
+template <int MT>
+__global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int blocks0, int bands0, int bands1) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][64 * 128];
+  const int wave = threadIdx.x >> 6;
+  const bool second = (int)blockIdx.x >= blocks0;
+  const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
+  const GemvSeg& sg = args.seg[second ? 1 : 0];
+  const int bands = second ? bands1 : bands0;
+  const int band = local % bands, slice = local / bands;
+  const int row0 = (band * 4 + wave) * 64;
+  if (row0 >= sg.N) return;  // wave-uniform; no block barrier in this kernel
+  // block-uniform weight format, taken once outside the step loop
+  if (sg.w_f32)
+    gemv_body<MT, true>(args, sg, slice, row0, wave, lds_all[wave]);
+  else
+    gemv_body<MT, false>(args, sg, slice, row0, wave, lds_all[wave]);
 }
 
 __global__ __launch_bounds__(256) void finish_up_kernel(const float* __restrict__ part, int splits, int M, int N,
