@@ -121,25 +121,30 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     uint2 sc[4];
   };
   u32x4_t anext[2];
-  auto issue = [&](Stage& st, int d, bool with_a) {
-    if (with_a) {  // activations first: they are waited on before this step's weights
+  // A double step past the end loads from a zero-size resource (zeros, no memory traffic), so
+  // every step issues the same loads with no branch: a load under a branch makes the
+  // compiler wait for every load in flight before the next use of any of them.
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(a.W, 0u);
+  auto issue = [&](Stage& st, int d) {
+    const bool on = d < (K >> 8);
+    {  // activations first: they are waited on before this step's weights
       const uint32_t ao = aoff_fill + (uint32_t)d * a_step;
-      anext[0] = buf_load16(a_rs, ao);
-      anext[1] = buf_load16(a_rs, aoff_fill == kOob ? kOob : ao + 256);
+      anext[0] = buf_load16(on ? a_rs : none, ao);
+      anext[1] = buf_load16(on ? a_rs : none, aoff_fill == kOob ? kOob : ao + 256);
     }
     const uint32_t vo = gbase + (uint32_t)d * 128;  // 256 weights of a row per double step
 #pragma unroll
     for (int l = 0; l < 8; ++l) {
       const int t = l >> 1;
       const uint32_t so = (uint32_t)(16 * tt(t) + 8 * (l & 1)) * kb2;
-      st.w[l] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128((GLU && t >= 2) ? w_hi : w_lo,
-                                                                                     vo, so, kNonTemporal));
+      st.w[l] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                on ? ((GLU && t >= 2) ? w_hi : w_lo) : none, vo, so, kNonTemporal));
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t so = (uint32_t)(16 * tt(t)) * ks32 + (uint32_t)d * 8;
-      st.sc[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64((GLU && t >= 2) ? s_hi : s_lo,
-                                                                                  sbase, so, 0));
+      st.sc[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               on ? ((GLU && t >= 2) ? s_hi : s_lo) : none, sbase, so, 0));
     }
   };
   auto fill_a = [&](int buf) {
@@ -174,21 +179,20 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   // Pipeline: step d's weights sit in registers and its activations in lds_a[d & 1] while
   // step d+1's loads are in flight; one barrier per step publishes the next activation tile.
   const int nd = K >> 8;  // double steps (K is a multiple of 256)
+  // Steps past the last one load zeros and fill an activation buffer that is not read again.
   Stage s0, s1;
-  issue(s0, 0, true);
+  issue(s0, 0);
   fill_a(0);
   __syncthreads();
   int d = 0;
   for (; d + 2 <= nd; d += 2) {
-    const bool more1 = d + 1 < nd;  // always true here
-    if (more1) issue(s1, d + 1, true);
+    issue(s1, d + 1);
     consume(s0, d & 1);
-    if (more1) fill_a((d + 1) & 1);
+    fill_a((d + 1) & 1);
     __syncthreads();
-    const bool more2 = d + 2 < nd;
-    if (more2) issue(s0, d + 2, true);
+    issue(s0, d + 2);
     consume(s1, (d + 1) & 1);
-    if (more2) fill_a((d + 2) & 1);
+    fill_a((d + 2) & 1);
     __syncthreads();
   }
   if (d < nd) consume(s0, d & 1);
