@@ -28,6 +28,10 @@ float64 from exactly upcast inputs (bf16 and MXFP4 values are exact in fp64):
                      one E8M0 scale per 32), the deployment numerics of the K3
                      report review (quantization-aware training section);
                      layer.forward(act="mxfp8") uses them
+  qb                 Quantile Balancing: the selection bias that matches every
+                     expert's target load m*k/n, exactly and from 1000-bin
+                     integer histograms (K3 report review, section on Quantile
+                     Balancing; readings Q1-Q6 in its docstring)
   brute              a pure-Python scalar twin of the whole layer for tiny
                      sizes, written independently (bit-field decoding, explicit
                      loops) and used only as a cross-check.
@@ -38,5 +42,5 @@ Readings where the pages are silent are listed in the module docstrings of
 Parity status: every function here is pinned by the CPU tests (pages' facts,
 closed forms, invariants, brute force); none is "parity unpinned".
 """
-from . import numerics, mxfp4, mxfp8, layer  # noqa: F401
+from . import numerics, mxfp4, mxfp8, layer, qb  # noqa: F401
 from .layer import forward, route, align, rmsnorm, silu  # noqa: F401
