@@ -85,6 +85,68 @@ def cpu_baseline(c, dl, x_bits, n_tokens: int):
                       f"{dt:.1f} s wall; expert decode single-threaded, matmuls on {blas_threads} BLAS threads"}
 
 
+def cpu_baseline_qb(s, b, k):
+    """The oracle's Quantile Balancing update, as it stands, on the same scores (host cores)."""
+    from oracle import qb
+    t0 = time.perf_counter()
+    qb.qb_bias(s, b, k)
+    dt = time.perf_counter() - t0
+    return {"value": s.shape[0] / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole {s.shape[0]}x{s.shape[1]} batch, numpy oracle (sort and bincount, one thread), "
+                      f"{dt:.2f} s wall"}
+
+
+def measure_qb(L, m=8192, n=896, k=16, iters=200, with_cpu=True):
+    """Quantile Balancing bias update on the router scores of an m-token batch at the K3
+    router shape, scores and bias resident in HBM. A step is one moe_qb_update (thresholds,
+    histograms and the new bias); moe_qb_histogram and moe_qb_bias, the two halves used
+    when histograms of several batches are summed in between, are timed on their own."""
+    import torch
+    from workload import gen
+    s_host = gen.make_router_scores(m, n, seed=0)
+    b_host = gen.make_selection_bias(n, seed=0)
+    s = torch.from_numpy(s_host).cuda()
+    b = torch.from_numpy(b_host).cuda()
+    alpha = torch.empty(m, dtype=torch.float32, device="cuda")
+    hist = torch.empty((n, 1000), dtype=torch.int32, device="cuda")
+    nb = torch.empty(n, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        L.moe_qb_histogram(s, b, k, alpha, hist, stream=stream)
+        L.moe_qb_bias(hist, m, k, nb, stream=stream)
+    torch.cuda.synchronize()
+    # events on the launch stream around `iters` calls of each entry point
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    for _ in range(iters):
+        L.moe_qb_histogram(s, b, k, alpha, hist, stream=stream)
+    ev[1].record(stream)
+    for _ in range(iters):
+        L.moe_qb_bias(hist, m, k, nb, stream=stream)
+    ev[2].record(stream)
+    for _ in range(iters):
+        L.moe_qb_update(s, b, k, alpha, hist, nb, stream=stream)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    h_ms = ev[0].elapsed_time(ev[1]) / iters
+    b_ms = ev[1].elapsed_time(ev[2]) / iters
+    step_ms = ev[2].elapsed_time(ev[3]) / iters
+    # algorithmic bytes of moe_qb_histogram: the scores once, the bias, alpha and the histograms written once
+    h_bytes = m * n * 4 + n * 4 + m * 4 + n * 1000 * 4
+    achieved = h_bytes / (h_ms * 1e-3) / 1e9
+    rec = {"config": {"workload": f"qb{m}: Quantile Balancing bias update over the router scores of {m} tokens, "
+                                  f"{n} experts, top-{k}, 1000-bin histograms", "global_batch": m},
+           "value": round(m / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 5),
+           "roofline": {"bound": "hbm", "kernel": "moe_qb_histogram (qb_alpha_kernel + qb_hist_kernel)",
+                        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": h_bytes,
+                        "avg_launch_ms": round(h_ms, 5)},
+           "bias_ms": round(b_ms, 5)}
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline_qb(s_host, b_host, k)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +160,9 @@ def main():
                     help="skip the secondary 8192-token prefill measurement of the default run")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the secondary measurements with MXFP8 routed-expert activations")
+    ap.add_argument("--no-qb", action="store_true",
+                    help="skip the secondary Quantile Balancing measurement of the default run")
+    ap.add_argument("--qb-only", action="store_true", help="only the Quantile Balancing measurement")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the steps, run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -120,6 +185,9 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.copy_mb} MiB device copies")
         del src, dst
+    if args.qb_only:
+        print(json.dumps(measure_qb(L, with_cpu=not args.no_cpu_baseline)), flush=True)
+        return
     if c.n_layers > 1:
         record = measure_stack(c, args.steps, args.warmup, L, DeviceLayer, to_dev_bf16)
         print(json.dumps(record), flush=True)
@@ -145,6 +213,8 @@ def main():
         if not args.no_mxfp8:
             record["prefill_mxfp8"] = measure(cp, dl, xp_bits, xp, max(3, args.steps // 4), 2, L, rotate=2,
                                               summary=True, act_format=1)
+    if not args.no_qb and c.name == "decode16":
+        record["qb"] = measure_qb(L, with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         record["cpu_baseline"] = cpu_baseline(c, dl, xs_bits[:c.T], args.cpu_tokens)
     print(json.dumps(record), flush=True)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 3
+#define MOE_LATENT_ABI_VERSION 4
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, negative or inconsistent size */
@@ -213,6 +213,59 @@ int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts
  * x / 2^s, so it matches any exact evaluation bit for bit.
  */
 int moe_mxfp8_round(const void* x, int rows, int K, void* y, void* stream);
+
+/*
+ * Quantile Balancing (K3 report review, section on Quantile Balancing): the
+ * selection-only router bias that gives every expert the target load
+ * q = max(1, floor(m*k/n)) of m tokens, n experts and k experts per token.
+ * Each token's threshold alpha is the (k+1)-th largest of its biased keys
+ * s + b; its margin at expert j is s_j - alpha; expert j's new bias is minus
+ * the margin that q of its margins reach, estimated from a histogram of
+ * MOE_QB_BINS bins of width 0.004 over [-2, 2) (margins outside are counted in
+ * the end bins). Summing the histograms of several batches (integer addition,
+ * the page's all-reduce) before moe_qb_bias gives the update of their union.
+ * The new bias takes effect as moe_router.select_bias of later forwards.
+ * Exact fp32 operations, in this order, with no contraction:
+ *   key = s + b;  mu = s - alpha;  bin = min(999, max(0, floor((mu + 2) * 250)));
+ *   new_bias = -(-2 + t * 0.004), t = the largest bin whose count from t up
+ *   to the last bin reaches q (the lower edge of the bin that holds the q-th
+ *   largest margin, so within one bin width of the exact quantile).
+ */
+#define MOE_QB_BINS 1000
+
+/*
+ * Thresholds and margin histograms of one batch.
+ *   scores  fp32 [m, n] router scores (sigmoid of the logits), finite, 16-byte aligned
+ *   bias    fp32 [n] current selection bias, or NULL (zero)
+ *   m >= 0 tokens, 2 <= n <= 4096 experts, 1 <= topk < n
+ *   alpha   fp32 [m] out: each token's threshold
+ *   hist    int32 [n, MOE_QB_BINS] out, fully overwritten (zeros when m = 0)
+ * Outputs must not overlap the inputs or each other (MOE_EALIAS). Integer
+ * results: bit-exact against any exact fp32 evaluation of the rules above.
+ */
+int moe_qb_histogram(const float* scores, const float* bias, int m, int n, int topk, float* alpha, int32_t* hist,
+                     void* stream);
+
+/*
+ * One batch's update in one call: moe_qb_histogram followed by moe_qb_bias with
+ * m_total = m (m >= 1), the bias taken from the histograms in the same launch.
+ * For several batches (ranks) sum their histograms and call moe_qb_bias instead.
+ *   new_bias  fp32 [n] out, overlapping no other argument
+ */
+int moe_qb_update(const float* scores, const float* bias, int m, int n, int topk, float* alpha, int32_t* hist,
+                  float* new_bias, void* stream);
+
+/* Host-only. The integer target q = max(1, floor(m_total*topk/n)) into *q. */
+int moe_qb_target(long long m_total, int n, int topk, long long* q);
+
+/*
+ * New selection bias from (summed) histograms.
+ *   hist      int32 [n, MOE_QB_BINS], counts of m_total margins per expert
+ *   m_total   tokens the histograms cover (over every batch summed into them)
+ *   new_bias  fp32 [n] out; NaN for an expert whose histogram holds fewer than
+ *             q margins (inconsistent m_total); must not overlap hist
+ */
+int moe_qb_bias(const int32_t* hist, int n, long long m_total, int topk, float* new_bias, void* stream);
 
 /*
  * Stage timing for measurement. While enabled, moe_latent_forward records HIP

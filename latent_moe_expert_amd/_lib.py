@@ -8,6 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_latent.so")
 
 MOE_OK = 0
+QB_BINS = 1000
 PATH_AUTO, PATH_STREAM, PATH_MFMA = 0, 1, 2
 ACT_BF16, ACT_MXFP8 = 0, 1
 ERRORS = {-1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EALIAS", -4: "MOE_EWORKSPACE", -5: "MOE_EHIP",
@@ -41,6 +42,7 @@ class MoeLatentTaps(ctypes.Structure):
 EXPORTS = ["moe_latent_abi_version", "moe_latent_strerror", "moe_latent_last_hip_error",
            "moe_latent_workspace_size", "moe_latent_align_layout", "moe_latent_forward", "moe_latent_forward_ex",
            "moe_route", "moe_align_workspace_size", "moe_align_block_size", "moe_mxfp8_round",
+           "moe_qb_histogram", "moe_qb_update", "moe_qb_target", "moe_qb_bias",
            "moe_latent_timing_enable",
            "moe_latent_stage_count", "moe_latent_stage_name", "moe_latent_timing_read"]
 
@@ -72,6 +74,10 @@ def load() -> ctypes.CDLL:
         "moe_align_workspace_size": ([I, I, I, ctypes.POINTER(SZ)], I),
         "moe_align_block_size": ([P, I, I, I, I, P, P, P, P, P, P, SZ, P], I),
         "moe_mxfp8_round": ([P, I, I, P, P], I),
+        "moe_qb_histogram": ([P, P, I, I, I, P, P, P], I),
+        "moe_qb_update": ([P, P, I, I, I, P, P, P, P], I),
+        "moe_qb_target": ([ctypes.c_longlong, I, I, ctypes.POINTER(ctypes.c_longlong)], I),
+        "moe_qb_bias": ([P, I, ctypes.c_longlong, I, P, P], I),
         "moe_latent_timing_enable": ([I], I),
         "moe_latent_stage_count": ([], I),
         "moe_latent_stage_name": ([I], ctypes.c_char_p),

@@ -24,7 +24,8 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["api.cpp", "dense.hip", "dense_gemv.hip", "gemm.hip", "router.hip", "align.hip", "mxfp4_small.hip", "mxfp4_mfma.hip", "quant.hip", "combine.hip"]
+SOURCES = ["api.cpp", "dense.hip", "dense_gemv.hip", "gemm.hip", "router.hip", "align.hip", "mxfp4_small.hip",
+           "mxfp4_mfma.hip", "quant.hip", "combine.hip", "qb.hip"]
 
 
 def _compile(src: str) -> str:

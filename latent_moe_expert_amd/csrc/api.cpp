@@ -649,6 +649,62 @@ int moe_mxfp8_round(const void* x, int rows, int K, void* y, void* stream) {
   return MOE_OK;
 }
 
+namespace {
+int qb_check(const float* scores, const float* bias, int m, int n, int topk, const float* alpha, const int32_t* hist,
+             const float* new_bias) {
+  if (m < 0 || n < 2 || topk < 1 || topk >= n) return MOE_EINVAL;
+  if (n > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (!hist || (m > 0 && (!scores || !alpha)) || ((uintptr_t)scores & 15)) return MOE_EINVAL;
+  const size_t sb = (size_t)m * n * sizeof(float), hb = (size_t)n * moe::kQbBins * sizeof(int32_t);
+  const size_t ab = (size_t)m * sizeof(float), bb = bias ? (size_t)n * sizeof(float) : 0;
+  const size_t nb = new_bias ? (size_t)n * sizeof(float) : 0;
+  if (overlap(hist, hb, scores, sb) || overlap(hist, hb, bias, bb) || overlap(hist, hb, alpha, ab) ||
+      overlap(alpha, ab, scores, sb) || overlap(alpha, ab, bias, bb) || overlap(new_bias, nb, scores, sb) ||
+      overlap(new_bias, nb, bias, bb) || overlap(new_bias, nb, alpha, ab) || overlap(new_bias, nb, hist, hb))
+    return MOE_EALIAS;
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_qb_histogram(const float* scores, const float* bias, int m, int n, int topk, float* alpha, int32_t* hist,
+                     void* stream) {
+  const int rc = qb_check(scores, bias, m, n, topk, alpha, hist, nullptr);
+  if (rc != MOE_OK) return rc;
+  MOE_HIP(moe::launch_qb_histogram(scores, bias, m, n, topk, alpha, hist, 0, nullptr, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_qb_update(const float* scores, const float* bias, int m, int n, int topk, float* alpha, int32_t* hist,
+                  float* new_bias, void* stream) {
+  if (m < 1 || !new_bias) return MOE_EINVAL;
+  const int rc = qb_check(scores, bias, m, n, topk, alpha, hist, new_bias);
+  if (rc != MOE_OK) return rc;
+  const long long t = (long long)m * topk / n;
+  MOE_HIP(moe::launch_qb_histogram(scores, bias, m, n, topk, alpha, hist, t < 1 ? 1 : t, new_bias,
+                                   (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_qb_target(long long m_total, int n, int topk, long long* q) {
+  if (m_total < 1 || n < 2 || topk < 1 || topk >= n || !q) return MOE_EINVAL;
+  if (m_total > (1ll << 40)) return MOE_EUNSUPPORTED;
+  const long long t = m_total * topk / n;
+  *q = t < 1 ? 1 : t;
+  return MOE_OK;
+}
+
+int moe_qb_bias(const int32_t* hist, int n, long long m_total, int topk, float* new_bias, void* stream) {
+  long long q = 0;
+  const int rc = moe_qb_target(m_total, n, topk, &q);
+  if (rc != MOE_OK) return rc;
+  if (n > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (!hist || !new_bias) return MOE_EINVAL;
+  if (overlap(new_bias, (size_t)n * sizeof(float), hist, (size_t)n * moe::kQbBins * sizeof(int32_t)))
+    return MOE_EALIAS;
+  MOE_HIP(moe::launch_qb_bias(hist, n, q, new_bias, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_latent_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   g_timing.on = on != 0;

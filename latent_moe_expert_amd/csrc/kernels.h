@@ -197,6 +197,16 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
 hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
                                const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
 
+// ---------------------------------------------------------------- Quantile Balancing
+constexpr int kQbBins = 1000;
+// alpha [m] = (k+1)-th largest of scores[t] + bias; hist [n, kQbBins] int32 = margin histograms.
+// scores fp32 [m, n], 16-byte aligned; 2 <= n <= 4096; 1 <= k < n; m >= 0 (m = 0 stores zero histograms).
+// With new_bias non-null, also new_bias [n] for the target q (the histograms' own batch).
+hipError_t launch_qb_histogram(const float* scores, const float* bias, int m, int n, int k, float* alpha,
+                               int32_t* hist, long long q, float* new_bias, hipStream_t s);
+// new_bias [n] from hist [n, kQbBins] and the integer target q >= 1 (NaN where fewer than q margins)
+hipError_t launch_qb_bias(const int32_t* hist, int n, long long q, float* new_bias, hipStream_t s);
+
 // fill with a constant (a kernel, so that captured graphs hold no memset node)
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
 

@@ -147,6 +147,52 @@ def moe_mxfp8_round(x, y, stream=None) -> None:
     _check("moe_mxfp8_round", rc)
 
 
+def moe_qb_histogram(scores, bias, topk: int, alpha, hist, stream=None) -> None:
+    """alpha [m] and hist [n, 1000] int32 from scores fp32 [m, n] and bias fp32 [n] (or None)."""
+    if scores.dim() != 2:
+        raise ValueError("scores: [m, n]")
+    m, n = scores.shape
+    if alpha.numel() != m or tuple(hist.shape) != (n, _lib.QB_BINS):
+        raise ValueError("alpha: [m], hist: [n, 1000]")
+    if bias is not None and bias.numel() != n:
+        raise ValueError("bias: [n]")
+    rc = _lib.load().moe_qb_histogram(_ptr(scores, torch.float32, "scores"), _ptr(bias, torch.float32, "bias"), m, n,
+                                      topk, _ptr(alpha, torch.float32, "alpha"), _ptr(hist, torch.int32, "hist"),
+                                      _stream(stream))
+    _check("moe_qb_histogram", rc)
+
+
+def moe_qb_update(scores, bias, topk: int, alpha, hist, new_bias, stream=None) -> None:
+    """moe_qb_histogram and moe_qb_bias of one batch (m_total = m) in one call."""
+    if scores.dim() != 2:
+        raise ValueError("scores: [m, n]")
+    m, n = scores.shape
+    if alpha.numel() != m or tuple(hist.shape) != (n, _lib.QB_BINS) or new_bias.numel() != n:
+        raise ValueError("alpha: [m], hist: [n, 1000], new_bias: [n]")
+    if bias is not None and bias.numel() != n:
+        raise ValueError("bias: [n]")
+    rc = _lib.load().moe_qb_update(_ptr(scores, torch.float32, "scores"), _ptr(bias, torch.float32, "bias"), m, n,
+                                   topk, _ptr(alpha, torch.float32, "alpha"), _ptr(hist, torch.int32, "hist"),
+                                   _ptr(new_bias, torch.float32, "new_bias"), _stream(stream))
+    _check("moe_qb_update", rc)
+
+
+def moe_qb_target(m_total: int, n: int, topk: int) -> int:
+    q = ctypes.c_longlong(0)
+    _check("moe_qb_target", _lib.load().moe_qb_target(m_total, n, topk, ctypes.byref(q)))
+    return q.value
+
+
+def moe_qb_bias(hist, m_total: int, topk: int, new_bias, stream=None) -> None:
+    """new_bias [n] from hist [n, 1000] int32 covering m_total tokens."""
+    n = hist.shape[0]
+    if tuple(hist.shape) != (n, _lib.QB_BINS) or new_bias.numel() != n:
+        raise ValueError("hist: [n, 1000], new_bias: [n]")
+    rc = _lib.load().moe_qb_bias(_ptr(hist, torch.int32, "hist"), n, m_total, topk,
+                                 _ptr(new_bias, torch.float32, "new_bias"), _stream(stream))
+    _check("moe_qb_bias", rc)
+
+
 def moe_latent_timing_enable(on: bool) -> None:
     _check("moe_latent_timing_enable", _lib.load().moe_latent_timing_enable(1 if on else 0))
 

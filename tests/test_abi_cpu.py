@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.moe_latent_abi_version() == 3
+    assert lib.moe_latent_abi_version() == 4
     for code in range(0, -7, -1):
         assert lib.moe_latent_strerror(code)
     assert lib.moe_latent_stage_count() == 8
@@ -136,3 +136,35 @@ def test_mxfp8_round_argument_errors(lib):
 
 def test_forward_rejects_unknown_act_format(lib):
     assert _forward(lib, _dims(act_format=7)) == -1
+
+
+def test_qb_argument_errors(lib):
+    P, Q, R = 0x100000, 0x900000, 0x2000000
+    # m, n, topk: topk must be below n, n at least 2 and at most 4096
+    assert lib.moe_qb_histogram(P, None, 16, 896, 896, Q, R, None) == -1
+    assert lib.moe_qb_histogram(P, None, 16, 1, 1, Q, R, None) == -1
+    assert lib.moe_qb_histogram(P, None, -1, 896, 16, Q, R, None) == -1
+    assert lib.moe_qb_histogram(P, None, 16, 5000, 16, Q, R, None) == -2
+    assert lib.moe_qb_histogram(None, None, 16, 896, 16, Q, R, None) == -1
+    assert lib.moe_qb_histogram(P + 4, None, 16, 896, 16, Q, R, None) == -1   # scores not 16-byte aligned
+    assert lib.moe_qb_histogram(P, None, 16, 896, 16, Q, None, None) == -1
+    assert lib.moe_qb_histogram(P, None, 16, 896, 16, P + 64, R, None) == -3  # alpha inside the scores
+    assert lib.moe_qb_histogram(P, None, 16, 896, 16, Q, P + 4096, None) == -3  # hist inside the scores
+    assert lib.moe_qb_histogram(P, R + 8, 16, 896, 16, Q, R, None) == -3      # bias inside hist
+    S = 0x3000000
+    assert lib.moe_qb_update(P, None, 0, 896, 16, Q, R, S, None) == -1         # needs at least one token
+    assert lib.moe_qb_update(P, None, 16, 896, 16, Q, R, None, None) == -1
+    assert lib.moe_qb_update(P, None, 16, 896, 16, Q, R, R + 64, None) == -3   # new_bias inside hist
+    assert lib.moe_qb_update(P, None, 16, 896, 16, Q, R, Q, None) == -3        # new_bias on alpha
+    assert lib.moe_qb_bias(R, 896, 0, 16, Q, None) == -1
+    assert lib.moe_qb_bias(R, 896, 8192, 896, Q, None) == -1
+    assert lib.moe_qb_bias(None, 896, 8192, 16, Q, None) == -1
+    assert lib.moe_qb_bias(R, 896, 8192, 16, R + 400, None) == -3
+
+
+@pytest.mark.parametrize("m,n,k,q", [(8192, 896, 16, 146), (3, 896, 16, 1), (4, 2, 1, 2), (1 << 36, 896, 16,
+                                                                                          (1 << 40) // 896)])
+def test_qb_target(lib, m, n, k, q):
+    out = ctypes.c_longlong(0)
+    assert lib.moe_qb_target(m, n, k, ctypes.byref(out)) == 0
+    assert out.value == q

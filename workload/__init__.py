@@ -17,4 +17,6 @@ from .gen import (  # noqa: F401
     expert_scale_bytes,
     shared_record_bytes,
     shared_scale_bytes,
+    make_router_scores,
+    make_selection_bias,
 )

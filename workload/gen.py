@@ -203,3 +203,21 @@ def fill_experts(c: LayerConfig, layer: int, packed_out: np.ndarray, scales_out:
 
     with ThreadPoolExecutor(threads or _workers()) as ex:
         list(ex.map(one, range(len(experts))))
+
+
+def make_router_scores(m: int, n: int, seed: int = 0, dyadic: bool = False, logit_std: float = 1.0) -> np.ndarray:
+    """Router scores fp32 [m, n] in (0, 1), as a sigmoid router emits them: logits drawn
+    N(0, logit_std) -- the configs' router gives logits of standard deviation about 1 --
+    then sigmoid, rounded once to fp32. dyadic=True instead draws multiples of 2^-12 in
+    (0, 1), so that many keys tie exactly. Own stream: SeedSequence(seed, (99, m, n))."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(99, m, n))))
+    if dyadic:
+        return (g.integers(1, 4096, size=(m, n)) / 4096.0).astype(np.float32)
+    z = g.standard_normal((m, n)) * logit_std
+    return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+
+
+def make_selection_bias(n: int, seed: int = 0, std: float = 0.05) -> np.ndarray:
+    """A selection bias fp32 [n] ~ N(0, std). Own stream: SeedSequence(seed, (98, n))."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(98, n))))
+    return (g.standard_normal(n) * std).astype(np.float32)
