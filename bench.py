@@ -147,6 +147,28 @@ def measure_qb(L, m=8192, n=896, k=16, iters=200, with_cpu=True):
     return rec
 
 
+def measure_hbm_read(L, gib=2, iters=10):
+    """HBM read bandwidth of the library's streaming-read kernel (moe_hbm_read) over a
+    buffer of `gib` GiB (far past the 256 MB last-level cache), non-temporal 16-byte loads."""
+    import torch
+    n = gib << 30
+    buf = torch.empty(n // 4, dtype=torch.int32, device="cuda").fill_(0x5a5a5a5a)
+    out = torch.empty(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        L.moe_hbm_read(buf, out, stream=stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(iters):
+        L.moe_hbm_read(buf, out, stream=stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / iters
+    del buf
+    return {"gbs": round(n / (ms * 1e-3) / 1e9, 1), "bytes": n, "ms": round(ms, 4),
+            "kernel": "hbm_read_kernel (moe_hbm_read)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +221,11 @@ def main():
     log(f"inputs resident in HBM in {time.time() - t0:.1f} s")
 
     record = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L)
+    if c.name == "decode16":
+        # the measured HBM read ceiling beside the vendor peak
+        hb = measure_hbm_read(L)
+        record["hbm_read_measured"] = hb
+        record["roofline"]["frac_of_measured_read"] = round(record["roofline"]["achieved"] / hb["gbs"], 4)
     if c.name == "decode16" and not args.no_mxfp8:
         # the same decode with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
         record["decode_mxfp8"] = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L, summary=True,

@@ -268,6 +268,17 @@ int moe_qb_target(long long m_total, int n, int topk, long long* q);
 int moe_qb_bias(const int32_t* hist, int n, long long m_total, int topk, float* new_bias, void* stream);
 
 /*
+ * Measurement, not a step of the layer: the HBM read bandwidth that the
+ * weight-streaming expert kernels are compared against. Reads every 16-byte
+ * chunk of `buf` once with non-temporal loads (as those kernels read their
+ * weights) and writes the XOR of all its dwords to *checksum, a value that does
+ * not depend on the order of the reads (so it can be checked against the host).
+ *   buf       device, 16-byte aligned, `bytes` a multiple of 16 (0 gives 0)
+ *   checksum  device uint32, must not overlap buf
+ */
+int moe_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, void* stream);
+
+/*
  * Stage timing for measurement. While enabled, moe_latent_forward records HIP
  * events around each stage on its stream (at most 256 forwards are kept).
  * moe_latent_timing_read synchronises on the recorded events and returns, per

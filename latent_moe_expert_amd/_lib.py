@@ -42,7 +42,7 @@ class MoeLatentTaps(ctypes.Structure):
 EXPORTS = ["moe_latent_abi_version", "moe_latent_strerror", "moe_latent_last_hip_error",
            "moe_latent_workspace_size", "moe_latent_align_layout", "moe_latent_forward", "moe_latent_forward_ex",
            "moe_route", "moe_align_workspace_size", "moe_align_block_size", "moe_mxfp8_round",
-           "moe_qb_histogram", "moe_qb_update", "moe_qb_target", "moe_qb_bias",
+           "moe_qb_histogram", "moe_qb_update", "moe_qb_target", "moe_qb_bias", "moe_hbm_read",
            "moe_latent_timing_enable",
            "moe_latent_stage_count", "moe_latent_stage_name", "moe_latent_timing_read"]
 
@@ -78,6 +78,7 @@ def load() -> ctypes.CDLL:
         "moe_qb_update": ([P, P, I, I, I, P, P, P, P], I),
         "moe_qb_target": ([ctypes.c_longlong, I, I, ctypes.POINTER(ctypes.c_longlong)], I),
         "moe_qb_bias": ([P, I, ctypes.c_longlong, I, P, P], I),
+        "moe_hbm_read": ([P, SZ, P, P], I),
         "moe_latent_timing_enable": ([I], I),
         "moe_latent_stage_count": ([], I),
         "moe_latent_stage_name": ([I], ctypes.c_char_p),

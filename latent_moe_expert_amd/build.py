@@ -25,7 +25,7 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["api.cpp", "dense.hip", "dense_gemv.hip", "gemm.hip", "router.hip", "align.hip", "mxfp4_small.hip",
-           "mxfp4_mfma.hip", "quant.hip", "combine.hip", "qb.hip"]
+           "mxfp4_mfma.hip", "quant.hip", "combine.hip", "qb.hip", "stream.hip"]
 
 
 def _compile(src: str) -> str:

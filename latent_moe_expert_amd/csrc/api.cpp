@@ -705,6 +705,14 @@ int moe_qb_bias(const int32_t* hist, int n, long long m_total, int topk, float* 
   return MOE_OK;
 }
 
+int moe_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, void* stream) {
+  if (!checksum || ((uintptr_t)checksum & 3) || bytes % 16 || (bytes && (!buf || ((uintptr_t)buf & 15))))
+    return MOE_EINVAL;
+  if (overlap(checksum, sizeof(uint32_t), buf, bytes)) return MOE_EALIAS;
+  MOE_HIP(moe::launch_hbm_read(buf, bytes, checksum, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_latent_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   g_timing.on = on != 0;

@@ -207,6 +207,10 @@ hipError_t launch_qb_histogram(const float* scores, const float* bias, int m, in
 // new_bias [n] from hist [n, kQbBins] and the integer target q >= 1 (NaN where fewer than q margins)
 hipError_t launch_qb_bias(const int32_t* hist, int n, long long q, float* new_bias, hipStream_t s);
 
+// ---------------------------------------------------------------- streaming read (measurement)
+// *checksum = XOR of all dwords of buf (bytes % 16 == 0, buf 16-byte aligned), every chunk read once.
+hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, hipStream_t s);
+
 // fill with a constant (a kernel, so that captured graphs hold no memset node)
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
 

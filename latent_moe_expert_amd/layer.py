@@ -193,6 +193,13 @@ def moe_qb_bias(hist, m_total: int, topk: int, new_bias, stream=None) -> None:
     _check("moe_qb_bias", rc)
 
 
+def moe_hbm_read(buf, checksum, stream=None) -> None:
+    """checksum (int32 [1], GPU) = XOR of all dwords of buf (any contiguous GPU tensor, size % 16 == 0)."""
+    rc = _lib.load().moe_hbm_read(_ptr(buf, None, "buf"), buf.numel() * buf.element_size(),
+                                  _ptr(checksum, torch.int32, "checksum"), _stream(stream))
+    _check("moe_hbm_read", rc)
+
+
 def moe_latent_timing_enable(on: bool) -> None:
     _check("moe_latent_timing_enable", _lib.load().moe_latent_timing_enable(1 if on else 0))
 

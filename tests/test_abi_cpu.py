@@ -168,3 +168,13 @@ def test_qb_target(lib, m, n, k, q):
     out = ctypes.c_longlong(0)
     assert lib.moe_qb_target(m, n, k, ctypes.byref(out)) == 0
     assert out.value == q
+
+
+def test_hbm_read_argument_errors(lib):
+    P, Q = 0x100000, 0x900000
+    assert lib.moe_hbm_read(P, 64, None, None) == -1
+    assert lib.moe_hbm_read(P, 60, Q, None) == -1          # not a multiple of 16
+    assert lib.moe_hbm_read(P + 8, 64, Q, None) == -1      # not 16-byte aligned
+    assert lib.moe_hbm_read(None, 64, Q, None) == -1
+    assert lib.moe_hbm_read(P, 64, Q + 2, None) == -1      # checksum not 4-byte aligned
+    assert lib.moe_hbm_read(P, 64, P + 32, None) == -3     # checksum inside the buffer
