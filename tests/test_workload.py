@@ -46,3 +46,19 @@ def test_dense_recipe_shapes_and_scales():
     assert np.abs(u).max() <= np.sqrt(3 / 512) and abs(u.std() * np.sqrt(512) - 1) < 0.05
     z = gen.make_dense(c.with_(zipf_s=1.1, zipf_c=0.5))["select_bias"]
     assert np.isclose(z.max(), 0.5) and np.isclose(np.sort(z)[-2], 0.5 * 2 ** -1.1, rtol=1e-6)
+
+
+def test_router_scores_and_bias_streams():
+    """Seeded, reproducible, of the stated ranges, and independent of other streams."""
+    from workload import gen
+    a = gen.make_router_scores(64, 96, seed=3)
+    b = gen.make_router_scores(64, 96, seed=3)
+    assert a.dtype == np.float32 and a.shape == (64, 96) and np.array_equal(a, b)
+    assert np.all((a > 0) & (a < 1))
+    assert not np.array_equal(a, gen.make_router_scores(64, 96, seed=4))
+    d = gen.make_router_scores(32, 40, seed=1, dyadic=True)
+    assert np.all(d * 4096 == np.round(d * 4096)) and np.all((d > 0) & (d < 1))
+    assert len(np.unique(d)) < d.size                      # exact ties occur
+    s = gen.make_selection_bias(896, seed=0)
+    assert s.dtype == np.float32 and abs(float(s.std()) - 0.05) < 0.01
+    assert np.array_equal(s, gen.make_selection_bias(896, seed=0))
