@@ -38,7 +38,8 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_PROFILES = {"decode16": "mx_small_decode16_traffic.md", "prefill8192": "mx_mfma_prefill8192_traffic.md"}
+TRAFFIC_PROFILES = {"decode16": "mx_small_decode16_traffic.md", "prefill8192": "mx_mfma_prefill8192_traffic.md",
+                    "qb8192": "qb8192_traffic.md"}
 
 
 def measured_traffic(workload: str):
@@ -139,7 +140,9 @@ def measure_qb(L, m=8192, n=896, k=16, iters=200, with_cpu=True):
            "value": round(m / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 5),
            "roofline": {"bound": "hbm", "kernel": "moe_qb_histogram (qb_alpha_kernel + qb_hist_kernel)",
                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": h_bytes,
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(f"qb{m}") if (n, k) == (896, 16) else None,
+                        "bytes_per_launch": h_bytes,
                         "avg_launch_ms": round(h_ms, 5)},
            "bias_ms": round(b_ms, 5)}
     if with_cpu:
