@@ -60,6 +60,24 @@ def measured_traffic(workload: str):
     return rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
 
 
+def measured_mfma(workload: str):
+    """MFMA busy fraction and engine clock of the prefill gate/up launch from the committed
+    rocprofv3 counter summary, or None when it was taken on a different kernel source."""
+    import hashlib
+    if workload != "prefill8192":
+        return None
+    path = os.path.join(ROOT, "profiles", "mx_mfma_prefill8192_mfma_util.md")
+    try:
+        line = next(l for l in open(path) if l.startswith("mfma_record:"))
+        rec = json.loads(line.split(":", 1)[1])
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, StopIteration, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return {"mfma_busy": rec["mfma_busy"], "clock_ghz": rec["clock_ghz"]}
+
+
 def cpu_baseline(c, dl, x_bits, n_tokens: int):
     """The oracle, as it stands, on the first n_tokens of one batch (host cores)."""
     from oracle import layer as ol
@@ -384,6 +402,8 @@ def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False, act_fo
                     "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tf / peak, 4), "traffic": None if act_format else measured_traffic(c.name),
                     "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 5)}
+        if not act_format:
+            roofline["counters"] = measured_mfma(c.name)
         extra = {"expert_kernels_mfma_frac": round(all_flops / ((gu_ms + dn_ms) * 1e-3) / 1e12 / peak, 4)}
     else:
         gu_per_expert = 2 * (c.inter * c.latent // 2 + c.inter * c.latent // 32)     # w1 + w3, packed + scales
