@@ -190,6 +190,42 @@ def measure_hbm_read(L, gib=2, iters=10):
             "kernel": "hbm_read_kernel (moe_hbm_read)"}
 
 
+def path_sweep(L, Ts=(128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096), steps=10):
+    """The K3 layer with each expert path forced (MOE_PATH_STREAM, MOE_PATH_MFMA) across batch
+    sizes, on one resident layer: the measurement behind MOE_PATH_AUTO's threshold."""
+    import torch
+    from tests.gpu_harness import DeviceLayer, to_dev_bf16
+    from workload import gen
+    c = gen.named_config("decode16")
+    dl = DeviceLayer(c)
+    xb = gen.make_x(c, 0, T=2 * max(Ts))
+    rows = []
+    for T in Ts:
+        xs = [to_dev_bf16(xb[i * T:(i + 1) * T]) for i in range(2)]
+        y = torch.empty((T, c.hidden), dtype=torch.bfloat16, device="cuda")
+        ms = {}
+        for path in (1, 2):
+            dims = dl.dims(T, expert_path=path)
+            ws = torch.empty(L.moe_latent_workspace_size(dims, c.topk), dtype=torch.uint8, device="cuda")
+
+            def step(i):
+                L.moe_latent_forward(dims, xs[i % 2], dl.down, dl.norm, dl.router, dl.bias, dl.packed, dl.scales,
+                                     dl.up, dl.sh_packed, dl.sh_scales, c.topk, y, ws)
+            for i in range(3):
+                step(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                step(i)
+            torch.cuda.synchronize()
+            ms["stream" if path == 1 else "mfma"] = round((time.perf_counter() - t0) / steps * 1e3, 3)
+            del ws
+        auto = "mfma" if uses_mfma_path(c.with_(T=T)) else "stream"
+        rows.append({"T": T, "pairs_per_expert": round(T * c.topk / c.n_experts, 2), "layer_ms": ms, "auto": auto})
+        log(json.dumps(rows[-1]))
+    return {"path_sweep": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +242,8 @@ def main():
     ap.add_argument("--no-qb", action="store_true",
                     help="skip the secondary Quantile Balancing measurement of the default run")
     ap.add_argument("--qb-only", action="store_true", help="only the Quantile Balancing measurement")
+    ap.add_argument("--path-sweep", action="store_true",
+                    help="only the streaming-vs-MFMA expert path sweep over batch sizes")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the steps, run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -228,6 +266,9 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.copy_mb} MiB device copies")
         del src, dst
+    if args.path_sweep:
+        print(json.dumps(path_sweep(L)), flush=True)
+        return
     if args.qb_only:
         print(json.dumps(measure_qb(L, with_cpu=not args.no_cpu_baseline)), flush=True)
         return
@@ -326,7 +367,7 @@ def measure_stack(c, steps, warmup, L, DeviceLayer, to_dev_bf16):
 def uses_mfma_path(c) -> bool:
     """The library's automatic expert-path rule (MOE_PATH_AUTO in include/moe_latent.h)."""
     sizes = all(v % 512 == 0 for v in (c.hidden, c.latent, c.inter, c.shared_inter))
-    return sizes and c.T * c.topk >= 32 * c.n_experts
+    return sizes and c.T * c.topk >= 12 * c.n_experts
 
 
 def measure(c, dl, x_bits, xs, steps, warmup, L, rotate=4, summary=False, act_format=0):

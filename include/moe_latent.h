@@ -55,7 +55,10 @@ extern "C" {
  *     keeps about 8 significant bits; for prefill-sized batches. Needs hidden,
  *     latent, inter and shared_inter to be multiples of 512.
  *   MOE_PATH_AUTO: MFMA when its size rule holds and the batch averages at
- *     least 32 token slots per expert (T*k >= 32*E), else STREAM. */
+ *     least 12 token slots per expert (T*k >= 12*E), else STREAM. The
+ *     streaming path reads an expert's weights once per 16 slots, the MFMA
+ *     path once per 192; for the K3 layer on MI355X the two cross between
+ *     T = 512 and T = 768 (T*k = 10.1*E .. 13.7*E). */
 #define MOE_PATH_AUTO 0
 #define MOE_PATH_STREAM 1
 #define MOE_PATH_MFMA 2

@@ -115,7 +115,7 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.cap = moe::align_capacity(p.T, p.k, p.E, p.B);
   p.small = p.T <= 64;
   p.mfma = d->expert_path == MOE_PATH_MFMA ||
-           (d->expert_path == MOE_PATH_AUTO && mfma_sizes_ok(d) && (long long)p.pairs >= 32ll * p.E);
+           (d->expert_path == MOE_PATH_AUTO && mfma_sizes_ok(d) && (long long)p.pairs >= 12ll * p.E);
   p.fp8 = d->act_format == MOE_ACT_MXFP8;
   p.max_jobs = p.mfma ? moe::mx_max_jobs(p.pairs, p.E, moe::kMfmaSlotsPerJob) : 0;
   p.sz = slices(p.H, 2);
