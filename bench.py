@@ -11,7 +11,9 @@ on the expert-weight bytes of the gate/up launch.
 
 The default run also times the same layer at an 8192-token prefill (two
 rotating batches) and reports it under "prefill", with the MXFP4 MFMA roofline
-of its gate/up launch (algorithmic flops over the FP4/FP6 dense MFMA peak).
+of its gate/up launch (algorithmic flops over the FP4/FP6 dense MFMA peak),
+and at a 256-token decode batch with a uniform router ("decode256"), plus the
+MXFP8 mode, Quantile Balancing and the measured HBM read ceiling.
 
 Prints one JSON line (rank 0). Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -239,6 +241,8 @@ def main():
                     help="skip the secondary 8192-token prefill measurement of the default run")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the secondary measurements with MXFP8 routed-expert activations")
+    ap.add_argument("--no-decode256", action="store_true",
+                    help="skip the secondary 256-token decode measurement of the default run")
     ap.add_argument("--no-qb", action="store_true",
                     help="skip the secondary Quantile Balancing measurement of the default run")
     ap.add_argument("--qb-only", action="store_true", help="only the Quantile Balancing measurement")
@@ -292,6 +296,17 @@ def main():
         # the same decode with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
         record["decode_mxfp8"] = measure(c, dl, xs_bits, xs, args.steps, args.warmup, L, summary=True,
                                          act_format=1)
+    if not args.no_decode256 and c.name == "decode16":
+        # the large decode batch: T=256 with the uniform router (nearly every expert touched),
+        # same resident experts and projections, its own router weight
+        c2 = gen.named_config("decode256")
+        router_k3 = dl.router
+        dl.router = torch.from_numpy(np.ascontiguousarray(gen.make_dense(c2, 0)["router"])).cuda()
+        x2_bits = gen.make_x(c2, 0, T=4 * c2.T)
+        x2 = [to_dev_bf16(x2_bits[i * c2.T:(i + 1) * c2.T]) for i in range(4)]
+        record["decode256"] = measure(c2, dl, x2_bits, x2, args.steps, 5, L, summary=True)
+        dl.router = router_k3
+        del x2
     if not args.no_prefill and c.name == "decode16":
         # the 8192-token prefill on the same resident layer (the scaled-MFMA expert path)
         cp = gen.named_config("prefill8192")
