@@ -129,12 +129,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wav
 }
 
 // LDS position of 16-byte chunk c of a staged row whose index within its 16-row tile is
-// nl. The 16 lanes of a lane group read the same chunk index of 16 rows (64 banks of 4
-// bytes: 16 chunk slots per bank cycle), so each row is rotated to spread such a read
-// over all 16 slots.
+// nl. The 16 lanes of a lane group read the same chunk index of 16 rows; each row is
+// rotated so that those 16 reads fall on 16 different 16-byte bank slots.
 // FP6: a lane group's operands are chunks 3q..3q+2 (16 bytes of hi, then 8 of hi and 8
-// of lo, then 16 of lo); rows are 12 chunks long, so unrotated rows 4 apart would share
-// slots. FP8: chunks q and 4+q; rows are 8 chunks long, so rows 2 apart would.
+// of lo, then 16 of lo); rows are 12 chunks long. FP8: chunks q and 4+q; rows are 8
+// chunks long.
+// Measured on gfx950 (a ds_read_b128 probe, 4 waves per CU): the LDS reaches its full
+// rate only when each group of 16 lanes reads one contiguous 256-byte block (22 clocks
+// per wave instruction); these rotated reads take 32, as do unrotated ones, and the
+// kernel's counters show bank conflicts in 35% of its cycles. A chunk-major tile (the 16
+// rows of a chunk contiguous) cut that to 13.5%, but its LDS-DMA then gathers 16 rows x
+// 64 bytes per instruction and the kernel ran 14% slower, so the row-major tile stays.
 template <bool FP8>
 __host__ __device__ constexpr int a_rot(int nl) {
   return FP8 ? ((nl >> 1) & 7) : (((nl >> 1) & 3) ^ ((nl >> 3) & 1));
