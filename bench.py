@@ -126,27 +126,35 @@ def measure_qb(L, m=8192, n=896, k=16, iters=200, with_cpu=True):
     from workload import gen
     s_host = gen.make_router_scores(m, n, seed=0)
     b_host = gen.make_selection_bias(n, seed=0)
-    s = torch.from_numpy(s_host).cuda()
+    s0 = torch.from_numpy(s_host).cuda()
     b = torch.from_numpy(b_host).cuda()
+    # 12 row-rotated copies (12 x 29 MB, past the 256 MB last-level cache) used in turn, so that
+    # every call reads its scores from HBM
+    rot = [torch.roll(s0, shifts=37 * i, dims=0).contiguous() for i in range(12)]
+    it = [0]
+
+    def nxt():
+        it[0] += 1
+        return rot[it[0] % len(rot)]
     alpha = torch.empty(m, dtype=torch.float32, device="cuda")
     hist = torch.empty((n, 1000), dtype=torch.int32, device="cuda")
     nb = torch.empty(n, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     for _ in range(20):
-        L.moe_qb_histogram(s, b, k, alpha, hist, stream=stream)
+        L.moe_qb_histogram(nxt(), b, k, alpha, hist, stream=stream)
         L.moe_qb_bias(hist, m, k, nb, stream=stream)
     torch.cuda.synchronize()
     # events on the launch stream around `iters` calls of each entry point
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     ev[0].record(stream)
     for _ in range(iters):
-        L.moe_qb_histogram(s, b, k, alpha, hist, stream=stream)
+        L.moe_qb_histogram(nxt(), b, k, alpha, hist, stream=stream)
     ev[1].record(stream)
     for _ in range(iters):
         L.moe_qb_bias(hist, m, k, nb, stream=stream)
     ev[2].record(stream)
     for _ in range(iters):
-        L.moe_qb_update(s, b, k, alpha, hist, nb, stream=stream)
+        L.moe_qb_update(nxt(), b, k, alpha, hist, nb, stream=stream)
     ev[3].record(stream)
     torch.cuda.synchronize()
     h_ms = ev[0].elapsed_time(ev[1]) / iters
