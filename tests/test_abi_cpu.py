@@ -178,3 +178,15 @@ def test_hbm_read_argument_errors(lib):
     assert lib.moe_hbm_read(None, 64, Q, None) == -1
     assert lib.moe_hbm_read(P, 64, Q + 2, None) == -1      # checksum not 4-byte aligned
     assert lib.moe_hbm_read(P, 64, P + 32, None) == -3     # checksum inside the buffer
+
+
+def test_auto_path_threshold_at_12_slots_per_expert(lib):
+    """MOE_PATH_AUTO switches to the MFMA path (whose workspace adds the MXFP6 activation
+    tensors and the job table) at T*k = 12*E: T = 672 for the K3 layer (896 experts, top-16).
+    Forcing either path shows which one each T took."""
+    for T in (671, 672):
+        auto = _ws(lib, _dims(T=T))[1]
+        stream = _ws(lib, _dims(T=T, expert_path=1))[1]
+        mfma = _ws(lib, _dims(T=T, expert_path=2))[1]
+        assert stream != mfma
+        assert auto == (stream if T < 672 else mfma), T
