@@ -102,6 +102,11 @@ int check_dims(const moe_latent_dims* d, int topk) {
     if (cap * d->inter * 2 >= lim || (long long)d->T * d->hidden * 2 >= lim ||
         (long long)d->T * d->shared_inter * 2 >= lim)
       return MOE_EUNSUPPORTED;
+    // the MFMA path's tiled shared h rounds T up to 16 rows
+    const bool mfma = d->expert_path == MOE_PATH_MFMA ||
+                      (d->expert_path == MOE_PATH_AUTO && mfma_sizes_ok(d) && pairs >= 12ll * d->n_experts);
+    const long long t16 = ((long long)d->T + 15) / 16 * 16;
+    if (mfma && t16 * d->shared_inter * 3 / 2 >= lim) return MOE_EUNSUPPORTED;
   }
   return MOE_OK;
 }
@@ -147,14 +152,15 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.z_part = take((size_t)p.sz * ts * p.L * 4);
   p.r_part = take((size_t)p.sr * ts * p.E * 4);
   p.y_part = take((size_t)p.su * ts * p.H * 4);
-  const size_t tq = p.mfma ? (size_t)p.T : 0, cq = p.mfma ? (size_t)p.cap : 0;
+  // FP6 sizes (MXFP8 rows are smaller); h and the shared h are tiled (a multiple of 16 rows)
+  const size_t tq = p.mfma ? (size_t)p.T : 0, cq = p.mfma ? (size_t)p.cap : 0, tq16 = (tq + 15) / 16 * 16;
   p.zq = take(tq * p.L * 3 / 2);
   p.zqs = take(tq * p.L / 16);
   p.xq = take(p.Is ? tq * p.H * 3 / 2 : 0);
   p.xqs = take(p.Is ? tq * p.H / 16 : 0);
   p.hq = take(cq * p.I * 3 / 2);
   p.hqs = take(cq * p.I / 16);
-  p.hsq = take(tq * p.Is * 3 / 2);
+  p.hsq = take(tq16 * p.Is * 3 / 2);
   p.hsqs = take(tq * p.Is / 16);
   p.jobs = take((size_t)p.max_jobs * 16);
   p.n_jobs = take(p.mfma ? 4 : 0);
@@ -342,6 +348,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     uint8_t* hsqs = at<uint8_t>(ws, p.hsqs);
     const int4* jobs = at<int4>(ws, p.jobs);
     const int32_t* n_jobs = at<int32_t>(ws, p.n_jobs);
+    const int t16 = (p.T + 15) / 16 * 16;  // rows of the tiled shared h
     if (p.fp8)
       MOE_HIP(moe::launch_quant_fp8(z, p.L, p.T, p.L, zq, zqs, s));
     else
@@ -356,6 +363,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
         g.Aq = xq;
         g.Aqs = xqs;
         g.a_rows = p.T;
+        g.s_rows = p.T;
         g.routed = 0;
         g.M = p.T;
         g.W = shared->packed;
@@ -372,6 +380,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
       g.Aq = zq;
       g.Aqs = zqs;
       g.a_rows = p.T;
+      g.s_rows = p.T;
       g.routed = 1;
       g.a_by_pos = 0;
       g.sorted_ids = sorted;
@@ -400,7 +409,8 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
         moe::MfmaProblem& dn = m.p[n++];
         dn.Aq = hsq;
         dn.Aqs = hsqs;
-        dn.a_rows = p.T;
+        dn.a_rows = t16;
+        dn.s_rows = p.T;
         dn.routed = 0;
         dn.M = p.T;
         dn.W = shared->packed + 2 * sgu;
@@ -415,6 +425,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
       g.Aq = hq;
       g.Aqs = hqs;
       g.a_rows = p.cap;
+      g.s_rows = p.cap;
       g.routed = 1;
       g.a_by_pos = 1;
       g.sorted_ids = sorted;

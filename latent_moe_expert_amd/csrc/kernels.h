@@ -141,7 +141,8 @@ struct MxArgs {
 hipError_t launch_mx_small(const MxArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- MXFP6 activations (scaled-MFMA path)
-// bf16 [rows, lda] -> FP6 E2M3 hi/lo tensor of rows of K values (layout in mxfp6.h); K % 512 == 0
+// bf16 [rows, lda] -> FP6 E2M3 hi/lo tensor of rows of K values, row after row (layout in
+// mxfp6.h); K % 512 == 0
 hipError_t launch_quant_fp6(const uint16_t* A, int lda, int rows, int K, uint8_t* data, uint8_t* scales,
                             hipStream_t s);
 
@@ -164,11 +165,13 @@ hipError_t launch_mx_jobs(const int32_t* counts, int E, int B, int slots_per_job
 // Grouped MXFP4 contraction on the scaled MFMA: A = FP6 hi/lo or MXFP8 activations, B = MXFP4 weights.
 struct MfmaProblem {
   int fp8;                    // 0: A (and a GLU's h) in FP6 hi/lo (mxfp6.h); 1: in MXFP8 (mxfp8.h)
-  const uint8_t* Aq;          // A data (row stride 1.5*K bytes FP6, K bytes FP8)
-  const uint8_t* Aqs;         // A scales (row stride K/16 bytes FP6, K/32 bytes FP8)
-  int a_rows;                 // rows of the A tensor (bounds its buffer resources)
+  const uint8_t* Aq;          // A data (1.5*K bytes per row FP6, K bytes FP8): GLU problems row after
+                              // row; plain problems tiled (atile_offset), row = slot position / row
+  const uint8_t* Aqs;         // A scales, row after row (K/16 bytes per row FP6, K/32 bytes FP8)
+  int a_rows;                 // rows of the A data (plain: a multiple of 16); bounds its buffer resource
+  int s_rows;                 // rows of the scale tensor (bounds its buffer resource)
   int routed;                 // 1: jobs from the table below; 0: dense rows 0..M-1
-  int a_by_pos;               // routed: A row = slot position; else sorted_ids[slot] / topk
+  int a_by_pos;               // routed: scale row = slot position; else sorted_ids[slot] / topk
   const int32_t* sorted_ids;  // routed
   int topk;
   const int4* jobs;           // routed
@@ -181,7 +184,7 @@ struct MfmaProblem {
   const uint8_t* S2;
   size_t w_stride, s_stride;
   int N, K;                   // GLU: N = h width, multiple of 512; plain: N multiple of 256; K multiple of 512
-  uint8_t* outq;              // GLU: h rows in A's format (routed: slot position, dense: row), width N
+  uint8_t* outq;              // GLU: h rows in A's format, data tiled (routed: slot position, dense: row), width N
   uint8_t* outqs;
   float* outf;                // plain: fp32 [row, ldo] (routed: slot position)
   int ldo;

@@ -24,8 +24,21 @@
 // (opsel s picks byte s). The activation encoding stores its scales in that
 // gathered order already.
 //
+// Activation layouts. Gate/up (GLU): the A rows are the tokens' rows, stored row after
+// row and gathered through the sorted token ids; each staged row is rotated in LDS (a_rot).
+// Down (plain): A is h, which the GLU epilogue writes tiled (mxfp6.h, atile_offset: 16-row
+// tiles, chunk-major inside a tile) in slot order. A job starts at a multiple of 16 slots,
+// so one k-step of its rows is NT contiguous blocks of 16 x 192 bytes (FP6) or 16 x 128
+// (FP8): every LDS-DMA instruction moves 1 KB of contiguous memory, and the LDS tile comes
+// out chunk-major, where the 16 lanes of a lane group read one chunk of 16 rows as 256
+// contiguous bytes, the pattern at which gfx950's LDS serves ds_read_b128 without bank
+// conflicts. Measured at an 8192-token prefill on one GPU: the down launch 2.55 ms tiled
+// against 2.66 ms gathered; the gate/up launch tiled 5.30 ms against 5.46, but its rows
+// then have to be copied per slot first (750 MB, 0.17-0.2 ms), which cancels that gain,
+// so gate/up keeps the gathered rows. The scales stay row after row.
+//
 // Dataflow per block (8 waves, 2 per SIMD). The A rows of a k-step (192 rows x
-// 192 bytes FP6 or 128 FP8, gathered through the sorted token ids) go to LDS by LDS-DMA loads
+// 192 bytes FP6 or 128 FP8) go to LDS by LDS-DMA loads
 // (no registers), into a ring of four stages, three k-steps ahead of their use;
 // every wave reads all of them, one barrier per k-step. Each wave owns 32 weight
 // rows (GLU: 16 gate + the same 16 up rows) and loads them straight into MFMA
@@ -137,9 +150,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wav
 // Measured on gfx950 (a ds_read_b128 probe, 4 waves per CU): the LDS reaches its full
 // rate only when each group of 16 lanes reads one contiguous 256-byte block (22 clocks
 // per wave instruction); these rotated reads take 32, as do unrotated ones, and the
-// kernel's counters show bank conflicts in 35% of its cycles. A chunk-major tile (the 16
-// rows of a chunk contiguous) cut that to 13.5%, but its LDS-DMA then gathers 16 rows x
-// 64 bytes per instruction and the kernel ran 14% slower, so the row-major tile stays.
+// gate/up kernel's counters show bank conflicts in 35% of its cycles. A chunk-major tile
+// of the gathered rows cut that to 13.5%, but its LDS-DMA then gathers 16 rows x 64 bytes
+// per instruction and the launch ran 14% slower; the tiled layout of h (above) gives the
+// down launch chunk-major LDS tiles with contiguous DMA reads.
 template <bool FP8>
 __host__ __device__ constexpr int a_rot(int nl) {
   return FP8 ? ((nl >> 1) & 7) : (((nl >> 1) & 3) ^ ((nl >> 3) & 1));
@@ -175,23 +189,36 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
 
   const int K = a.K;
   const uint32_t arow_bytes = (uint32_t)Fm::row_bytes(K), asrow_bytes = (uint32_t)Fm::scale_row_bytes(K);
-  auto a_row = [&](int j) -> int {  // A row of job slot j, -1 past the valid slots
+  auto a_row = [&](int j) -> int {  // scale row of job slot j, -1 past the valid slots
     if (j >= nvalid) return -1;
     if (!a.routed || a.a_by_pos) return first + j;
     return a.sorted_ids[first + j] / a.topk;
   };
 
-  // ---- A stage by LDS-DMA: chunk t = tid + 512 i lands at LDS byte 16 t, i.e. position
-  // t % kChunks of staged row j = t / kChunks, and carries the row's global chunk whose
-  // rotated position that is.
+  // ---- A stage by LDS-DMA; chunk t = tid + 512 i lands at LDS byte 16 t.
+  // Gathered rows (GLU): LDS byte 16 t is position t % kChunks of staged row j = t / kChunks,
+  // which receives the row's global chunk whose rotated position that is; k-step ks starts
+  // ks * kStep bytes into a row.
+  // Tiled (plain): chunk t is byte 16 t of the job's tiles' blocks for the k-step (tile
+  // t / (16 kChunks), chunk t / 16 % kChunks of row t % 16); k-step ks starts 16 kStep * ks
+  // bytes into a tile.
   constexpr int kCh = Fm::kChunks;
+  constexpr uint32_t kAStepOff = GLU ? (uint32_t)Fm::kStep : 16u * Fm::kStep;  // buffer offset per k-step
   uint32_t goff[kADma];
 #pragma unroll
   for (int i = 0; i < kADma; ++i) {
-    const int t = tid + kThreads * i, j = t / kCh, pos = t % kCh;
-    const int c = (pos + kCh - a_rot<FP8>(j & 15)) % kCh;
-    const int r = j < NT * 16 ? a_row(j) : -1;
-    goff[i] = r >= 0 ? (uint32_t)r * arow_bytes + 16u * c : kOob;
+    const int t = tid + kThreads * i;
+    if constexpr (GLU) {
+      const int j = t / kCh, pos = t % kCh;
+      const int c = (pos + kCh - a_rot<FP8>(j & 15)) % kCh;
+      const int r = j < NT * 16 ? a_row(j) : -1;
+      goff[i] = r >= 0 ? (uint32_t)r * arow_bytes + 16u * c : kOob;
+    } else {
+      const int mf = t / (16 * kCh), j = 16 * mf + (t & 15);
+      goff[i] = j < NT * 16 && j < nvalid
+                    ? (uint32_t)((first >> 4) + mf) * 16u * arow_bytes + (uint32_t)(t % (16 * kCh)) * 16u
+                    : kOob;
+    }
   }
   uint32_t sgoff[kSDma];
 #pragma unroll
@@ -201,7 +228,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
     sgoff[i] = r >= 0 ? (uint32_t)r * asrow_bytes + 16u * c : kOob;
   }
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a.Aq, (uint32_t)a.a_rows * arow_bytes);
-  const __amdgpu_buffer_rsrc_t as_rs = make_rsrc(a.Aqs, (uint32_t)a.a_rows * asrow_bytes);
+  const __amdgpu_buffer_rsrc_t as_rs = make_rsrc(a.Aqs, (uint32_t)a.s_rows * asrow_bytes);
 
   // ---- weights: two B tiles per wave, lane (nl, q) of tile nf reads row rows(nf) + nl.
   // GLU: tile 0 = 16 gate rows, tile 1 = the same 16 up rows; plain: 32 consecutive rows.
@@ -258,7 +285,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   };
   auto dma_a = [&](uint8_t* st, int ks, bool on) {  // kADma loads
 #pragma unroll
-    for (int i = 0; i < kADma; ++i) dma16(on ? a_rs : none, a_dst_of(st, i), goff[i], (uint32_t)(ks * Fm::kStep));
+    for (int i = 0; i < kADma; ++i) dma16(on ? a_rs : none, a_dst_of(st, i), goff[i], (uint32_t)ks * kAStepOff);
   };
   auto dma_s = [&](int w, bool on) {  // kSDma loads
 #pragma unroll
@@ -289,7 +316,8 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
 #pragma unroll
   for (int u = 0; u < kRd; ++u) {
     const int c = FP8 ? q + 4 * u : 3 * q + u;
-    aoff[u] = (uint32_t)(nl * kArow + a_chunk_pos<FP8>(c, nl) * 16);
+    // gathered: chunk c of row nl at its rotated position; tiled: chunk c of the 16 rows, row nl
+    aoff[u] = GLU ? (uint32_t)(nl * kArow + a_chunk_pos<FP8>(c, nl) * 16) : (uint32_t)(c * 256 + nl * 16);
   }
   // activation scale dwords of the window, read at its start: the scale area (in stage 0)
   // receives the next window's scales from k-step 1 of the window on
@@ -410,7 +438,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
                   (uint32_t)((w + 1) * Fm::kWinScale));
           } else if constexpr (o < nS + kADma) {
             constexpr int i = o - nS;
-            dma16(a_on ? a_rs : none, a_dst_of(a_dst, i), goff[i], (uint32_t)((ks + 3) * Fm::kStep));
+            dma16(a_on ? a_rs : none, a_dst_of(a_dst, i), goff[i], (uint32_t)(ks + 3) * kAStepOff);
           } else if constexpr (o < nS + kADma + 2) {
             constexpr int nf = o - nS - kADma;
             b[bs][nf] = buf_load16(b_on ? w_rs(nf) : none, bvoff[nf], (uint32_t)(256 * bw_win + 64 * bs));
@@ -482,22 +510,21 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
         if constexpr (FP8) {
           uint32_t codes[8], sc;
           mxfp8_encode_group(v, codes, sc);
-          u32x4_t* d = (u32x4_t*)(a.outq + (size_t)(first + j) * orow_bytes + (size_t)g * 32);
-          d[0] = u32x4_t{codes[0], codes[1], codes[2], codes[3]};
-          d[1] = u32x4_t{codes[4], codes[5], codes[6], codes[7]};
+          const size_t r = (size_t)(first + j);
+          *(u32x4_t*)(a.outq + atile_offset(r, 32u * g, orow_bytes)) = u32x4_t{codes[0], codes[1], codes[2], codes[3]};
+          *(u32x4_t*)(a.outq + atile_offset(r, 32u * g + 16, orow_bytes)) =
+              u32x4_t{codes[4], codes[5], codes[6], codes[7]};
           a.outqs[(size_t)(first + j) * osrow_bytes + fp8_scale_offset(g)] = (uint8_t)sc;
           continue;
         }
         uint32_t hi[6], lo[6], s_hi, s_lo;
         fp6_encode_group(v, hi, lo, s_hi, s_lo);
-        uint8_t* drow = a.outq + (size_t)(first + j) * orow_bytes;
-        uint2* dh = (uint2*)(drow + fp6_data_offset(g, 0));
-        uint2* dl = (uint2*)(drow + fp6_data_offset(g, 1));
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          dh[u] = make_uint2(hi[2 * u], hi[2 * u + 1]);
-          dl[u] = make_uint2(lo[2 * u], lo[2 * u + 1]);
-        }
+        // the group's 48 bytes (hi, then lo) are chunks 3g .. 3g+2 of its row
+        const size_t r = (size_t)(first + j);
+        const uint32_t b = fp6_data_offset(g, 0);
+        *(u32x4_t*)(a.outq + atile_offset(r, b, orow_bytes)) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+        *(u32x4_t*)(a.outq + atile_offset(r, b + 16, orow_bytes)) = u32x4_t{hi[4], hi[5], lo[0], lo[1]};
+        *(u32x4_t*)(a.outq + atile_offset(r, b + 32, orow_bytes)) = u32x4_t{lo[2], lo[3], lo[4], lo[5]};
         uint8_t* srow = a.outqs + (size_t)(first + j) * osrow_bytes;
         srow[fp6_scale_offset(g, 0)] = (uint8_t)s_hi;
         srow[fp6_scale_offset(g, 1)] = (uint8_t)s_lo;
@@ -590,7 +617,8 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
     if (glu ? (p.N % 512) : (p.N % 256)) return hipErrorInvalidValue;
     // 32-bit byte offsets: activations, weights of one matrix, outputs
     const long long a_row_bytes = p.fp8 ? (long long)fp8_row_bytes(p.K) : (long long)fp6_row_bytes(p.K);
-    if (p.a_rows < 0 || (long long)p.a_rows * a_row_bytes >= (1ll << 31) ||
+    // plain (down) problems read A tiled: whole 16-row tiles
+    if (p.a_rows < 0 || (!glu && p.a_rows % 16) || p.s_rows < 0 || (long long)p.a_rows * a_row_bytes >= (1ll << 31) ||
         (long long)p.N * p.K / 2 >= (1ll << 31) || (!p.routed && p.M > p.a_rows))
       return hipErrorInvalidValue;
     const long long jobs = p.routed ? p.max_jobs : (p.M + kRows - 1) / kRows;

@@ -24,8 +24,10 @@
 //   scales [row][K/512 windows][plane hi|lo][4][4 B]: window w, dword q, byte s is the
 //          scale of group 16w + 4s + q
 // so MFMA lane group q of k-step 4w + s finds both planes of its group as 48
-// contiguous, 16-byte aligned bytes (three 16-byte reads fill the two operands),
+// contiguous, 16-byte aligned bytes (three 16-byte chunks fill the two operands),
 // and its four scales of the window as one aligned dword (byte s for k-step s).
+// The scales are stored row after row; the data rows are stored row after row (gate/up
+// inputs) or tiled (atile_offset; h, the down contraction's input).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,6 +39,17 @@ constexpr int kFp6WindowScaleBytes = 32;
 
 __host__ __device__ constexpr size_t fp6_row_bytes(int K) { return (size_t)K * 3 / 2; }
 __host__ __device__ constexpr size_t fp6_scale_row_bytes(int K) { return (size_t)K / 16; }
+
+// Tiled layout of the contraction's A data (FP6 hi/lo or MXFP8 rows alike). Rows come in
+// tiles of 16, and inside a tile the rows' bytes are stored chunk-major: 16-byte chunk c of
+// the 16 rows, then chunk c + 1. Byte b of row r of a tensor of row_bytes bytes per row is at
+//   (r / 16) * 16 * row_bytes + (b / 16) * 256 + (r % 16) * 16 + b % 16.
+// One k-step of a tile is then one contiguous block (LDS-DMA moves it unchanged, 1 KB per
+// instruction), and the 16 lanes of an MFMA lane group, which read one chunk of 16 rows,
+// read 256 contiguous bytes of LDS. A tiled tensor holds a multiple of 16 rows.
+__host__ __device__ inline size_t atile_offset(size_t r, size_t b, size_t row_bytes) {
+  return (r >> 4) * 16 * row_bytes + (b >> 4) * 256 + (r & 15) * 16 + (b & 15);
+}
 
 typedef __attribute__((ext_vector_type(16))) float fp6_f32x16_t;
 typedef __attribute__((ext_vector_type(32))) float fp6_f32x32_t;

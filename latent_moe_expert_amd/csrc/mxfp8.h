@@ -16,6 +16,8 @@
 //          group 16w + 4s + q, so MFMA lane group q, which supplies the scale of K
 //          block q of a k-step, finds its four scales of the window in one dword (byte
 //          s for k-step 4w + s).
+// The data rows of h (the down contraction's input) are stored tiled instead
+// (atile_offset in mxfp6.h); the bytes of each row are the same.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
