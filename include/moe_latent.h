@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 4
+#define MOE_LATENT_ABI_VERSION 5
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, negative or inconsistent size */
@@ -126,6 +126,9 @@ typedef struct moe_latent_taps {
   uint16_t* c_norm;       /* bf16 [T, L]  input of the up-projection */
   float* y_routed;        /* fp32 [T, H]  up-projection output */
   float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none) */
+  float* O;               /* fp32 [capacity, L] each routed expert's output for the slot at that
+                             position of sorted_ids, before the routing weight; rows of padding
+                             positions are unspecified */
 } moe_latent_taps;
 
 int moe_latent_abi_version(void);
@@ -153,8 +156,12 @@ int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacit
  *   up              bf16 [H, L]   routed_expert_up_proj
  *   shared          merged shared GLU or NULL
  *   topk            experts per token, 1 <= topk <= min(E, 64)
- *   y               bf16 [T, H] output; must not overlap x or the workspace
+ *   y               bf16 [T, H] output
  *   workspace       >= moe_latent_workspace_size bytes, 256-byte aligned
+ *
+ * Aliasing: y, the workspace and every tap must overlap no input (x, down, norm,
+ * router weight and bias, the expert records, up, the shared record) and no other
+ * of them (MOE_EALIAS); inputs may overlap one another.
  *
  * Routing: s = sigmoid(x . W_r^T), key = s + select_bias; the topk largest keys
  * win, ties to the lower expert id; weights w = s / sum(s_selected) * rsf. The
@@ -188,7 +195,9 @@ int moe_align_workspace_size(int T, int topk, int n_experts, size_t* bytes);
  * moe_align_block_size (SlimServe quants.md, note on the alignment fix): the
  * expert-sorted layout of the T*topk (token, slot) pairs.
  *   topk_ids   [T, topk], ids in [0, E), each token listing an expert at most
- *              once (ids outside the range are dropped and get inv_pos -1)
+ *              once (the router's ids are distinct). Ids outside the range get no
+ *              entry and inv_pos -1; an id a token repeats keeps its first slot and
+ *              its later slots are handled like ids out of range.
  *   block      B >= 1: every expert segment is padded to a multiple of B; a
  *              consumer with tile height h | B expands expert_ids B/h times
  *   sorted_ids [capacity]: segments in ascending expert id, each the flat
@@ -282,16 +291,42 @@ int moe_qb_bias(const int32_t* hist, int n, long long m_total, int topk, float* 
 int moe_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, void* stream);
 
 /*
+ * RMSNorm of bf16 rows, y = x / sqrt(mean(x^2) + eps) * g, with g = 1 when weight
+ * is NULL. The layer applies the same formula to the aggregated latent (K3
+ * report review, "Stable LatentMoE"; WASTE "Kimi K3, as released", "Against the
+ * technical report": RMSNorm before the up-projection); a decoder applies it
+ * without the MoE, before each layer's input, which is what a stack of layers
+ * needs between one layer's output and the next layer's input.
+ *   x, y    bf16 [rows, cols] device, 8-byte aligned; y may equal x (in place),
+ *           other overlaps are MOE_EALIAS
+ *   weight  bf16 [cols] device or NULL; must not overlap y
+ *   cols    multiple of 4; rows >= 0 (0 enqueues nothing); eps >= 0
+ * Sum of squares in fp32 in a fixed order (bitwise reproducible), result rounded
+ * to bf16 (nearest even).
+ */
+int moe_rmsnorm(const void* x, int rows, int cols, const void* weight, float eps, void* y, void* stream);
+
+/*
  * Stage timing for measurement. While enabled, moe_latent_forward records HIP
  * events around each stage on its stream (at most 256 forwards are kept).
  * moe_latent_timing_read synchronises on the recorded events and returns, per
  * stage, the summed milliseconds and the number of forwards recorded; it then
- * clears the record. Stage names: moe_latent_stage_name(i), i < stage count.
+ * clears the record. A forward that returned an error is not counted (its record
+ * is incomplete and skipped). Stage names: moe_latent_stage_name(i), i < stage
+ * count.
  */
 int moe_latent_timing_enable(int on);
 int moe_latent_stage_count(void);
 const char* moe_latent_stage_name(int i);
 int moe_latent_timing_read(float* ms_per_stage /* host [stage count] */, int* n_forwards /* host */);
+
+/*
+ * Releases what the library keeps between calls: the stage-timing events (timing
+ * is switched off and its record cleared). Call it with no forward in flight,
+ * e.g. before the process unloads the library; later calls work as before (the
+ * events are created again when timing is enabled).
+ */
+int moe_latent_shutdown(void);
 
 #ifdef __cplusplus
 }

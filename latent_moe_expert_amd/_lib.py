@@ -32,7 +32,7 @@ class MoeShared(ctypes.Structure):
 
 
 TAP_FIELDS = ["z", "logits", "topk_ids", "topk_w", "counts", "sorted_ids", "expert_ids", "num_post", "inv_pos",
-              "c", "c_norm", "y_routed", "y_shared"]
+              "c", "c_norm", "y_routed", "y_shared", "O"]
 
 
 class MoeLatentTaps(ctypes.Structure):
@@ -44,7 +44,8 @@ EXPORTS = ["moe_latent_abi_version", "moe_latent_strerror", "moe_latent_last_hip
            "moe_route", "moe_align_workspace_size", "moe_align_block_size", "moe_mxfp8_round",
            "moe_qb_histogram", "moe_qb_update", "moe_qb_target", "moe_qb_bias", "moe_hbm_read",
            "moe_latent_timing_enable",
-           "moe_latent_stage_count", "moe_latent_stage_name", "moe_latent_timing_read"]
+           "moe_latent_stage_count", "moe_latent_stage_name", "moe_latent_timing_read", "moe_latent_shutdown",
+           "moe_rmsnorm"]
 
 _lib = None
 
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
         "moe_latent_stage_count": ([], I),
         "moe_latent_stage_name": ([I], ctypes.c_char_p),
         "moe_latent_timing_read": ([ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)], I),
+        "moe_latent_shutdown": ([], I),
+        "moe_rmsnorm": ([P, I, I, P, ctypes.c_float, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

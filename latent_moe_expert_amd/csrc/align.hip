@@ -19,7 +19,9 @@
 //   scatter one block per chunk rebuilds the masks; a slot's rank inside its
 //           expert is (chunk prefix) + popcount(mask & lower tokens).
 // Each token lists an expert at most once (the router's ids are distinct), so
-// token order inside an expert equals flat-index order.
+// token order inside an expert equals flat-index order. An id a token repeats is
+// kept at its first slot only; the later slots are treated like ids out of range
+// (no entry, inv_pos -1), so the result is still deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,6 +43,13 @@ __device__ void build_masks(const int32_t* __restrict__ ids, int T, int k, int E
     if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << (i / k));
   }
   __syncthreads();
+}
+
+// true when slot j of the token whose ids start at tok repeats the id of an earlier slot
+__device__ __forceinline__ bool repeated_in_token(const int32_t* __restrict__ tok, int j, int e) {
+  for (int u = 0; u < j; ++u)
+    if (tok[u] == e) return true;
+  return false;
 }
 
 __global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -116,11 +125,11 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   for (int i = threadIdx.x; i < np; i += blockDim.x) {
     const int flat = t0 * k + i;
     const int e = ids[flat];
-    if (e < 0 || e >= E) {
+    const int tl = i / k;
+    if (e < 0 || e >= E || repeated_in_token(ids + (size_t)(t0 + tl) * k, i - tl * k, e)) {
       inv_pos[flat] = -1;
       continue;
     }
-    const int tl = i / k;
     const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
     const int pos = offs[e] + chunk_pre[(size_t)blockIdx.x * E + e] + __popcll(below);
     sorted_ids[pos] = flat;
@@ -174,11 +183,11 @@ __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __res
   __syncthreads();
   for (int i = tid; i < pairs; i += 1024) {
     const int e = ids[i];
-    if (e < 0 || e >= E) {
+    const int tl = i / k;
+    if (e < 0 || e >= E || repeated_in_token(ids + (size_t)tl * k, i - tl * k, e)) {
       inv_pos[i] = -1;
       continue;
     }
-    const int tl = i / k;
     const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
     const int pos = offs[e] + __popcll(below);
     sorted_ids[pos] = i;

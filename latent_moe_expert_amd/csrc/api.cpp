@@ -38,8 +38,10 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   std::vector<hipEvent_t> ev;  // kMaxTimed * (kNumStages + 1)
-  int n = 0;                   // forwards recorded
-  hipEvent_t* slot() {         // events of the next forward, or null when full
+  std::vector<char> done;      // record f complete: every stage event of that forward was recorded
+  int n = 0;                   // records claimed
+  // events of the next forward (claimed, not yet complete), or null when full
+  hipEvent_t* claim(int* idx) {
     if (n >= kMaxTimed) return nullptr;
     const size_t need = (size_t)(n + 1) * (kNumStages + 1);
     while (ev.size() < need) {
@@ -47,7 +49,16 @@ struct Timing {
       if (hipEventCreate(&e) != hipSuccess) return nullptr;
       ev.push_back(e);
     }
-    return &ev[(size_t)n * (kNumStages + 1)];
+    done.resize((size_t)n + 1);
+    done[(size_t)n] = 0;
+    *idx = n++;
+    return &ev[(size_t)*idx * (kNumStages + 1)];
+  }
+  void release() {  // caller holds mu
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    done.clear();
+    n = 0;
   }
 } g_timing;
 
@@ -100,7 +111,13 @@ int check_dims(const moe_latent_dims* d, int topk) {
     const long long cap = B * ((pairs + (pairs < d->n_experts ? pairs : d->n_experts) * (B - 1)) / B);
     const long long lim = 1ll << 31;
     if (cap * d->inter * 2 >= lim || (long long)d->T * d->hidden * 2 >= lim ||
-        (long long)d->T * d->shared_inter * 2 >= lim)
+        (long long)d->T * d->shared_inter * 2 >= lim || (long long)d->T * d->latent * 2 >= lim)
+      return MOE_EUNSUPPORTED;
+    // weight matrices the kernels index with 32-bit byte offsets: the bf16 projections, the
+    // fp32 router (and its three bf16 planes), one MXFP4 matrix of an expert or of the shared GLU
+    const long long H = d->hidden, L = d->latent, E = d->n_experts;
+    if (L * H * 2 >= lim || E * H * 6 >= lim || (long long)d->inter * L / 2 >= lim ||
+        (long long)d->shared_inter * H / 2 >= lim)
       return MOE_EUNSUPPORTED;
     // the MFMA path's tiled shared h rounds T up to 16 rows
     const bool mfma = d->expert_path == MOE_PATH_MFMA ||
@@ -180,6 +197,57 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
+// Every buffer the forward writes (y, the workspace, each tap) must overlap no buffer it
+// reads and no other buffer it writes. Inputs may overlap one another (they are only read).
+bool check_alias(const moe_latent_dims* d, const Plan& p, const void* x, const void* down, const void* norm,
+                 const moe_router* router, const uint8_t* packed, const uint8_t* scales, const void* up,
+                 const moe_shared* shared, const void* y, const void* workspace, const moe_latent_taps* taps) {
+  struct Range {
+    const void* p;
+    size_t n;
+  };
+  const size_t T = p.T, H = p.H, L = p.L, E = p.E, I = p.I, Is = p.Is;
+  const size_t rec = 3 * I * L / 2, srec = 3 * I * L / 32;
+  const Range in[] = {
+      {x, T * H * 2},
+      {down, L * H * 2},
+      {norm, L * 2},
+      {router->weight, E * H * 4},
+      {router->select_bias, E * 4},
+      {packed, E * rec},
+      {scales, E * srec},
+      {up, H * L * 2},
+      {shared ? shared->packed : nullptr, 3 * Is * H / 2},
+      {shared ? shared->scales : nullptr, 3 * Is * H / 32},
+  };
+  std::vector<Range> out = {{y, T * H * 2}, {workspace, p.total}};
+  if (taps) {
+    const size_t pairs = p.pairs, cap = p.cap;
+    out.push_back({taps->z, T * L * 2});
+    out.push_back({taps->logits, T * E * 4});
+    out.push_back({taps->topk_ids, pairs * 4});
+    out.push_back({taps->topk_w, pairs * 4});
+    out.push_back({taps->counts, E * 4});
+    out.push_back({taps->sorted_ids, cap * 4});
+    out.push_back({taps->expert_ids, cap / p.B * 4});
+    out.push_back({taps->num_post, 4});
+    out.push_back({taps->inv_pos, pairs * 4});
+    out.push_back({taps->c, T * L * 4});
+    out.push_back({taps->c_norm, T * L * 2});
+    out.push_back({taps->y_routed, T * H * 4});
+    out.push_back({taps->y_shared, T * H * 4});
+    out.push_back({taps->O, cap * L * 4});
+  }
+  (void)d;
+  for (size_t i = 0; i < out.size(); ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i].p, out[i].n, r.p, r.n)) return true;
+    for (size_t j = i + 1; j < out.size(); ++j)
+      if (overlap(out[i].p, out[i].n, out[j].p, out[j].n)) return true;
+  }
+  return false;
+}
+
 int copy_tap(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (!dst || !bytes) return MOE_OK;
   MOE_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
@@ -240,8 +308,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
   const Plan p = make_plan(d, topk);
   if (!workspace) return MOE_EWORKSPACE;
   if (ws_bytes < p.total || ((uintptr_t)workspace & 255)) return MOE_EWORKSPACE;
-  const size_t xb = (size_t)p.T * p.H * 2, yb = (size_t)p.T * p.H * 2;
-  if (overlap(y, yb, x, xb) || overlap(y, yb, workspace, p.total) || overlap(workspace, p.total, x, xb))
+  if (check_alias(d, p, x, down, norm, router, experts_packed, experts_scales, up, shared, y, workspace, taps))
     return MOE_EALIAS;
 
   hipStream_t s = (hipStream_t)stream;
@@ -261,13 +328,14 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
   uint16_t* hs = at<uint16_t>(ws, p.hs);
   float* ys = at<float>(ws, p.ys);
 
+  // Stage events: the record is claimed here and marked complete after the last stage
+  // event; a forward that fails on the way leaves an incomplete record, which
+  // moe_latent_timing_read skips.
   hipEvent_t* ev = nullptr;
+  int ev_idx = -1;
   {
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    if (g_timing.on) {
-      ev = g_timing.slot();
-      if (ev) ++g_timing.n;
-    }
+    if (g_timing.on) ev = g_timing.claim(&ev_idx);
   }
   auto mark = [&](int i) -> int {
     if (ev) MOE_HIP(hipEventRecord(ev[i], s));
@@ -569,6 +637,10 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
   STAGE_MARK(8);
+  if (ev) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (ev_idx < (int)g_timing.done.size()) g_timing.done[(size_t)ev_idx] = 1;
+  }
 
   if (taps) {
     int r;
@@ -582,6 +654,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     if ((r = copy_tap(taps->num_post, num_post, 4, s))) return r;
     if ((r = copy_tap(taps->inv_pos, inv_pos, (size_t)p.pairs * 4, s))) return r;
     if ((r = copy_tap(taps->c_norm, cn, (size_t)p.T * p.L * 2, s))) return r;
+    if ((r = copy_tap(taps->O, O, (size_t)p.cap * p.L * 4, s))) return r;
     if (taps->y_shared) {
       if (shared) {
         if ((r = copy_tap(taps->y_shared, ys, (size_t)p.T * p.H * 4, s))) return r;
@@ -738,17 +811,42 @@ int moe_latent_timing_read(float* ms_per_stage, int* n_forwards) {
   if (!ms_per_stage || !n_forwards) return MOE_EINVAL;
   std::lock_guard<std::mutex> lk(g_timing.mu);
   for (int i = 0; i < kNumStages; ++i) ms_per_stage[i] = 0.f;
-  for (int f = 0; f < g_timing.n; ++f) {
+  const int n = g_timing.n;
+  g_timing.n = 0;  // the record is cleared whatever happens below
+  int done = 0, rc = MOE_OK;
+  for (int f = 0; f < n && rc == MOE_OK; ++f) {
+    if (!g_timing.done[(size_t)f]) continue;  // a forward that returned an error
     hipEvent_t* e = &g_timing.ev[(size_t)f * (kNumStages + 1)];
-    MOE_HIP(hipEventSynchronize(e[kNumStages]));
-    for (int i = 0; i < kNumStages; ++i) {
+    hipError_t he = hipEventSynchronize(e[kNumStages]);
+    for (int i = 0; i < kNumStages && he == hipSuccess; ++i) {
       float ms = 0.f;
-      MOE_HIP(hipEventElapsedTime(&ms, e[i], e[i + 1]));
+      he = hipEventElapsedTime(&ms, e[i], e[i + 1]);
       ms_per_stage[i] += ms;
     }
+    if (he != hipSuccess) rc = hip_fail(he);
+    ++done;
   }
-  *n_forwards = g_timing.n;
-  g_timing.n = 0;
+  *n_forwards = rc == MOE_OK ? done : 0;
+  return rc;
+}
+
+int moe_latent_shutdown(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = false;
+  g_timing.release();
+  return MOE_OK;
+}
+
+int moe_rmsnorm(const void* x, int rows, int cols, const void* weight, float eps, void* y, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 4 || !(eps >= 0.f)) return MOE_EINVAL;
+  if ((long long)rows * cols * 2 >= (1ll << 40)) return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !y || ((uintptr_t)x & 7) || ((uintptr_t)y & 7) || ((uintptr_t)weight & 7)) return MOE_EINVAL;
+  const size_t bytes = (size_t)rows * cols * 2;
+  if (x != y && overlap(x, bytes, y, bytes)) return MOE_EALIAS;
+  if (overlap(y, bytes, weight, (size_t)cols * 2)) return MOE_EALIAS;
+  MOE_HIP(moe::launch_rmsnorm((const uint16_t*)x, rows, cols, (const uint16_t*)weight, eps, (uint16_t*)y,
+                              (hipStream_t)stream));
   return MOE_OK;
 }
 

@@ -94,11 +94,48 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restri
   }
 }
 
+// RMSNorm of bf16 rows: y = x / sqrt(mean(x^2) + eps) * g (g = 1 without a weight), one
+// block per row. Pass 1 sums the squares (each thread its columns in ascending order,
+// then a fixed-order wave and block reduction); pass 2 re-reads the row (from L2) and
+// writes it, each element read before its own store, so y may be x.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x, int cols,
+                                                      const uint16_t* __restrict__ g, float eps, uint16_t* y) {
+  __shared__ float red[4];
+  const size_t row = (size_t)blockIdx.x * cols;
+  const int nvec = cols >> 2;
+  float ss = 0.f;
+  for (int v = threadIdx.x; v < nvec; v += 256) {
+    const uint2 u = *(const uint2*)(x + row + 4 * v);
+    const float a = bf16_bits_to_f32(u.x & 0xffffu), b = bf16_bits_to_f32(u.x >> 16);
+    const float c = bf16_bits_to_f32(u.y & 0xffffu), d = bf16_bits_to_f32(u.y >> 16);
+    ss += a * a + b * b + c * c + d * d;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float scale = rsqrtf((((red[0] + red[1]) + red[2]) + red[3]) / (float)cols + eps);
+  for (int v = threadIdx.x; v < nvec; v += 256) {
+    const uint2 u = *(const uint2*)(x + row + 4 * v);
+    float o[4] = {bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xffffu),
+                  bf16_bits_to_f32(u.y >> 16)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = g ? o[e] * scale * bf16_bits_to_f32(g[4 * v + e]) : o[e] * scale;
+    *(uint2*)(y + row + 4 * v) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  }
+}
+
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
 }  // namespace
+
+hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t* g, float eps, uint16_t* y,
+                          hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, cols, g, eps, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
   if (n == 0) return hipSuccess;

@@ -200,6 +200,10 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
 hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
                                const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
 
+// y = x / sqrt(mean(x^2) + eps) * g per row (g null: no weight); bf16 [rows, cols], cols % 4 == 0; y may be x
+hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t* g, float eps, uint16_t* y,
+                          hipStream_t s);
+
 // ---------------------------------------------------------------- Quantile Balancing
 constexpr int kQbBins = 1000;
 // alpha [m] = (k+1)-th largest of scores[t] + bias; hist [n, kQbBins] int32 = margin histograms.

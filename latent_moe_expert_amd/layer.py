@@ -217,3 +217,18 @@ def moe_latent_timing_read() -> tuple:
     nf = ctypes.c_int(0)
     _check("moe_latent_timing_read", lib.moe_latent_timing_read(arr, ctypes.byref(nf)))
     return dict(zip(moe_latent_stage_names(), list(arr))), nf.value
+
+
+def moe_latent_shutdown() -> None:
+    _check("moe_latent_shutdown", _lib.load().moe_latent_shutdown())
+
+
+def moe_rmsnorm(x, y, weight=None, eps: float = 1e-6, stream=None) -> None:
+    """y = RMSNorm(x) per row (bf16 [rows, cols]); weight bf16 [cols] or None; y may be x."""
+    if x.dim() != 2 or tuple(y.shape) != tuple(x.shape):
+        raise ValueError("x and y: the same [rows, cols] shape")
+    if weight is not None and weight.numel() != x.shape[1]:
+        raise ValueError("weight: [cols]")
+    rc = _lib.load().moe_rmsnorm(_ptr(x, _BF16, "x"), x.shape[0], x.shape[1], _ptr(weight, _BF16, "weight"), eps,
+                                 _ptr(y, _BF16, "y"), _stream(stream))
+    _check("moe_rmsnorm", rc)

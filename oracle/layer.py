@@ -75,6 +75,15 @@ def rmsnorm(c, g, eps: float):
     return out if g is None else out * np.asarray(g, dtype=np.float64)
 
 
+def chain_input(y_bits: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """The next layer's input in a stack of layers: the weightless RMSNorm of this layer's
+    bf16 output, rounded to bf16 (reading R16). The pages put an RMSNorm in front of each
+    decoder block's input (K3 report review, section on Block AttnRes: standard PreNorm
+    residuals); without it the chained outputs grow by the shared experts' gain at every
+    layer. Harness glue between layers, not part of the layer."""
+    return f64_to_bf16(rmsnorm(bf16_to_f64(y_bits), None, eps))
+
+
 # --------------------------------------------------------------------------- router
 
 def route(x64: np.ndarray, router_w: np.ndarray, select_bias: Optional[np.ndarray], k: int,

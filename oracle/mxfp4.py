@@ -21,11 +21,12 @@ def decode(packed: np.ndarray, scales: np.ndarray, rows: int, cols: int) -> np.n
         raise ValueError("cols must be a multiple of 32")
     p = np.asarray(packed, dtype=np.uint8).reshape(rows, cols // 2)
     s = np.asarray(scales, dtype=np.uint8).reshape(rows, cols // 32)
-    vals = np.empty((rows, cols), dtype=np.float64)
-    vals[:, 0::2] = E2M1_TABLE[p & 0x0F]
-    vals[:, 1::2] = E2M1_TABLE[p >> 4]
-    scale = np.repeat(e8m0_value(s), 32, axis=1)
-    return vals * scale
+    # element 2j (low nibble of byte j) then element 2j+1 (high nibble): stacked on a last
+    # axis of 2, so that row-major order of [rows, cols/2, 2] is the element order
+    vals = np.stack([E2M1_TABLE[p & 0x0F], E2M1_TABLE[p >> 4]], axis=-1)
+    # one scale per 32 consecutive elements of a row
+    vals = vals.reshape(rows, cols // 32, 32) * e8m0_value(s)[:, :, None]
+    return vals.reshape(rows, cols)
 
 
 def split_glu_record(packed: np.ndarray, scales: np.ndarray, inp: int, inter: int):

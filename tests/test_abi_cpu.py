@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.moe_latent_abi_version() == 4
+    assert lib.moe_latent_abi_version() == 5
     for code in range(0, -7, -1):
         assert lib.moe_latent_strerror(code)
     assert lib.moe_latent_stage_count() == 8
@@ -70,6 +70,9 @@ def test_workspace_size_and_layout(lib):
     (dict(align_block=24), 16, -2), (dict(T=-1), 16, -1), (dict(n_experts=8), 9, -1),
     (dict(), 0, -1), (dict(), 65, -2), (dict(rms_eps=-1.0), 16, -1),
     (dict(act_format=2), 16, -1), (dict(act_format=-1), 16, -1),
+    # the latent z [T, L] bf16 is indexed with 32-bit byte offsets: T * L * 2 below 2 GiB
+    (dict(T=131072, hidden=256, latent=8192, n_experts=1, inter=256, shared_inter=0), 1, -2),
+    (dict(T=131071, hidden=256, latent=8192, n_experts=1, inter=256, shared_inter=0), 1, 0),
 ])
 def test_dims_validation(lib, kw, k, code):
     rc, _ = _ws(lib, _dims(**kw), k)
@@ -104,6 +107,60 @@ def test_forward_argument_errors_before_any_launch(lib):
     n = _ws(lib, d)[1]
     assert _forward(lib, d, y=0x200000000 + n // 2) == -3   # y inside the workspace
     assert _forward(lib, _dims(T=0)) == 0                  # nothing to do, nothing enqueued
+
+
+# fake device addresses for the alias checks, each range far from the others
+_X, _DOWN, _ROUTER, _BIAS, _UP, _SHP, _SHS = 0x10000, 0x1000000, 0x8000000, 0x9000000, 0xa000000, 0x10000000, 0x18000000
+_PACKED, _SCALES, _WS, _Y, _TAPS = 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44
+
+
+def _forward_ex(lib, d, taps, k=16, y=_Y, packed=_PACKED):
+    router = _lib.MoeRouter(_ROUTER, _BIAS)
+    sh = _lib.MoeShared(_SHP, _SHS)
+    tp = _lib.MoeLatentTaps(ctypes.sizeof(_lib.MoeLatentTaps), *[taps.get(n) for n in _lib.TAP_FIELDS])
+    return lib.moe_latent_forward_ex(ctypes.byref(d), _X, _DOWN, None, ctypes.byref(router), packed, _SCALES, _UP,
+                                     ctypes.byref(sh), k, y, _WS, _ws(lib, d, k)[1], None, ctypes.byref(tp))
+
+
+def test_forward_alias_checks_cover_weights_and_taps(lib):
+    """y, the workspace and every tap may overlap no input and no other output; inputs may
+    overlap one another. Without a GPU a call that passes every check fails at its first
+    launch (MOE_EHIP), never with MOE_EALIAS."""
+    d = _dims(T=4)
+    assert _forward_ex(lib, d, {}) == -5
+    assert _forward_ex(lib, d, {"z": _TAPS, "O": _TAPS + (1 << 32)}) == -5
+    # y on the expert records (E x 17,547,264 bytes from _PACKED on), on the selection bias
+    assert _forward_ex(lib, d, {}, y=_PACKED + 5 * 16515072) == -3
+    assert _forward_ex(lib, d, {}, y=_BIAS) == -3
+    # a tap on an input, on y, on the workspace, on another tap
+    assert _forward_ex(lib, d, {"z": _DOWN + 64}) == -3
+    assert _forward_ex(lib, d, {"c": _Y + 64}) == -3
+    assert _forward_ex(lib, d, {"O": _WS + 4096}) == -3
+    assert _forward_ex(lib, d, {"c": _TAPS, "y_shared": _TAPS + 8}) == -3
+    # the expert records overlapping the down-projection are only read: no alias
+    assert _forward_ex(lib, d, {}, packed=_DOWN) == -5
+
+
+def test_shutdown_releases_timing(lib):
+    assert lib.moe_latent_timing_enable(1) == 0
+    assert lib.moe_latent_shutdown() == 0
+    arr = (ctypes.c_float * 9)()
+    nf = ctypes.c_int(-1)
+    assert lib.moe_latent_timing_read(arr, ctypes.byref(nf)) == 0 and nf.value == 0
+    assert lib.moe_latent_shutdown() == 0                  # idempotent
+
+
+def test_rmsnorm_argument_errors(lib):
+    P, Q, W = 0x100000, 0x900000, 0x2000000
+    assert lib.moe_rmsnorm(P, -1, 64, None, 1e-6, Q, None) == -1
+    assert lib.moe_rmsnorm(P, 4, 62, None, 1e-6, Q, None) == -1       # cols not a multiple of 4
+    assert lib.moe_rmsnorm(P, 4, 64, None, -1.0, Q, None) == -1       # negative eps
+    assert lib.moe_rmsnorm(None, 4, 64, None, 1e-6, Q, None) == -1
+    assert lib.moe_rmsnorm(P + 4, 4, 64, None, 1e-6, Q, None) == -1   # not 8-byte aligned
+    assert lib.moe_rmsnorm(P, 4, 64, None, 1e-6, P + 128, None) == -3  # partial overlap
+    assert lib.moe_rmsnorm(P, 4, 64, Q + 64, 1e-6, Q, None) == -3     # weight inside y
+    assert lib.moe_rmsnorm(None, 0, 64, None, 1e-6, None, None) == 0  # nothing to do, nothing enqueued
+    assert lib.moe_rmsnorm(P, 4, 64, W, 1e-6, P, None) != -3          # in place is allowed
 
 
 def test_align_argument_errors(lib):

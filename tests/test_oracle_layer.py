@@ -199,3 +199,23 @@ def test_closed_form_with_signed_permutation_weights():
         ys = hs[g2] * b2
         np.testing.assert_allclose(out["y_routed"][t], yr, rtol=1e-12, atol=1e-300)
         np.testing.assert_allclose(out["y_shared"][t], ys, rtol=1e-12, atol=1e-300)
+
+
+def test_chain_input_closed_forms():
+    """The stack's chaining step (weightless RMSNorm of a layer's bf16 output, rounded to
+    bf16): a hand-computed row, constant rows, exact scale invariance with eps = 0, and
+    unit RMS up to bf16 rounding."""
+    f = lambda v: np.asarray(v, np.float32).view(np.uint32).__rshift__(16).astype(np.uint16)
+    # [3, 4, 0, 0]: mean square 6.25, RMS 2.5 -> [1.2, 1.6, 0, 0], rounded to bf16 by hand:
+    # 1.2 = 1.0011001|1001..b -> 1.0011010b = 0x3f9a; 1.6 = 1.1001100|1100..b -> 0x3fcd
+    out = layer.chain_input(f([[3.0, 4.0, 0.0, 0.0]]), eps=0.0)
+    assert out.tolist() == [[0x3F9A, 0x3FCD, 0, 0]]
+    # constant rows normalise to +-1 exactly
+    out = layer.chain_input(f([[7.5] * 8, [-0.25] * 8]), eps=0.0)
+    assert (out[0] == 0x3F80).all() and (out[1] == 0xBF80).all()
+    rng = np.random.default_rng(5)
+    y = f(rng.standard_normal((6, 256)) * 300.0)
+    y2 = f(bf16_to_f64(y) * 2.0)                       # exact: doubling a bf16 value
+    assert np.array_equal(layer.chain_input(y, eps=0.0), layer.chain_input(y2, eps=0.0))
+    rms = np.sqrt(np.mean(bf16_to_f64(layer.chain_input(y)) ** 2, axis=1))
+    assert np.all(np.abs(rms - 1.0) <= 2.0 ** -8)

@@ -62,3 +62,14 @@ def test_router_scores_and_bias_streams():
     s = gen.make_selection_bias(896, seed=0)
     assert s.dtype == np.float32 and abs(float(s.std()) - 0.05) < 0.01
     assert np.array_equal(s, gen.make_selection_bias(896, seed=0))
+
+
+def test_stack_zipf_amplitude_matches_its_calibration():
+    """The stacked workload's bias amplitude is the one tests/golden/zipf_amplitude.py found
+    (hottest expert of layer 0 at about 10x the mean load, reading R13)."""
+    import json
+    import os
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "zipf_amplitude.json")))
+    c = gen.named_config("stack8x4096")
+    assert rec["workload"] == c.name and rec["zipf_s"] == c.zipf_s and rec["zipf_c"] == c.zipf_c
+    assert abs(rec["ratio"] - 10.0) < 0.5

@@ -100,8 +100,11 @@ NAMED_CONFIGS = {
     "decode256": LayerConfig("decode256", T=256, router_dist="uniform"),
     # Prefill of 8192 tokens.
     "prefill8192": LayerConfig("prefill8192", T=8192),
-    # Eight chained layers, 4096 tokens, Zipf(1.1) selection bias.
-    "stack8x4096": LayerConfig("stack8x4096", T=4096, n_layers=8, zipf_s=1.1, zipf_c=0.25),
+    # Eight chained layers, 4096 tokens, Zipf(1.1) selection bias. The amplitude puts the
+    # hottest expert of layer 0 at about 10x the mean load (731 of 65,536 pairs); it was
+    # found by bisection over the oracle's router (tests/golden/zipf_amplitude.py, which
+    # records it in tests/golden/zipf_amplitude.json).
+    "stack8x4096": LayerConfig("stack8x4096", T=4096, n_layers=8, zipf_s=1.1, zipf_c=0.1754),
 }
 
 
