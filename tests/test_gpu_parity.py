@@ -246,7 +246,72 @@ def test_tiny_named_config_full_width():
 
 # ------------------------------------------------------------------ full K3 layer sizes
 
-def _full_case(name, sample):
+SLOTS_PER_JOB = 192      # the MFMA path's job size (12 row tiles of 16)
+
+
+def _job_table(counts, spj=SLOTS_PER_JOB):
+    """(expert, first slot within the expert, valid slots) per job, in the order the MFMA
+    path numbers its jobs: experts ascending, each split into chunks of spj slots."""
+    jobs = []
+    for e, n in enumerate(counts.tolist()):
+        for f in range(0, n, spj):
+            jobs.append((e, f, min(spj, n - f)))
+    return jobs
+
+
+def _tile_bucket(nvalid):
+    tiles = -(-nvalid // 16)
+    return 4 if tiles <= 4 else 8 if tiles <= 8 else 10 if tiles <= 10 else 12
+
+
+def _pick_mfma_cases(out, k, n_random, seed):
+    """Experts whose every slot is compared (tap O) and tokens whose outputs are compared,
+    chosen from the job table so that they cover: every row-tile bucket (4/8/10/12), all 8
+    XCD classes (job index mod 8), the last job, an expert split over several jobs, the
+    last valid row of a full 192-slot job, a row of a later job and a partial 16-row tile."""
+    counts = out["counts"]
+    jobs = _job_table(counts)
+    experts, tokens = [], set()
+    want_bucket = {4, 8, 10, 12}
+    want_xcd = set(range(8))
+    for j, (e, f, n) in enumerate(jobs):
+        b, x = _tile_bucket(n), j % 8
+        if b in want_bucket or x in want_xcd:
+            if e not in experts:
+                experts.append(e)
+            want_bucket.discard(b)
+            want_xcd.discard(x)
+        if not want_bucket and not want_xcd:
+            break
+    last_e = jobs[-1][0]
+    if last_e not in experts:
+        experts.append(last_e)
+    hot = int(np.argmax(counts))
+    if hot not in experts:
+        experts.append(hot)
+    # tokens at chosen slots of chosen jobs, read from the GPU's expert-sorted layout
+    s, ex, B = out["sorted_ids"], out["expert_ids"], out["B"]
+    n_post = int(out["num_post"][0])
+
+    def token_at(e, slot):
+        blocks = np.nonzero(ex[: n_post // B] == e)[0]
+        return int(s[blocks[0] * B + slot]) // k
+
+    if counts[hot] > SLOTS_PER_JOB:
+        tokens.add(token_at(hot, SLOTS_PER_JOB - 1))         # last valid row of a full job
+        tokens.add(token_at(hot, int(counts[hot]) - 1))      # a row of the last (later) job
+    for e in experts:
+        n = int(counts[e])
+        tokens.add(token_at(e, n - 1))                       # last valid row (a partial tile if n % 16)
+    rng = np.random.default_rng(seed)
+    T = out["topk_ids"].shape[0]
+    tokens |= set(rng.choice(T, size=n_random, replace=False).tolist()) | {0, T - 1}
+    return experts, sorted(tokens)
+
+
+def _full_case(name, sample=None, n_random=12, o_experts=None, seed=0):
+    """One K3 layer at full size: routing and align for every token, numeric outputs on the
+    sampled tokens, and every slot of selected experts (tap O) on either expert path."""
     H = _harness()
     c = gen.named_config(name)
     dl = H.k3_layer()
@@ -256,39 +321,56 @@ def _full_case(name, sample):
         dl.router = torch.from_numpy(dense["router"]).cuda()
     x = gen.make_x(c)
     try:
-        out = dl.run(x)
+        out = dl.run(x, with_O=True)
     finally:
         if c.router_dist != "normal":
             dl.router = torch.from_numpy(dl.host_dense["router"]).cuda()
+    if o_experts is None:
+        experts, tokens = _pick_mfma_cases(out, c.topk, n_random, seed)
+    else:
+        experts, tokens = o_experts(out), []
+    if sample is not None:
+        tokens = sorted(set(tokens) | set(sample))
+    print(f"  {name}: {len(tokens)} tokens, every slot of experts {experts}")
     ref = li.oracle_forward(c, {"x": x, **dense, "shared": gen.make_shared(c)}, experts=dl.oracle_experts(),
-                            align_block=out["B"], tokens=sample)
+                            align_block=out["B"], tokens=tokens)
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
+    H.expert_outputs_check(out, c, x, dense["down"], dl.oracle_experts(), experts, c.topk)
+
+
+def _busiest(n):
+    return lambda out: [int(e) for e in np.argsort(-out["counts"], kind="stable")[:n]]
 
 
 @pytest.mark.fullsize
 @pytest.mark.timeout(900)
 def test_full_decode16():
-    _full_case("decode16", sample=[0, 9, 15])
+    """Every one of the 16 tokens, and every slot of the 4 busiest experts."""
+    _full_case("decode16", sample=list(range(16)), o_experts=_busiest(4))
 
 
 @pytest.mark.fullsize
 @pytest.mark.timeout(900)
 def test_full_decode256():
-    _full_case("decode256", sample=[3, 255])
+    """24 tokens spread over the batch, and every slot of the 6 busiest experts."""
+    _full_case("decode256", sample=list(range(3, 256, 11)), o_experts=_busiest(6))
 
 
 @pytest.mark.fullsize
 @pytest.mark.timeout(900)
 def test_full_prefill8192():
-    _full_case("prefill8192", sample=[0, 4097, 8191])
+    """The MFMA path at 8192 tokens: every slot of experts chosen to cover each row-tile
+    bucket, all 8 XCD classes, the last job and the busiest expert; tokens at job
+    boundaries and partial tiles plus random ones."""
+    _full_case("prefill8192", n_random=14, seed=1)
 
 
 @pytest.mark.fullsize
 @pytest.mark.timeout(900)
 def test_full_stack_layer_zipf_hot_experts():
     """Layer 0 of the 8-layer stack workload: T=4096 with the Zipf(1.1) selection bias, where
-    the hottest expert takes ~1155 of the 65536 pairs (about 16x the mean) and is split over
-    several MFMA jobs. Same weights as the decode workloads (layer 0), plus the bias."""
+    the hottest expert takes ~731 of the 65536 pairs (about 10x the mean) and is split over
+    four MFMA jobs. Same weights as the decode workloads (layer 0), plus the bias."""
     H = _harness()
     c = gen.named_config("stack8x4096")
     dl = H.k3_layer()
@@ -297,15 +379,15 @@ def test_full_stack_layer_zipf_hot_experts():
     saved = dl.bias
     dl.bias = torch.from_numpy(dense["select_bias"]).cuda()
     try:
-        out = dl.run(x)
+        out = dl.run(x, with_O=True)
     finally:
         dl.bias = saved
     counts = out["counts"]
     hot = int(np.argmax(counts))
-    assert counts[hot] > 160  # more than one job
-    hot_token = int(np.nonzero((out["topk_ids"] == hot).any(axis=1))[0][-1])
-    sample = sorted({0, 2047, 4095, hot_token})
+    assert counts[hot] > 3 * SLOTS_PER_JOB  # four jobs
+    experts, tokens = _pick_mfma_cases(out, c.topk, n_random=8, seed=2)
+    print(f"  hottest expert {hot}: {int(counts[hot])} pairs; {len(tokens)} tokens; experts {experts}")
     ref = li.oracle_forward(c, {"x": x, **dense, "shared": gen.make_shared(c)}, experts=dl.oracle_experts(),
-                            align_block=out["B"], tokens=sample)
+                            align_block=out["B"], tokens=tokens)
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
-
+    H.expert_outputs_check(out, c, x, dense["down"], dl.oracle_experts(), experts, c.topk)
