@@ -380,7 +380,7 @@ class CacheFlush:
     def __call__(self, stream):
         import torch
         with torch.cuda.stream(stream):
-            torch.sum(self.buf, dtype=torch.int64, out=self.acc)
+            torch.sum(self.buf, dim=0, dtype=torch.int64, out=self.acc)
 
 
 def timed_steps(step, steps, stream, flush):

@@ -126,9 +126,8 @@ typedef struct moe_latent_taps {
   uint16_t* c_norm;       /* bf16 [T, L]  input of the up-projection */
   float* y_routed;        /* fp32 [T, H]  up-projection output */
   float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none) */
-  float* O;               /* fp32 [capacity, L] each routed expert's output for the slot at that
-                             position of sorted_ids, before the routing weight; rows of padding
-                             positions are unspecified */
+  float* O;               /* fp32 [T*k, L] the routed expert's output of slot t*k+j (token t's
+                             j-th selected expert), before the routing weight */
 } moe_latent_taps;
 
 int moe_latent_abi_version(void);

@@ -160,8 +160,8 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.num_post = take(4);
   p.inv_pos = take((size_t)p.pairs * 4);
   p.align_scratch = take(moe::align_scratch_bytes(p.T, p.E));
-  p.h = take(p.mfma ? 0 : (size_t)p.cap * p.I * 2);
-  p.O = take((size_t)p.cap * p.L * 4);
+  p.h = take(p.mfma ? 0 : (size_t)p.pairs * p.I * 2);  // stream: one row per (token, slot)
+  p.O = take((size_t)p.pairs * p.L * 4);                 // one row per (token, slot)
   p.cn = take((size_t)p.T * p.L * 2);
   p.hs = take(p.mfma ? 0 : (size_t)p.T * p.Is * 2);
   p.ys = take((size_t)p.T * p.H * 4);
@@ -236,7 +236,7 @@ bool check_alias(const moe_latent_dims* d, const Plan& p, const void* x, const v
     out.push_back({taps->c_norm, T * L * 2});
     out.push_back({taps->y_routed, T * H * 4});
     out.push_back({taps->y_shared, T * H * 4});
-    out.push_back({taps->O, cap * L * 4});
+    out.push_back({taps->O, pairs * L * 4});
   }
   (void)d;
   for (size_t i = 0; i < out.size(); ++i) {
@@ -293,10 +293,15 @@ int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacit
   return MOE_OK;
 }
 
-int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
-                          const moe_router* router, const uint8_t* experts_packed,
-                          const uint8_t* experts_scales, const void* up, const moe_shared* shared, int topk,
-                          void* y, void* workspace, size_t ws_bytes, void* stream, const moe_latent_taps* taps) {
+}  // extern "C"
+
+namespace {
+
+// The forward of every entry point; with record_stages false it records no stage events.
+int forward_impl(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                 const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,
+                 const void* up, const moe_shared* shared, int topk, void* y, void* workspace, size_t ws_bytes,
+                 void* stream, const moe_latent_taps* taps, bool record_stages) {
   int rc = check_dims(d, topk);
   if (rc) return rc;
   if (taps && taps->struct_size != sizeof(moe_latent_taps)) return MOE_EABI;
@@ -333,7 +338,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
   // moe_latent_timing_read skips.
   hipEvent_t* ev = nullptr;
   int ev_idx = -1;
-  {
+  if (record_stages) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     if (g_timing.on) ev = g_timing.claim(&ev_idx);
   }
@@ -544,7 +549,8 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     g.A = z_in;
     g.lda = p.L;
     g.routed = 1;
-    g.a_by_pos = 0;
+    g.a_row = moe::kRowToken;
+    g.out_row = moe::kRowFlat;
     g.sorted_ids = sorted;
     g.expert_ids = expert_ids;
     g.tiles_per_block = p.B / 16;
@@ -589,7 +595,8 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     g.A = h;
     g.lda = p.I;
     g.routed = 1;
-    g.a_by_pos = 1;
+    g.a_row = moe::kRowFlat;
+    g.out_row = moe::kRowFlat;
     g.sorted_ids = sorted;
     g.expert_ids = expert_ids;
     g.tiles_per_block = p.B / 16;
@@ -611,7 +618,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
   STAGE_MARK(6);
   }
   // a7 + a8: weighted combine and RMSNorm
-  MOE_HIP(moe::launch_combine_norm(O, p.L, inv_pos, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
+  MOE_HIP(moe::launch_combine_norm(O, p.L, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
                                    taps ? taps->c : nullptr, cn, s));
   STAGE_MARK(7);
   // a9: up-projection, plus the shared output, rounded to bf16
@@ -654,7 +661,7 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
     if ((r = copy_tap(taps->num_post, num_post, 4, s))) return r;
     if ((r = copy_tap(taps->inv_pos, inv_pos, (size_t)p.pairs * 4, s))) return r;
     if ((r = copy_tap(taps->c_norm, cn, (size_t)p.T * p.L * 2, s))) return r;
-    if ((r = copy_tap(taps->O, O, (size_t)p.cap * p.L * 4, s))) return r;
+    if ((r = copy_tap(taps->O, O, (size_t)p.pairs * p.L * 4, s))) return r;
     if (taps->y_shared) {
       if (shared) {
         if ((r = copy_tap(taps->y_shared, ys, (size_t)p.T * p.H * 4, s))) return r;
@@ -667,12 +674,24 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
 #undef STAGE_MARK
 }
 
+}  // namespace
+
+extern "C" {
+
+int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                          const moe_router* router, const uint8_t* experts_packed,
+                          const uint8_t* experts_scales, const void* up, const moe_shared* shared, int topk,
+                          void* y, void* workspace, size_t ws_bytes, void* stream, const moe_latent_taps* taps) {
+  return forward_impl(d, x, down, norm, router, experts_packed, experts_scales, up, shared, topk, y, workspace,
+                      ws_bytes, stream, taps, true);
+}
+
 int moe_latent_forward(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
                        const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,
                        const void* up, const moe_shared* shared, int topk, void* y, void* workspace,
                        size_t ws_bytes, void* stream) {
-  return moe_latent_forward_ex(d, x, down, norm, router, experts_packed, experts_scales, up, shared, topk, y,
-                               workspace, ws_bytes, stream, nullptr);
+  return forward_impl(d, x, down, norm, router, experts_packed, experts_scales, up, shared, topk, y, workspace,
+                      ws_bytes, stream, nullptr, true);
 }
 
 int moe_route(const moe_latent_dims* d, const void* x, const moe_router* router, int topk, int32_t* topk_ids,

@@ -104,13 +104,18 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t*
                         int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, void* scratch, hipStream_t s);
 
 // ---------------------------------------------------------------- MXFP4 contractions
+// Row of slot position pos of the expert-sorted layout in a routed problem's tensors:
+// kRowToken = the slot's token sorted_ids[pos] / topk, kRowPos = pos itself, kRowFlat = the
+// flat slot index sorted_ids[pos] = t * topk + j (tensors with one row per (token, slot)).
+enum RowMode : int { kRowToken = 0, kRowPos = 1, kRowFlat = 2 };
 // One grouped contraction problem: out[row] = act(A_row . W1^T, A_row . W2^T) (GLU) or A_row . W^T.
 struct MxProblem {
   // activations: bf16 rows
   const uint16_t* A;
   int lda;
-  int routed;                 // 1: row of slot pos = sorted_ids[pos] / topk (gather); 0: row = pos
-  int a_by_pos;               // routed only: 1 = A row is pos itself (h rows in sorted order)
+  int routed;                 // 1: the rows are the slots of the expert-sorted layout; 0: dense rows
+  int a_row;                  // routed: A row of slot pos (kRowToken, kRowPos or kRowFlat)
+  int out_row;                // routed: output row of slot pos (kRowPos or kRowFlat)
   const int32_t* sorted_ids;  // routed
   const int32_t* expert_ids;  // routed: expert of each layout block of B slots
   int tiles_per_block;        // routed: B / 16 (the kernel's 16-slot tiles per layout block)
@@ -186,7 +191,7 @@ struct MfmaProblem {
   int N, K;                   // GLU: N = h width, multiple of 512; plain: N multiple of 256; K multiple of 512
   uint8_t* outq;              // GLU: h rows in A's format, data tiled (routed: slot position, dense: row), width N
   uint8_t* outqs;
-  float* outf;                // plain: fp32 [row, ldo] (routed: slot position)
+  float* outf;                // plain: fp32 [row, ldo] (routed: flat slot index t * topk + j)
   int ldo;
 };
 struct MfmaArgs {
@@ -197,8 +202,9 @@ constexpr int kMfmaSlotsPerJob = 192;  // 12 MFMA row tiles of 16
 hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- combine + norm
-hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
-                               const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
+// O fp32 [T * k, L] by flat slot index; c_t = sum_j w[t][j] * O[t * k + j] in slot order
+hipError_t launch_combine_norm(const float* O, int L, const float* w, int T, int k, const uint16_t* norm, float eps,
+                               float* c_tap, uint16_t* c_norm, hipStream_t s);
 
 // y = x / sqrt(mean(x^2) + eps) * g per row (g null: no weight); bf16 [rows, cols], cols % 4 == 0; y may be x
 hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t* g, float eps, uint16_t* y,

@@ -27,6 +27,11 @@
 // the matching 32 activations (lane group q supplies the same K sub-range in
 // both operands, so no reordering of K is visible in the result).
 //
+// Rows: a routed problem reads its A row of slot position pos as the slot's token,
+// the position itself or the flat slot index (RowMode), and writes its output row at
+// the position or the flat slot index; the layer keeps h and O one row per
+// (token, slot), so their size follows T * k, not the padded layout.
+//
 // GLU variant: the epilogue applies act(gate) * up in registers and writes
 // bf16 h (with MXFP8 activations: each row's 32 columns of a wave are one
 // block, rounded to their MXFP8 values first); the plain variant (w2, or the
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     int arow = -1;
     if (a.routed) {
       const int sid = a.sorted_ids[pos];
-      if (sid < a.pairs) arow = a.a_by_pos ? pos : sid / a.topk;
+      if (sid < a.pairs) arow = a.a_row == kRowPos ? pos : (a.a_row == kRowFlat ? sid : sid / a.topk);
     } else if (pos < a.M) {
       arow = pos;
     }
@@ -203,8 +208,9 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int pos = blk * 16 + 4 * q + r;
-    opos[r] = pos;
-    valid[r] = a.routed ? (a.sorted_ids[pos] < a.pairs) : (pos < a.M);
+    const int sid = a.routed ? a.sorted_ids[pos] : 0;
+    opos[r] = a.routed && a.out_row == kRowFlat ? sid : pos;
+    valid[r] = a.routed ? (sid < a.pairs) : (pos < a.M);
   }
   if (GLU) {
     // a wave's 32 columns of a row are one MXFP8 group: lanes 16q..16q+15 (tiles 0 and 1) of row 4q + r

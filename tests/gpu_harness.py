@@ -96,8 +96,8 @@ class DeviceLayer:
                 "y_routed": torch.empty((T, c.hidden), dtype=torch.float32, device=dv),
                 "y_shared": torch.empty((T, c.hidden), dtype=torch.float32, device=dv),
             }
-            if with_O:   # expert outputs by slot position: capacity x latent fp32
-                tp["O"] = torch.empty((cap, c.latent), dtype=torch.float32, device=dv)
+            if with_O:   # expert outputs by flat slot index t*k+j: T*k x latent fp32
+                tp["O"] = torch.empty((T * c.topk, c.latent), dtype=torch.float32, device=dv)
             out["B"] = blk
         L.moe_latent_forward_ex(dims, x, self.down, self.norm, self.router, self.bias, self.packed, self.scales,
                                 self.up, self.sh_packed, self.sh_scales, c.topk, y, ws, taps=tp)
@@ -199,8 +199,8 @@ def compare_layer(out: dict, ref: dict, T: int, k: int, E: int, tokens=None, w_t
 
 def expert_outputs_check(out: dict, c, x_bits: np.ndarray, down_bits: np.ndarray, experts_src, experts, k: int,
                          act: str = "bf16"):
-    """Every slot of each expert in `experts`: the GPU's expert output O (tap, by slot
-    position, before the routing weight) against the oracle's expert FFN applied to the
+    """Every slot of each expert in `experts`: the GPU's expert output O (tap, by flat slot
+    index t*k+j, before the routing weight) against the oracle's expert FFN applied to the
     oracle's latent of the slot's token, within MAX_REL / MIN_COS per expert. Slots are
     those of the GPU's align output (itself checked bit-exact against the oracle)."""
     from oracle.layer import expert_ffn
@@ -215,9 +215,10 @@ def expert_outputs_check(out: dict, c, x_bits: np.ndarray, down_bits: np.ndarray
         blocks = np.nonzero(ex[: n_post // B] == e)[0]
         pos = np.concatenate([np.arange(b * B, (b + 1) * B) for b in blocks])
         pos = pos[sorted_ids[pos] < pairs]
-        toks = sorted_ids[pos] // k
+        flat = sorted_ids[pos]
+        toks = flat // k
         z = bf16_to_f64(x_bits[toks]) @ Wd.T
         p, sc = experts_src(int(e))
         w1, w3, w2 = decode_glu_record(p, sc, c.latent, c.inter)
         ref = expert_ffn(z, w1, w3, w2, act)
-        assert_close(f"O[expert {int(e)}: {len(pos)} slots]", out["O"][pos], ref)
+        assert_close(f"O[expert {int(e)}: {len(pos)} slots]", out["O"][flat], ref)
