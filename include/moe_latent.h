@@ -180,6 +180,27 @@ int moe_latent_forward_ex(const moe_latent_dims* d, const void* x, const void* d
                           void* y, void* workspace, size_t ws_bytes, void* stream, const moe_latent_taps* taps);
 
 /*
+ * moe_latent_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The workspace is a static array of
+ * MOE_LATENT_STATIC_SCRATCH_BYTES in the library's code object, one copy per GPU, held
+ * until the process ends (its device address is looked up once per device). It holds
+ * the workspace of a K3-shape decode batch of up to 16 tokens (13.6 MiB at T = 16);
+ * layers whose moe_latent_workspace_size exceeds it return MOE_EWORKSPACE before
+ * anything is enqueued. Arguments, results and errors otherwise as moe_latent_forward
+ * (the current device must be the stream's); no stage events are recorded. Every call
+ * on one GPU uses that GPU's one array: calls whose execution overlaps on one GPU (on
+ * different streams, or from several host threads) race and give wrong results; calls
+ * in one stream's order are safe. Each call writes every part of the array it later
+ * reads, so nothing carries over from one call to the next.
+ */
+#define MOE_LATENT_STATIC_SCRATCH_BYTES (16u << 20)
+int moe_latent_forward_noalloc(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                               const moe_router* router, const uint8_t* experts_packed,
+                               const uint8_t* experts_scales, const void* up, const moe_shared* shared, int topk,
+                               void* y, void* stream);
+
+/*
  * Routing only: logits = x . W_r^T (fp32), then the selection of
  * moe_latent_forward. Writes topk_ids [T, topk] (ascending ids per token) and
  * topk_w [T, topk]; logits [T, E] fp32 is required scratch/output.

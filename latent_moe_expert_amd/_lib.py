@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_latent.so")
 
 MOE_OK = 0
 QB_BINS = 1000
+STATIC_SCRATCH_BYTES = 16 << 20   # MOE_LATENT_STATIC_SCRATCH_BYTES
 PATH_AUTO, PATH_STREAM, PATH_MFMA = 0, 1, 2
 ACT_BF16, ACT_MXFP8 = 0, 1
 ERRORS = {-1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EALIAS", -4: "MOE_EWORKSPACE", -5: "MOE_EHIP",
@@ -45,7 +46,7 @@ EXPORTS = ["moe_latent_abi_version", "moe_latent_strerror", "moe_latent_last_hip
            "moe_qb_histogram", "moe_qb_update", "moe_qb_target", "moe_qb_bias", "moe_hbm_read",
            "moe_latent_timing_enable",
            "moe_latent_stage_count", "moe_latent_stage_name", "moe_latent_timing_read", "moe_latent_shutdown",
-           "moe_rmsnorm"]
+           "moe_rmsnorm", "moe_latent_forward_noalloc"]
 
 _lib = None
 
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
         "moe_latent_timing_read": ([ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)], I),
         "moe_latent_shutdown": ([], I),
         "moe_rmsnorm": ([P, I, I, P, ctypes.c_float, P, P], I),
+        "moe_latent_forward_noalloc": ([D, P, P, P, ctypes.POINTER(MoeRouter), P, P, P, ctypes.POINTER(MoeShared), I,
+                                        P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

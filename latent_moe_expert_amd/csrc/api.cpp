@@ -297,7 +297,8 @@ int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacit
 
 namespace {
 
-// The forward of every entry point; with record_stages false it records no stage events.
+// The forward of every entry point; with record_stages false it records no stage events
+// (the entry point that allocates nothing must not create events either).
 int forward_impl(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
                  const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,
                  const void* up, const moe_shared* shared, int topk, void* y, void* workspace, size_t ws_bytes,
@@ -674,6 +675,31 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
 #undef STAGE_MARK
 }
 
+// ------------------------------------------------------------------ static scratch
+// Workspace of moe_latent_forward_noalloc: one array per GPU in the code object. In host code
+// `scratch` names a host-side stand-in; the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and only that
+// address is ever passed to kernels.
+__device__ __align__(256) uint8_t scratch[MOE_LATENT_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_addr;  // by device id; null until looked up
+
+int static_scratch(void** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_addr.size()) g_scratch_addr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_addr[(size_t)dev]) {
+    void* ptr = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return MOE_EHIP;
+    g_scratch_addr[(size_t)dev] = ptr;
+  }
+  *out = g_scratch_addr[(size_t)dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -692,6 +718,21 @@ int moe_latent_forward(const moe_latent_dims* d, const void* x, const void* down
                        size_t ws_bytes, void* stream) {
   return forward_impl(d, x, down, norm, router, experts_packed, experts_scales, up, shared, topk, y, workspace,
                       ws_bytes, stream, nullptr, true);
+}
+
+int moe_latent_forward_noalloc(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
+                               const moe_router* router, const uint8_t* experts_packed,
+                               const uint8_t* experts_scales, const void* up, const moe_shared* shared, int topk,
+                               void* y, void* stream) {
+  const int rc = check_dims(d, topk);
+  if (rc) return rc;
+  if (make_plan(d, topk).total > (size_t)MOE_LATENT_STATIC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  const int r = static_scratch(&ws);
+  if (r) return r;
+  return forward_impl(d, x, down, norm, router, experts_packed, experts_scales, up, shared, topk, y, ws,
+                      (size_t)MOE_LATENT_STATIC_SCRATCH_BYTES, stream, nullptr, false);
 }
 
 int moe_route(const moe_latent_dims* d, const void* x, const moe_router* router, int topk, int32_t* topk_ids,

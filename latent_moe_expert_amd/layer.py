@@ -110,6 +110,23 @@ def moe_latent_forward(dims: MoeLatentDims, x, down, norm, router_weight, select
     _check("moe_latent_forward", rc)
 
 
+def moe_latent_forward_noalloc(dims: MoeLatentDims, x, down, norm, router_weight, select_bias, experts_packed,
+                               experts_scales, up, shared_packed, shared_scales, topk: int, y, stream=None) -> None:
+    """moe_latent_forward with the library's static per-GPU scratch as its workspace."""
+    lib = _lib.load()
+    router = MoeRouter(_ptr(router_weight, torch.float32, "router"), _ptr(select_bias, torch.float32, "select_bias"))
+    shared = None
+    if shared_packed is not None:
+        shared = MoeShared(_ptr(shared_packed, torch.uint8, "shared_packed"),
+                           _ptr(shared_scales, torch.uint8, "shared_scales"))
+    rc = lib.moe_latent_forward_noalloc(
+        ctypes.byref(dims), _ptr(x, _BF16, "x"), _ptr(down, _BF16, "down"), _ptr(norm, _BF16, "norm"),
+        ctypes.byref(router), _ptr(experts_packed, torch.uint8, "experts_packed"),
+        _ptr(experts_scales, torch.uint8, "experts_scales"), _ptr(up, _BF16, "up"),
+        ctypes.byref(shared) if shared is not None else None, topk, _ptr(y, _BF16, "y"), _stream(stream))
+    _check("moe_latent_forward_noalloc", rc)
+
+
 def moe_route(dims: MoeLatentDims, x, router_weight, select_bias, topk: int, topk_ids, topk_w, logits,
               stream=None) -> None:
     lib = _lib.load()

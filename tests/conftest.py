@@ -15,6 +15,11 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are collected last within the gpu selection so that a failure in a
-    # late, heavy full-size case does not hide the small parity cases before it.
-    items.sort(key=lambda it: 1 if it.get_closest_marker("fullsize") else 0)
+    # Full-size GPU cases run after the small ones, so that a failure in a late, heavy
+    # case does not hide the small parity cases before it; the entry point that
+    # allocates nothing (test_zz_no_alloc.py) is checked after everything else.
+    def order(it):
+        if os.path.basename(str(it.fspath)) == "test_zz_no_alloc.py":
+            return 2
+        return 1 if it.get_closest_marker("fullsize") else 0
+    items.sort(key=order)

@@ -247,3 +247,20 @@ def test_auto_path_threshold_at_12_slots_per_expert(lib):
         mfma = _ws(lib, _dims(T=T, expert_path=2))[1]
         assert stream != mfma
         assert auto == (stream if T < 672 else mfma), T
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_launch(lib):
+    """moe_latent_forward_noalloc: a layer whose workspace exceeds the static scratch
+    (16 MiB: the K3 layer at T = 64 needs 54 MiB) returns MOE_EWORKSPACE; T = 0 enqueues
+    nothing; argument errors come first."""
+    router = _lib.MoeRouter(_ROUTER, None)
+    sh = _lib.MoeShared(_SHP, _SHS)
+    call = lambda d: lib.moe_latent_forward_noalloc(ctypes.byref(d), _X, _DOWN, None, ctypes.byref(router), _PACKED,
+                                                    _SCALES, _UP, ctypes.byref(sh), 16, _Y, None)
+    assert _ws(lib, _dims(T=64))[1] > _lib.STATIC_SCRATCH_BYTES >= _ws(lib, _dims(T=16))[1]
+    assert call(_dims(T=64)) == -4
+    assert call(_dims(T=0)) == 0
+    assert call(_dims(n_experts=5000)) == -2
+    bad = _dims()
+    bad.struct_size = 8
+    assert call(bad) == -6
