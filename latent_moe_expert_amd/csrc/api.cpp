@@ -161,7 +161,8 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.inv_pos = take((size_t)p.pairs * 4);
   p.align_scratch = take(moe::align_scratch_bytes(p.T, p.E));
   p.h = take(p.mfma ? 0 : (size_t)p.pairs * p.I * 2);  // stream: one row per (token, slot)
-  p.O = take((size_t)p.pairs * p.L * 4);                 // one row per (token, slot)
+  // stream: one row per (token, slot); MFMA: by layout position (a job's rows contiguous)
+  p.O = take((size_t)(p.mfma ? p.cap : p.pairs) * p.L * 4);
   p.cn = take((size_t)p.T * p.L * 2);
   p.hs = take(p.mfma ? 0 : (size_t)p.T * p.Is * 2);
   p.ys = take((size_t)p.T * p.H * 4);
@@ -619,8 +620,8 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
   STAGE_MARK(6);
   }
   // a7 + a8: weighted combine and RMSNorm
-  MOE_HIP(moe::launch_combine_norm(O, p.L, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
-                                   taps ? taps->c : nullptr, cn, s));
+  MOE_HIP(moe::launch_combine_norm(O, p.L, p.mfma ? inv_pos : nullptr, w, p.T, p.k, (const uint16_t*)norm,
+                                   d->rms_eps, taps ? taps->c : nullptr, cn, s));
   STAGE_MARK(7);
   // a9: up-projection, plus the shared output, rounded to bf16
   if (p.small) {
@@ -662,7 +663,12 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     if ((r = copy_tap(taps->num_post, num_post, 4, s))) return r;
     if ((r = copy_tap(taps->inv_pos, inv_pos, (size_t)p.pairs * 4, s))) return r;
     if ((r = copy_tap(taps->c_norm, cn, (size_t)p.T * p.L * 2, s))) return r;
-    if ((r = copy_tap(taps->O, O, (size_t)p.pairs * p.L * 4, s))) return r;
+    if (taps->O) {
+      if (p.mfma)
+        MOE_HIP(moe::launch_gather_rows_f32(O, p.L, inv_pos, p.pairs, taps->O, s));
+      else if ((r = copy_tap(taps->O, O, (size_t)p.pairs * p.L * 4, s)))
+        return r;
+    }
     if (taps->y_shared) {
       if (shared) {
         if ((r = copy_tap(taps->y_shared, ys, (size_t)p.T * p.H * 4, s))) return r;

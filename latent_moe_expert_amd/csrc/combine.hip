@@ -4,9 +4,10 @@
 // up-projection; K3 report review, "Stable LatentMoE": aggregate -> normalise ->
 // up-project).
 //
-// Gather form: token t reads its k expert outputs, rows t*k .. t*k+k-1 of O (one row
-// per (token, slot), written there by the down contraction), and sums w_tj * O in
-// slot order j = 0..k-1 in fp32 (no atomics, deterministic). The
+// Gather form: token t reads its k expert outputs -- rows t*k .. t*k+k-1 of O when O has
+// one row per (token, slot), or rows inv_pos[t*k+j] when O follows the expert-sorted
+// layout -- and sums w_tj * O in slot order j = 0..k-1 in fp32 (no atomics,
+// deterministic). The
 // norm is c / sqrt(mean(c^2) + eps) * g with a fixed-order block reduction.
 // Output: bf16 c' (the up-projection's activations) and optionally fp32 c.
 #include "common.h"
@@ -23,14 +24,20 @@ constexpr int kMaxSlots = 64;
 // use, then added in slot order (a fixed rounding order).
 template <int KV>
 __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restrict__ O, int L,
+                                                           const int32_t* __restrict__ inv_pos,
                                                            const float* __restrict__ w, int k,
                                                            const uint16_t* __restrict__ norm, float eps,
                                                            float* __restrict__ c_tap, uint16_t* __restrict__ c_norm) {
   constexpr int G = 32 / KV;
+  __shared__ int pos[kMaxSlots];
   __shared__ float wt[kMaxSlots];
   __shared__ float red[4];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) wt[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+  if (threadIdx.x < k) {
+    const size_t f = (size_t)t * k + threadIdx.x;
+    pos[threadIdx.x] = inv_pos ? inv_pos[f] : (int)f;
+    wt[threadIdx.x] = w[f];
+  }
   __syncthreads();
   const int nvec = L >> 2;
   f32x4_t acc[KV];
@@ -41,7 +48,7 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restri
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int j = j0 + g;
-      const int p = j < k ? t * k + j : -1;
+      const int p = j < k ? pos[j] : -1;
       const f32x4_t* row = (const f32x4_t*)(O + (size_t)(p < 0 ? 0 : p) * L);
 #pragma unroll
       for (int i = 0; i < KV; ++i) {
@@ -120,6 +127,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   }
 }
 
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ src, int cols,
+                                                          const int32_t* __restrict__ idx, float* __restrict__ out) {
+  const size_t from = (size_t)idx[blockIdx.x] * cols, to = (size_t)blockIdx.x * cols;
+  for (int v = threadIdx.x; v < cols / 4; v += 256) *(f32x4_t*)(out + to + 4 * v) = *(const f32x4_t*)(src + from + 4 * v);
+}
+
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -133,6 +146,12 @@ hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t*
   return hipGetLastError();
 }
 
+hipError_t launch_gather_rows_f32(const float* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, s, src, cols, idx, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const size_t blocks = (n + 255) / 256;
@@ -140,19 +159,19 @@ hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine_norm(const float* O, int L, const float* w, int T, int k, const uint16_t* norm, float eps,
-                               float* c_tap, uint16_t* c_norm, hipStream_t s) {
+hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
+                               const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int nvec = L / 4;
   const int kv = (nvec + 255) / 256;
   if (kv <= 1)
-    hipLaunchKernelGGL(combine_norm_kernel<1>, dim3(T), dim3(256), 0, s, O, L, w, k, norm, eps, c_tap, c_norm);
+    hipLaunchKernelGGL(combine_norm_kernel<1>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
   else if (kv <= 2)
-    hipLaunchKernelGGL(combine_norm_kernel<2>, dim3(T), dim3(256), 0, s, O, L, w, k, norm, eps, c_tap, c_norm);
+    hipLaunchKernelGGL(combine_norm_kernel<2>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
   else if (kv <= 4)
-    hipLaunchKernelGGL(combine_norm_kernel<4>, dim3(T), dim3(256), 0, s, O, L, w, k, norm, eps, c_tap, c_norm);
+    hipLaunchKernelGGL(combine_norm_kernel<4>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
   else
-    hipLaunchKernelGGL(combine_norm_kernel<8>, dim3(T), dim3(256), 0, s, O, L, w, k, norm, eps, c_tap, c_norm);
+    hipLaunchKernelGGL(combine_norm_kernel<8>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
   return hipGetLastError();
 }
 

@@ -191,7 +191,9 @@ struct MfmaProblem {
   int N, K;                   // GLU: N = h width, multiple of 512; plain: N multiple of 256; K multiple of 512
   uint8_t* outq;              // GLU: h rows in A's format, data tiled (routed: slot position, dense: row), width N
   uint8_t* outqs;
-  float* outf;                // plain: fp32 [row, ldo] (routed: flat slot index t * topk + j)
+  float* outf;                // plain: fp32 [row, ldo] (routed: slot position, or with out_flat the
+                              // flat slot index t * topk + j)
+  int out_flat;
   int ldo;
 };
 struct MfmaArgs {
@@ -202,9 +204,10 @@ constexpr int kMfmaSlotsPerJob = 192;  // 12 MFMA row tiles of 16
 hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- combine + norm
-// O fp32 [T * k, L] by flat slot index; c_t = sum_j w[t][j] * O[t * k + j] in slot order
-hipError_t launch_combine_norm(const float* O, int L, const float* w, int T, int k, const uint16_t* norm, float eps,
-                               float* c_tap, uint16_t* c_norm, hipStream_t s);
+// c_t = sum_j w[t][j] * O[row of slot t * k + j] in slot order: O fp32 by flat slot index
+// (inv_pos null) or by layout position (row = inv_pos[t * k + j])
+hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
+                               const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
 
 // y = x / sqrt(mean(x^2) + eps) * g per row (g null: no weight); bf16 [rows, cols], cols % 4 == 0; y may be x
 hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t* g, float eps, uint16_t* y,
@@ -223,6 +226,9 @@ hipError_t launch_qb_bias(const int32_t* hist, int n, long long q, float* new_bi
 // ---------------------------------------------------------------- streaming read (measurement)
 // *checksum = XOR of all dwords of buf (bytes % 16 == 0, buf 16-byte aligned), every chunk read once.
 hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, hipStream_t s);
+
+// out[i] = src[idx[i]] for rows of `cols` floats (cols % 4 == 0), i < n
+hipError_t launch_gather_rows_f32(const float* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s);
 
 // fill with a constant (a kernel, so that captured graphs hold no memset node)
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);

@@ -56,8 +56,9 @@
 // compile-time index, so the compiler can tell that a stage being read is not
 // the target of the loads in flight.
 //
-// Epilogue. Plain: fp32 rows, routed ones at the flat slot index t * topk + j of each
-// slot (one row per (token, slot), read by the combine in slot order). GLU: h = act(gate)*up
+// Epilogue. Plain: fp32 rows, routed ones at the slot's position (a job's rows are then
+// one contiguous block; writing them at the flat slot index instead, scattered, measured
+// 2.78 ms against 2.51 ms for the down launch at an 8192-token prefill). GLU: h = act(gate)*up
 // goes through LDS and is written directly in the encoding (FP6 hi/lo or MXFP8)
 // that the down contraction reads.
 #include <type_traits>
@@ -472,7 +473,7 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * mf + 4 * q + r;
         if (j < nvalid) {
-          const int orow = a.routed ? a.sorted_ids[first + j] : first + j;  // routed: flat slot index
+          const int orow = a.routed && a.out_flat ? a.sorted_ids[first + j] : first + j;
           float* o = a.outf + (size_t)orow * a.ldo + col0 + nl;
 #pragma unroll
           for (int nf = 0; nf < 2; ++nf) o[16 * nf] = acc[mf][nf][r];

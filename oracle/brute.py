@@ -55,16 +55,27 @@ def glu_record(packed, scales, inp, inter):
     return gate, up, down
 
 
-def glu_ffn(rec, v):
+def situ(g, u, beta, linear_beta):
+    """SiTU by the same reading as oracle.layer.situ (the sigmoid branch and the linear
+    branch each limited by beta * tanh(z / beta)), written with math.tanh."""
+    return beta * math.tanh(silu(g) / beta) * linear_beta * math.tanh(u / linear_beta)
+
+
+def glu_ffn(rec, v, situ_betas=None):
     gate, up, down = rec
     g = matvec(gate, v)
     u = matvec(up, v)
-    return matvec(down, [silu(a) * b for a, b in zip(g, u)])
+    if situ_betas is None:
+        h = [silu(a) * b for a, b in zip(g, u)]
+    else:
+        h = [situ(a, b, *situ_betas) for a, b in zip(g, u)]
+    return matvec(down, h)
 
 
 def forward(x_bits, down_bits, norm_bits, router_w, select_bias, exp_packed, exp_scales,
-            up_bits, shared, k, inter, shared_inter, rms_eps, rsf):
-    """Returns dict(ids, weights, y64) with nested Python lists."""
+            up_bits, shared, k, inter, shared_inter, rms_eps, rsf, situ_betas=None):
+    """Returns dict(ids, weights, y64) with nested Python lists. situ_betas = (beta,
+    linear_beta) selects SiTU as the GLU activation of every expert, else SiLU(g) * u."""
     T = len(x_bits)
     H = len(x_bits[0])
     L = len(down_bits)
@@ -86,7 +97,7 @@ def forward(x_bits, down_bits, norm_bits, router_w, select_bias, exp_packed, exp
         z = matvec(Wd, x)
         c = [0.0] * L
         for wj, e in zip(w, chosen):
-            o = glu_ffn(recs[e], z)
+            o = glu_ffn(recs[e], z, situ_betas)
             for i in range(L):
                 c[i] += wj * o[i]
         if g is not None:
@@ -95,7 +106,7 @@ def forward(x_bits, down_bits, norm_bits, router_w, select_bias, exp_packed, exp
             c = [c[i] * inv * g[i] for i in range(L)]
         y = matvec(Wu, c)
         if shrec is not None:
-            ysh = glu_ffn(shrec, x)
+            ysh = glu_ffn(shrec, x, situ_betas)
             y = [a + b for a, b in zip(y, ysh)]
         all_ids.append(chosen)
         all_w.append(w)

@@ -24,7 +24,10 @@ Dataflow, from the pages:
 Readings taken where the pages are silent (each also listed in the design doc):
   R1  the RMSNorm acts on the aggregated latent, after the combine.
   R2  RMSNorm(c) = c / sqrt(mean(c^2) + eps) * g (eps inside the root).
-  R4  the GLU activation is SiLU(gate) * up; SiTU's formula is not printed.
+  R4  the GLU activation is SiLU(gate) * up by default; SiTU's formula is not printed.
+  R17 SiTU, selectable (activation="situ"): beta * tanh(SiLU(gate) / beta) *
+      linear_beta * tanh(up / linear_beta), beta 4, linear_beta 25 -- a reading built from
+      the properties the pages state; parity unpinned against K3's own SituAndMul.
   R5  w1 is the gate, w3 the up projection, w2 the down projection.
   R8  ties in the selection key go to the lower expert id; the selected ids
       are stored in ascending id order (a function of the selected set only).
@@ -65,6 +68,38 @@ def silu(g):
 def glu(gate, up):
     """GLU activation of the experts: SiLU(gate) * up (reading R4)."""
     return silu(gate) * up
+
+
+# SiTU parameters of the K3 configuration (WASTE "Kimi K3, as released", "What is new since
+# Kimi-Linear", item 3: activation_situ_beta and activation_situ_linear_beta)
+SITU_BETA = 4.0
+SITU_LINEAR_BETA = 25.0
+
+
+def situ(gate, up, beta: float = SITU_BETA, linear_beta: float = SITU_LINEAR_BETA):
+    """SiTU ("Sigmoid Tanh Unit") GLU activation -- reading R17, PARITY UNPINNED against K3's
+    own SituAndMul, whose formula the pages do not print.
+
+    What the pages fix: SiTU replaces SiLU in the GLU of both FFN paths (WASTE page, "Port
+    status"); the sigmoid branch and the tanh branch of the GLU are each soft-limited, by
+    beta_1 = 4 and beta_2 = 25, so that one output coordinate stays below beta_1 * beta_2 =
+    100 in magnitude, and the limit has the form beta * tanh(z / beta) = z + O(z^3 / beta^2),
+    so that SiTU is close to SwiGLU near the origin (K3 report review, "SiTU-GLU").
+    Reading: the sigmoid branch is SiLU(gate) and the linear branch is up, each passed
+    through that limit with its own beta:
+        SiTU(gate, up) = beta * tanh(SiLU(gate) / beta) * linear_beta * tanh(up / linear_beta).
+    (An alternative that also meets every stated fact, SiLU(beta * tanh(gate / beta)) for
+    the first factor, is not used.)"""
+    return beta * np.tanh(silu(gate) / beta) * (linear_beta * np.tanh(up / linear_beta))
+
+
+def glu_activation(name: str, beta: float = SITU_BETA, linear_beta: float = SITU_LINEAR_BETA):
+    """The experts' GLU activation by name: "silu" (default) or "situ"."""
+    if name == "silu":
+        return glu
+    if name == "situ":
+        return lambda g, u: situ(g, u, beta, linear_beta)
+    raise ValueError("activation must be 'silu' or 'situ'")
 
 
 def rmsnorm(c, g, eps: float):
@@ -169,12 +204,14 @@ def _expert_source(experts) -> Callable[[int], tuple]:
     return lambda e: (packed[e], scales[e])
 
 
-def expert_ffn(z_rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray, act: str = "bf16") -> np.ndarray:
-    """One routed expert on latent rows: (SiLU(z W1^T) * (z W3^T)) W2^T.
+def expert_ffn(z_rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray, act: str = "bf16",
+               glu_fn=glu) -> np.ndarray:
+    """One routed expert on latent rows: (act(z W1^T, z W3^T)) W2^T with the GLU activation
+    glu_fn (default SiLU(gate) * up).
 
     act="mxfp8": the expert's inputs are MXFP8 (mxfp8.py): z_rows are expected already
     quantized, and the GLU output is quantized before w2."""
-    h = glu(z_rows @ w1.T, z_rows @ w3.T)
+    h = glu_fn(z_rows @ w1.T, z_rows @ w3.T)
     if act == "mxfp8":
         h = mxfp8.quantize(h)
     return h @ w2.T
@@ -184,7 +221,9 @@ def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.nd
             router_w: np.ndarray, select_bias: Optional[np.ndarray], experts,
             up_bits: np.ndarray, shared: Optional[tuple], k: int, *,
             inter: int, shared_inter: int = 0, rms_eps: float = 1e-6, rsf: float = 1.0,
-            align_block: int = 16, tokens: Optional[Sequence[int]] = None, act: str = "bf16") -> dict:
+            align_block: int = 16, tokens: Optional[Sequence[int]] = None, act: str = "bf16",
+            activation: str = "silu", situ_beta: float = SITU_BETA,
+            situ_linear_beta: float = SITU_LINEAR_BETA) -> dict:
     """Evaluate the layer.
 
     x_bits bf16 [T, H]; down_bits bf16 [L, H]; norm_bits bf16 [L] or None;
@@ -200,7 +239,11 @@ def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.nd
     act="bf16" (default): the routed experts read the latent and the GLU output as
     they are. act="mxfp8": they read MXFP8 activations (mxfp8.py), the latent
     rounded to bf16 and then quantized, the GLU output quantized before w2; the
-    shared experts, projections and router are unchanged."""
+    shared experts, projections and router are unchanged.
+
+    activation="situ": the GLU activation of the routed and the shared experts is SiTU
+    (situ, reading R17) with the given betas instead of SiLU(gate) * up."""
+    glu_fn = glu_activation(activation, situ_beta, situ_linear_beta)
     if act not in ("bf16", "mxfp8"):
         raise ValueError("act must be 'bf16' or 'mxfp8'")
     X = bf16_to_f64(x_bits)
@@ -226,7 +269,7 @@ def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.nd
         rows, slots = np.nonzero(ids_s == e)
         p, s = get(int(e))
         w1, w3, w2 = decode_glu_record(p, s, L, inter)
-        O[rows, slots] = expert_ffn(z_in[rows], w1, w3, w2, act)
+        O[rows, slots] = expert_ffn(z_in[rows], w1, w3, w2, act, glu_fn)
 
     w_s = r["weights"][toks]
     c = np.einsum("tj,tjl->tl", w_s, O)                    # weighted combine over slots
@@ -235,7 +278,7 @@ def forward(x_bits: np.ndarray, down_bits: np.ndarray, norm_bits: Optional[np.nd
 
     if shared is not None:
         gs, us, ds = decode_glu_record(shared[0], shared[1], H, shared_inter)
-        y_s = glu(Xs @ gs.T, Xs @ us.T) @ ds.T
+        y_s = glu_fn(Xs @ gs.T, Xs @ us.T) @ ds.T
     else:
         y_s = np.zeros_like(y_r)
 

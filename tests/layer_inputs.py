@@ -32,13 +32,15 @@ def build(c, layer=0, experts=True):
     return d
 
 
-def oracle_forward(c, d, tokens=None, align_block=16, experts=None, act="bf16"):
+def oracle_forward(c, d, tokens=None, align_block=16, experts=None, act="bf16", activation="silu",
+                   situ_betas=(4.0, 25.0)):
     from oracle import layer
     ex = (d["exp_packed"], d["exp_scales"]) if experts is None else experts
     return layer.forward(d["x"], d["down"], d["norm"], d["router"], d["select_bias"], ex,
                          d["up"], d["shared"], c.topk, inter=c.inter, shared_inter=c.shared_inter,
                          rms_eps=c.rms_eps, rsf=c.routed_scaling_factor, align_block=align_block,
-                         tokens=tokens, act=act)
+                         tokens=tokens, act=act, activation=activation, situ_beta=situ_betas[0],
+                         situ_linear_beta=situ_betas[1])
 
 
 def encode_mxfp4(values, scale_codes):
