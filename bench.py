@@ -13,7 +13,7 @@ The default run also times the same layer at an 8192-token prefill (two
 rotating batches) and reports it under "prefill", with the MXFP4 MFMA roofline
 of its gate/up launch (algorithmic flops over the FP4/FP6 dense MFMA peak),
 and at a 256-token decode batch with a uniform router ("decode256"), plus the
-MXFP8 mode, Quantile Balancing and the measured HBM read ceiling.
+MXFP8 mode, the SiTU activation, Quantile Balancing and the measured HBM read ceiling.
 
 Timing: after W warm-up steps, K steps are timed back to back (wall clock between device
 synchronisations), then K steps each bracketed by HIP events on the launch stream with a
@@ -271,6 +271,8 @@ def main():
                     help="skip the secondary 8192-token prefill measurement of the default run")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the secondary measurements with MXFP8 routed-expert activations")
+    ap.add_argument("--no-situ", action="store_true",
+                    help="skip the secondary measurements with the SiTU activation")
     ap.add_argument("--no-decode256", action="store_true",
                     help="skip the secondary 256-token decode measurement of the default run")
     ap.add_argument("--no-qb", action="store_true",
@@ -331,6 +333,10 @@ def main():
         # the same decode with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
         record["decode_mxfp8"] = measure(c, dl, xs, args.steps, args.warmup, L, summary=True, act_format=1,
                                          flush=flush)
+    if c.name == "decode16" and not args.no_situ:
+        # the same decode with the SiTU activation (MOE_GLU_SITU)
+        record["decode_situ"] = measure(c, dl, xs, args.steps, args.warmup, L, summary=True, flush=flush,
+                                        glu_act=1)
     if not args.no_decode256 and c.name == "decode16":
         # the large decode batch: T=256 with the uniform router (nearly every expert touched),
         # same resident experts and projections, its own router weight
@@ -356,6 +362,9 @@ def main():
         if cpu:
             record["prefill"]["cpu_baseline"] = cpu_baseline(cp, dl.host_dense, xp_bits[:cp.T], args.cpu_tokens,
                                                              shared_host)
+        if not args.no_situ:
+            record["prefill_situ"] = measure(cp, dl, xp, max(5, args.steps // 2), 2, L, rotate=2, summary=True,
+                                             flush=flush, glu_act=1)
         # the same prefill with MXFP8 routed-expert activations (MOE_ACT_MXFP8)
         if not args.no_mxfp8:
             record["prefill_mxfp8"] = measure(cp, dl, xp, max(5, args.steps // 2), 2, L, rotate=2,
@@ -515,7 +524,7 @@ def uses_mfma_path(c) -> bool:
     return sizes and c.T * c.topk >= 12 * c.n_experts
 
 
-def measure(c, dl, xs, steps, warmup, L, rotate=4, summary=False, act_format=0, flush=None):
+def measure(c, dl, xs, steps, warmup, L, rotate=4, summary=False, act_format=0, flush=None, glu_act=0):
     """Time `steps` forwards of config c over `rotate` resident token batches; returns the
     JSON record (or, with summary, the fields of a secondary measurement). act_format 1:
     MXFP8 activations of the routed experts. The step time is the median of per-step event
@@ -523,7 +532,7 @@ def measure(c, dl, xs, steps, warmup, L, rotate=4, summary=False, act_format=0, 
     wall time of the same number of steps is reported beside it."""
     import torch
     from workload import gen
-    dims = dl.dims(c.T, act_format=act_format)
+    dims = dl.dims(c.T, act_format=act_format, glu_act=glu_act)
     ws = torch.empty(L.moe_latent_workspace_size(dims, c.topk), dtype=torch.uint8, device="cuda")
     y = torch.empty((c.T, c.hidden), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
@@ -585,9 +594,10 @@ def measure(c, dl, xs, steps, warmup, L, rotate=4, summary=False, act_format=0, 
                 "their E8M0 scales per 32 values, about 8 significant bits)")
     else:
         acts = "activations bf16"
+    glu = "SiTU (beta 4, linear beta 25)" if glu_act else "SiLU(gate)*up"
     workload = (f"{c.name}: one K3 latent-MoE layer, T={c.T} tokens, hidden {c.hidden}, latent {c.latent}, "
                 f"{c.n_experts} MXFP4 experts top-{c.topk}, intermediate {c.inter}, RMSNorm={c.norm}, shared GLU "
-                f"{c.shared_inter}; weights MXFP4 (E2M1 + E8M0/32), {acts}, fp32 accumulation")
+                f"{c.shared_inter}, GLU activation {glu}; weights MXFP4 (E2M1 + E8M0/32), {acts}, fp32 accumulation")
     timing = {"ms_per_step_median_flushed": round(med, 4), "ms_per_step_mean_flushed": round(float(np.mean(step_ms)), 4),
               "ms_per_step_back_to_back": round(wall * 1e3 / steps, 4), "flush": flush is not None}
     rec_b = gen.expert_record_bytes(c) + gen.expert_scale_bytes(c)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 5
+#define MOE_LATENT_ABI_VERSION 6
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, negative or inconsistent size */
@@ -77,6 +77,19 @@ extern "C" {
 #define MOE_ACT_BF16 0
 #define MOE_ACT_MXFP8 1
 
+/* GLU activation of the routed and the shared experts (moe_latent_dims.glu_act).
+ *   MOE_GLU_SILU: SiLU(gate) * up.
+ *   MOE_GLU_SITU: SiTU, the activation K3 uses instead of SiLU in both FFN paths (WASTE
+ *     "Kimi K3, as released", "What is new since Kimi-Linear" item 3: beta 4.0, linear
+ *     beta 25.0). The pages do not print its formula; this library takes the reading
+ *       SiTU(gate, up) = b * tanh(SiLU(gate) / b) * lb * tanh(up / lb)
+ *     with b = situ_beta, lb = situ_linear_beta: the sigmoid branch and the linear branch
+ *     each soft-limited by beta * tanh(z / beta), so |output| < b * lb (100 for K3) and the
+ *     unit is SwiGLU up to O(z^3 / beta^2) near the origin (K3 report review, "SiTU-GLU").
+ *     Agreement with K3's own implementation is not established. */
+#define MOE_GLU_SILU 0
+#define MOE_GLU_SITU 1
+
 /* Layer sizes. Limits checked by every call (else MOE_EUNSUPPORTED):
  * hidden, latent, inter, shared_inter multiples of 256 (512 for MOE_PATH_MFMA);
  * 1 <= n_experts <= 4096; latent <= 8192; align_block 0 (library choice, 16) or
@@ -95,6 +108,9 @@ typedef struct moe_latent_dims {
   float routed_scaling_factor; /* 1.0 for K3 */
   int32_t expert_path;         /* MOE_PATH_* */
   int32_t act_format;          /* MOE_ACT_* */
+  int32_t glu_act;             /* MOE_GLU_* */
+  float situ_beta;             /* MOE_GLU_SITU: beta of the gate (sigmoid) branch, > 0 (4.0 for K3) */
+  float situ_linear_beta;      /* MOE_GLU_SITU: beta of the linear (up) branch, > 0 (25.0 for K3) */
 } moe_latent_dims;
 
 /* Router (WASTE page, "Shape" router row and "Against the technical report"). */
@@ -164,7 +180,7 @@ int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacit
  *
  * Routing: s = sigmoid(x . W_r^T), key = s + select_bias; the topk largest keys
  * win, ties to the lower expert id; weights w = s / sum(s_selected) * rsf. The
- * expert activation is SiLU(gate) * up. Near-ties of the key at the k-th place
+ * experts' GLU activation is d->glu_act (SiLU(gate) * up or SiTU). Near-ties of the key at the k-th place
  * can route differently from a float64 evaluation (fp32 here).
  */
 int moe_latent_forward(const moe_latent_dims* d, const void* x, const void* down, const void* norm,

@@ -12,6 +12,7 @@ QB_BINS = 1000
 STATIC_SCRATCH_BYTES = 16 << 20   # MOE_LATENT_STATIC_SCRATCH_BYTES
 PATH_AUTO, PATH_STREAM, PATH_MFMA = 0, 1, 2
 ACT_BF16, ACT_MXFP8 = 0, 1
+GLU_SILU, GLU_SITU = 0, 1
 ERRORS = {-1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EALIAS", -4: "MOE_EWORKSPACE", -5: "MOE_EHIP",
           -6: "MOE_EABI"}
 
@@ -21,7 +22,8 @@ class MoeLatentDims(ctypes.Structure):
                 ("latent", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("align_block", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("routed_scaling_factor", ctypes.c_float), ("expert_path", ctypes.c_int32),
-                ("act_format", ctypes.c_int32)]
+                ("act_format", ctypes.c_int32), ("glu_act", ctypes.c_int32), ("situ_beta", ctypes.c_float),
+                ("situ_linear_beta", ctypes.c_float)]
 
 
 class MoeRouter(ctypes.Structure):

@@ -102,6 +102,10 @@ int check_dims(const moe_latent_dims* d, int topk) {
   if (d->align_block % 16) return MOE_EUNSUPPORTED;
   if (d->expert_path < MOE_PATH_AUTO || d->expert_path > MOE_PATH_MFMA) return MOE_EINVAL;
   if (d->act_format != MOE_ACT_BF16 && d->act_format != MOE_ACT_MXFP8) return MOE_EINVAL;
+  if (d->glu_act != MOE_GLU_SILU && d->glu_act != MOE_GLU_SITU) return MOE_EINVAL;
+  if (d->glu_act == MOE_GLU_SITU &&
+      !(d->situ_beta > 0.f && d->situ_beta < 3.0e38f && d->situ_linear_beta > 0.f && d->situ_linear_beta < 3.0e38f))
+    return MOE_EINVAL;
   if (d->expert_path == MOE_PATH_MFMA && !mfma_sizes_ok(d)) return MOE_EUNSUPPORTED;
   if ((long long)d->T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
   // activation tensors the kernels index with 32-bit byte offsets stay below 2 GiB
@@ -409,6 +413,9 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
   STAGE_MARK(3);
   // a4 + a5 (and a10's gate/up): GLU contractions. The shared experts' blocks go
   // first in the same launch, so their long K rows overlap the routed work.
+  const bool situ = d->glu_act == MOE_GLU_SITU;
+  const GluAct act{situ ? kGluSitu : kGluSilu, d->situ_beta, d->situ_linear_beta, situ ? 1.0f / d->situ_beta : 0.f,
+                   situ ? 1.0f / d->situ_linear_beta : 0.f};
   const size_t gu_bytes = (size_t)p.I * p.L / 2, gu_scales = (size_t)p.I * p.L / 32;
   const size_t sgu = (size_t)p.Is * p.H / 2, sgs = (size_t)p.Is * p.H / 32;
   if (p.mfma) {
@@ -474,6 +481,7 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
       g.outq = hq;
       g.outqs = hqs;
       m.nprob = n;
+      for (int i = 0; i < n; ++i) m.p[i].act = act;
       MOE_HIP(moe::launch_mx_mfma(m, s));
     }
     STAGE_MARK(5);
@@ -572,6 +580,7 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     g.ldo = p.I;
     g.out_fp8 = p.fp8;
     m.nprob = n;
+    for (int i = 0; i < n; ++i) m.p[i].act = act;
     MOE_HIP(moe::launch_mx_small(m, s));
   }
   STAGE_MARK(5);

@@ -43,9 +43,38 @@ __device__ __forceinline__ float e8m0_as_f32_exponent(uint32_t code) { return __
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Swappable GLU activation of the experts: SiLU(gate) * up.
-__device__ __forceinline__ float glu_act(float gate, float up) {
-  return gate / (1.0f + __expf(-gate)) * up;
+// GLU activation of the experts, chosen per launch problem:
+//   kGluSilu: SiLU(gate) * up
+//   kGluSitu: SiTU, b1 * tanh(SiLU(gate) / b1) * b2 * tanh(up / b2) -- the sigmoid branch and
+//             the linear branch each soft-limited by beta * tanh(z / beta) (K3 report review,
+//             "SiTU-GLU"; betas 4 and 25 in the K3 configuration, WASTE "Kimi K3, as
+//             released", "What is new since Kimi-Linear" item 3); |output| < b1 * b2.
+enum GluKind : int { kGluSilu = 0, kGluSitu = 1 };
+struct GluAct {
+  int kind;
+  float b1, b2;     // kGluSitu: beta of the gate branch, beta of the linear (up) branch
+  float ib1, ib2;   // 1 / b1, 1 / b2
+};
+
+// The epilogues evaluate the activation for every element of h with no matrix work to hide
+// it behind, so the divisions use the hardware reciprocal (about 1 ulp) instead of the
+// correctly rounded division sequence.
+__device__ __forceinline__ float rcp_dev(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float silu_dev(float g) { return g * rcp_dev(1.0f + __expf(-g)); }
+
+// tanh(x) = sign(x) * (1 - 2 / (exp(2|x|) + 1)): one hardware exponential and a reciprocal;
+// saturates to +-1 without overflow (exp -> inf gives 1/inf = 0). Absolute error a few fp32
+// ulps of 1 (the subtraction from 1), relative error larger only where |tanh x| < 1e-3,
+// whose contribution to a GLU output is below 1e-7 * beta in absolute terms.
+__device__ __forceinline__ float tanh_dev(float x) {
+  const float t = 1.0f - 2.0f * rcp_dev(__expf(2.0f * fabsf(x)) + 1.0f);
+  return copysignf(t, x);
+}
+
+__device__ __forceinline__ float glu_act(float gate, float up, GluAct a) {
+  if (a.kind == kGluSitu) return a.b1 * tanh_dev(silu_dev(gate) * a.ib1) * (a.b2 * tanh_dev(up * a.ib2));
+  return silu_dev(gate) * up;
 }
 
 __device__ __forceinline__ float sigmoidf_dev(float x) { return 1.0f / (1.0f + __expf(-x)); }

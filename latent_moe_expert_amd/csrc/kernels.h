@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace moe {
 
 // ---------------------------------------------------------------- dense projections
@@ -134,6 +136,7 @@ struct MxProblem {
   void* out;
   int ldo;
   int out_fp8;                // GLU: h rounded to its MXFP8 value per 32 columns before the bf16 store
+  GluAct act;                 // GLU: the activation
 };
 
 // Up to two problems of the same kind (both GLU or both plain) in one launch;
@@ -194,6 +197,7 @@ struct MfmaProblem {
   float* outf;                // plain: fp32 [row, ldo] (routed: slot position, or with out_flat the
                               // flat slot index t * topk + j)
   int out_flat;
+  GluAct act;                 // GLU: the activation
   int ldo;
 };
 struct MfmaArgs {

@@ -492,7 +492,8 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
 #pragma unroll
     for (int mf = 0; mf < NT; ++mf)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hrow(16 * mf + 4 * q + r)[wave * 16 + nl] = glu_act(acc[mf][0][r], acc[mf][1][r]);
+      for (int r = 0; r < 4; ++r)
+        hrow(16 * mf + 4 * q + r)[wave * 16 + nl] = glu_act(acc[mf][0][r], acc[mf][1][r], a.act);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < (NT * 64 + kThreads - 1) / kThreads; ++i) {

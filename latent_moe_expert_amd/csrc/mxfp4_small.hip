@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hv[t][r] = glu_act(acc[t][r], acc[t + 2][r]);
+      for (int r = 0; r < 4; ++r) hv[t][r] = glu_act(acc[t][r], acc[t + 2][r], a.act);
     if (a.out_fp8) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

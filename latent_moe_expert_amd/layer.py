@@ -31,9 +31,11 @@ def _check(fn: str, rc: int) -> None:
 
 def make_dims(T: int, hidden: int, latent: int, n_experts: int, inter: int, shared_inter: int = 0,
               align_block: int = 0, rms_eps: float = 1e-6, routed_scaling_factor: float = 1.0,
-              expert_path: int = 0, act_format: int = 0) -> MoeLatentDims:
+              expert_path: int = 0, act_format: int = 0, glu_act: int = 0, situ_beta: float = 4.0,
+              situ_linear_beta: float = 25.0) -> MoeLatentDims:
     return MoeLatentDims(ctypes.sizeof(MoeLatentDims), T, hidden, latent, n_experts, inter, shared_inter,
-                         align_block, rms_eps, routed_scaling_factor, expert_path, act_format)
+                         align_block, rms_eps, routed_scaling_factor, expert_path, act_format, glu_act, situ_beta,
+                         situ_linear_beta)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "") -> Optional[int]:

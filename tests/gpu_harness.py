@@ -63,17 +63,19 @@ class DeviceLayer:
             self.sh_packed = torch.from_numpy(sh[0]).to(dev)
             self.sh_scales = torch.from_numpy(sh[1]).to(dev)
 
-    def dims(self, T: int, align_block: int = 0, expert_path: int = 0, act_format: int = 0):
+    def dims(self, T: int, align_block: int = 0, expert_path: int = 0, act_format: int = 0, glu_act: int = 0,
+             situ_betas=(4.0, 25.0)):
         c = self.c
         return L.make_dims(T, c.hidden, c.latent, c.n_experts, c.inter, c.shared_inter, align_block, c.rms_eps,
-                           c.routed_scaling_factor, expert_path, act_format)
+                           c.routed_scaling_factor, expert_path, act_format, glu_act, *situ_betas)
 
     def run(self, x_bits: np.ndarray = None, x_dev: torch.Tensor = None, taps: bool = True, align_block: int = 0,
-            expert_path: int = 0, act_format: int = 0, with_O: bool = False, keep_y_dev: bool = False):
+            expert_path: int = 0, act_format: int = 0, with_O: bool = False, keep_y_dev: bool = False,
+            glu_act: int = 0, situ_betas=(4.0, 25.0)):
         c = self.c
         x = to_dev_bf16(x_bits) if x_dev is None else x_dev
         T = x.shape[0]
-        dims = self.dims(T, align_block, expert_path, act_format)
+        dims = self.dims(T, align_block, expert_path, act_format, glu_act, situ_betas)
         ws = torch.empty(max(L.moe_latent_workspace_size(dims, c.topk), 256), dtype=torch.uint8, device=x.device)
         y = torch.empty((T, c.hidden), dtype=torch.bfloat16, device=x.device)
         out = {}
@@ -198,13 +200,14 @@ def compare_layer(out: dict, ref: dict, T: int, k: int, E: int, tokens=None, w_t
 
 
 def expert_outputs_check(out: dict, c, x_bits: np.ndarray, down_bits: np.ndarray, experts_src, experts, k: int,
-                         act: str = "bf16"):
+                         act: str = "bf16", activation: str = "silu", situ_betas=(4.0, 25.0)):
     """Every slot of each expert in `experts`: the GPU's expert output O (tap, by flat slot
     index t*k+j, before the routing weight) against the oracle's expert FFN applied to the
     oracle's latent of the slot's token, within MAX_REL / MIN_COS per expert. Slots are
     those of the GPU's align output (itself checked bit-exact against the oracle)."""
-    from oracle.layer import expert_ffn
+    from oracle.layer import expert_ffn, glu_activation
     from oracle.mxfp4 import decode_glu_record
+    glu_fn = glu_activation(activation, *situ_betas)
     from oracle.numerics import bf16_to_f64
     sorted_ids, B = out["sorted_ids"], out["B"]
     ex = out["expert_ids"]
@@ -220,5 +223,5 @@ def expert_outputs_check(out: dict, c, x_bits: np.ndarray, down_bits: np.ndarray
         z = bf16_to_f64(x_bits[toks]) @ Wd.T
         p, sc = experts_src(int(e))
         w1, w3, w2 = decode_glu_record(p, sc, c.latent, c.inter)
-        ref = expert_ffn(z, w1, w3, w2, act)
+        ref = expert_ffn(z, w1, w3, w2, act, glu_fn)
         assert_close(f"O[expert {int(e)}: {len(pos)} slots]", out["O"][flat], ref)

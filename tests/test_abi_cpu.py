@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.moe_latent_abi_version() == 5
+    assert lib.moe_latent_abi_version() == 6
     for code in range(0, -7, -1):
         assert lib.moe_latent_strerror(code)
     assert lib.moe_latent_stage_count() == 8
@@ -43,7 +43,8 @@ def test_abi_version_and_strerror(lib):
 
 def _dims(**kw):
     base = dict(T=16, hidden=7168, latent=3584, n_experts=896, inter=3072, shared_inter=6144, align_block=0,
-                rms_eps=1e-6, routed_scaling_factor=1.0, expert_path=0, act_format=0)
+                rms_eps=1e-6, routed_scaling_factor=1.0, expert_path=0, act_format=0, glu_act=0, situ_beta=4.0,
+                situ_linear_beta=25.0)
     base.update(kw)
     d = _lib.MoeLatentDims(ctypes.sizeof(_lib.MoeLatentDims), *[base[f] for f, _ in _lib.MoeLatentDims._fields_[1:]])
     return d
@@ -70,6 +71,9 @@ def test_workspace_size_and_layout(lib):
     (dict(align_block=24), 16, -2), (dict(T=-1), 16, -1), (dict(n_experts=8), 9, -1),
     (dict(), 0, -1), (dict(), 65, -2), (dict(rms_eps=-1.0), 16, -1),
     (dict(act_format=2), 16, -1), (dict(act_format=-1), 16, -1),
+    (dict(glu_act=2), 16, -1), (dict(glu_act=1), 16, 0), (dict(glu_act=1, situ_beta=0.0), 16, -1),
+    (dict(glu_act=1, situ_linear_beta=-25.0), 16, -1), (dict(glu_act=1, situ_beta=float("inf")), 16, -1),
+    (dict(glu_act=1, situ_beta=float("nan")), 16, -1), (dict(glu_act=0, situ_beta=0.0), 16, 0),
     # the latent z [T, L] bf16 is indexed with 32-bit byte offsets: T * L * 2 below 2 GiB
     (dict(T=131072, hidden=256, latent=8192, n_experts=1, inter=256, shared_inter=0), 1, -2),
     (dict(T=131071, hidden=256, latent=8192, n_experts=1, inter=256, shared_inter=0), 1, 0),
