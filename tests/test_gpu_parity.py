@@ -78,6 +78,29 @@ MFMA_SMALL = [
 ]
 
 
+# The MFMA path at intermediate widths of the K3 family (1536 and 3072 GLU columns, multiples
+# of 3 x 512): 9..12-tile jobs, two-job experts next to two dense shared jobs, three windows.
+MFMA_WIDE = [
+    # jobs of 9..11 row tiles (3 row tiles per row-wave, the last wave partly or wholly past the
+    # valid rows), ragged tails
+    ("wide_buckets", dict(T=430, hidden=512, latent=512, n_experts=8, topk=3, inter=1536, shared_inter=0)),
+    # k = E: each expert gets every token (280 slots, two jobs), shared experts over two dense jobs
+    ("wide_split_jobs_shared", dict(T=280, hidden=1536, latent=1024, n_experts=4, topk=4, inter=1536,
+                                    shared_inter=1536, norm=False)),
+    # small jobs and three K windows of the latent
+    ("wide_three_windows", dict(T=61, hidden=512, latent=1536, n_experts=12, topk=3, inter=3072,
+                                shared_inter=1536, routed_scaling_factor=2.446, zipf_s=1.1, zipf_c=0.05)),
+]
+
+
+@pytest.mark.parametrize("name,kw", MFMA_WIDE, ids=[s[0] for s in MFMA_WIDE])
+def test_mfma_path_k3_widths_parity(name, kw):
+    H = _harness()
+    c = li.small_config(**kw)
+    out, ref, d = _run_small(c, expert_path=PATH_MFMA)
+    H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
+
+
 @pytest.mark.parametrize("name,kw", MFMA_SMALL, ids=[s[0] for s in MFMA_SMALL])
 def test_mfma_path_parity(name, kw):
     H = _harness()
