@@ -22,6 +22,7 @@
 // token order inside an expert equals flat-index order. An id a token repeats is
 // kept at its first slot only; the later slots are treated like ids out of range
 // (no entry, inv_pos -1), so the result is still deterministic.
+#include "align_dev.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -29,33 +30,10 @@ namespace moe {
 
 namespace {
 
-constexpr int kChunk = 64;  // tokens per chunk (one bit each in a 64-bit mask)
-
-__device__ void build_masks(const int32_t* __restrict__ ids, int T, int k, int E, int chunk,
-                            unsigned long long* mask) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
-  __syncthreads();
-  const int t0 = chunk * kChunk;
-  const int nt = min(kChunk, T - t0);
-  const int np = nt * k;
-  for (int i = threadIdx.x; i < np; i += blockDim.x) {
-    const int e = ids[(size_t)t0 * k + i];
-    if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << (i / k));
-  }
-  __syncthreads();
-}
-
-// true when slot j of the token whose ids start at tok repeats the id of an earlier slot
-__device__ __forceinline__ bool repeated_in_token(const int32_t* __restrict__ tok, int j, int e) {
-  for (int u = 0; u < j; ++u)
-    if (tok[u] == e) return true;
-  return false;
-}
-
 __global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
                                                           int32_t* __restrict__ chunk_cnt) {
   extern __shared__ unsigned long long mask[];
-  build_masks(ids, T, k, E, blockIdx.x, mask);
+  build_masks(ids, T, k, E, blockIdx.x, mask, nullptr);
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     chunk_cnt[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
 }
@@ -118,7 +96,8 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
                                                             int32_t* __restrict__ sorted_ids,
                                                             int32_t* __restrict__ inv_pos) {
   extern __shared__ unsigned long long mask[];
-  build_masks(ids, T, k, E, blockIdx.x, mask);
+  __shared__ int32_t ids_l[kIdsLds];
+  build_masks(ids, T, k, E, blockIdx.x, mask, ids_l);
   const int t0 = blockIdx.x * kChunk;
   const int nt = min(kChunk, T - t0);
   const int np = nt * k;
@@ -126,7 +105,8 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
     const int flat = t0 * k + i;
     const int e = ids[flat];
     const int tl = i / k;
-    if (e < 0 || e >= E || repeated_in_token(ids + (size_t)(t0 + tl) * k, i - tl * k, e)) {
+    if (e < 0 || e >= E ||
+        repeated_in_token(ids_l + tl * k, ids + (size_t)(t0 + tl) * k, np <= kIdsLds, i - tl * k, e)) {
       inv_pos[flat] = -1;
       continue;
     }
@@ -148,51 +128,9 @@ __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __res
   extern __shared__ unsigned long long mask[];      // [E]
   int* offs = (int*)(mask + E);                      // [E]
   __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  build_masks(ids, T, k, E, 0, mask);
-  const int pairs = T * k;
-  const int per = (E + 1023) / 1024;
-  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  int local = 0;
-  for (int e = e0; e < e1; ++e) {
-    const int c = __popcll(mask[e]);
-    counts[e] = c;
-    local += (c + B - 1) / B * B;
-  }
-  part[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - local;
-  for (int e = e0; e < e1; ++e) {
-    offs[e] = run;
-    const int c = __popcll(mask[e]);
-    const int p = (c + B - 1) / B * B;
-    for (int b = 0; b < p / B; ++b) expert_ids[run / B + b] = e;
-    for (int i = c; i < p; ++i) sorted_ids[run + i] = pairs;
-    run += p;
-  }
-  const int total = part[1023];
-  if (tid == 0) *num_post = total;
-  for (int i = total + tid; i < cap; i += 1024) sorted_ids[i] = pairs;
-  for (int b = total / B + tid; b < cap / B; b += 1024) expert_ids[b] = -1;
-  __syncthreads();
-  for (int i = tid; i < pairs; i += 1024) {
-    const int e = ids[i];
-    const int tl = i / k;
-    if (e < 0 || e >= E || repeated_in_token(ids + (size_t)tl * k, i - tl * k, e)) {
-      inv_pos[i] = -1;
-      continue;
-    }
-    const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
-    const int pos = offs[e] + __popcll(below);
-    sorted_ids[pos] = i;
-    inv_pos[i] = pos;
-  }
+  __shared__ int32_t ids_l[kIdsLds];
+  align_one_chunk<1024>(ids, T, k, E, B, cap, counts, sorted_ids, expert_ids, num_post, inv_pos, mask, offs, part,
+                        ids_l);
 }
 
 }  // namespace

@@ -1,0 +1,101 @@
+// Device pieces of moe_align_block_size shared by the align kernels and the fused decode
+// route + align kernel (layout defined in align.hip).
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+constexpr int kChunk = 64;  // tokens per chunk (one bit each in a 64-bit mask)
+
+// Slots of a chunk whose ids are also staged in LDS (for the repeat check below).
+constexpr int kIdsLds = 4096;
+
+// The chunk's 64-bit token masks per expert; with ids_l, also the chunk's ids (when the chunk
+// has at most kIdsLds slots).
+__device__ __forceinline__ void build_masks(const int32_t* __restrict__ ids, int T, int k, int E, int chunk,
+                                            unsigned long long* mask, int32_t* ids_l) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+  __syncthreads();
+  const int t0 = chunk * kChunk;
+  const int nt = min(kChunk, T - t0);
+  const int np = nt * k;
+  const bool stage = np <= kIdsLds;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const int e = ids[(size_t)t0 * k + i];
+    if (stage) ids_l[i] = e;
+    if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << (i / k));
+  }
+  __syncthreads();
+}
+
+// true when slot j of a token repeats the id of an earlier slot of the same token; tok_l
+// (LDS) or tok (global) point at the token's first slot. The LDS copy keeps the up to k - 1
+// dependent reads off the memory path.
+__device__ __forceinline__ bool repeated_in_token(const int32_t* tok_l, const int32_t* __restrict__ tok, bool staged,
+                                                  int j, int e) {
+  if (staged) {
+    for (int u = 0; u < j; ++u)
+      if (tok_l[u] == e) return true;
+  } else {
+    for (int u = 0; u < j; ++u)
+      if (tok[u] == e) return true;
+  }
+  return false;
+}
+
+// All T <= 64 tokens in one chunk, by one block of NT threads: masks, counts, the scan over
+// experts, padding and scatter. mask and offs hold E entries, part NT, ids_l kIdsLds.
+template <int NT>
+__device__ __forceinline__ void align_one_chunk(const int32_t* __restrict__ ids, int T, int k, int E, int B, int cap,
+                                                int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
+                                                int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_post,
+                                                int32_t* __restrict__ inv_pos, unsigned long long* mask, int* offs,
+                                                int* part, int32_t* ids_l) {
+  const int tid = threadIdx.x;
+  build_masks(ids, T, k, E, 0, mask, ids_l);
+  const int pairs = T * k;
+  const int per = (E + NT - 1) / NT;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = __popcll(mask[e]);
+    counts[e] = c;
+    local += (c + B - 1) / B * B;
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < NT; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - local;
+  for (int e = e0; e < e1; ++e) {
+    offs[e] = run;
+    const int c = __popcll(mask[e]);
+    const int p = (c + B - 1) / B * B;
+    for (int b = 0; b < p / B; ++b) expert_ids[run / B + b] = e;
+    for (int i = c; i < p; ++i) sorted_ids[run + i] = pairs;
+    run += p;
+  }
+  const int total = part[NT - 1];
+  if (tid == 0) *num_post = total;
+  for (int i = total + tid; i < cap; i += NT) sorted_ids[i] = pairs;
+  for (int b = total / B + tid; b < cap / B; b += NT) expert_ids[b] = -1;
+  __syncthreads();
+  for (int i = tid; i < pairs; i += NT) {
+    const int e = ids[i];
+    const int tl = i / k;
+    if (e < 0 || e >= E || repeated_in_token(ids_l + tl * k, ids + (size_t)tl * k, pairs <= kIdsLds, i - tl * k, e)) {
+      inv_pos[i] = -1;
+      continue;
+    }
+    const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
+    const int pos = offs[e] + __popcll(below);
+    sorted_ids[pos] = i;
+    inv_pos[i] = pos;
+  }
+}
+
+}  // namespace moe

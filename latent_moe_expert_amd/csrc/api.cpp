@@ -83,10 +83,10 @@ bool mfma_sizes_ok(const moe_latent_dims* d) {
   return d->hidden % 512 == 0 && d->latent % 512 == 0 && d->inter % 512 == 0 && d->shared_inter % 512 == 0;
 }
 
-// K slices of a split-K projection: about 8 row steps of 128 bytes per slice
+// K slices of a split-K projection: about 7 row steps of 256 bytes per slice
 int slices(int K, int bytes_per_weight) {
-  const int steps = K * bytes_per_weight / 128;
-  int sp = steps / 8;
+  const int steps = K * bytes_per_weight / 256;
+  int sp = steps / 7;
   return sp < 1 ? 1 : (sp > 32 ? 32 : sp);
 }
 

@@ -68,12 +68,12 @@ struct GemvSeg {
   const void* W;   // [N, K] row-major, bf16 bits or fp32
   int N;           // rows of W
   int w_f32;       // 1: fp32 weights, split exactly into three bf16 planes
-  int splits;      // K slices (each a whole number of 128-byte row steps)
+  int splits;      // K slices (each a whole number of 256-byte row steps)
   float* part;     // [splits][M][N] fp32 partial sums
 };
 struct GemvArgs {
   const uint16_t* A;  // bf16 [M, lda]
-  int lda, M, K;      // K * (2 or 4) bytes a multiple of 128
+  int lda, M, K;      // K * (2 or 4) bytes a multiple of 256
   GemvSeg seg[2];
   int nseg;
 };

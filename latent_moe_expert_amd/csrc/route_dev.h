@@ -1,0 +1,155 @@
+// Top-k selection of one token's router keys in registers (gfx950, wave64), shared by the
+// per-token route kernel and the fused decode route + align kernel.
+//
+// Keys key_e = sigmoid(logit_e) + bias_e become unique 64-bit composites (ordered key bits,
+// then the inverted expert id), so the larger composite is the larger key with ties going to
+// the lower id (WASTE "Kimi K3, as released", "Against the technical report": the bias only
+// selects; the weights are the unbiased scores renormalised over the selected k, times
+// routed_scaling_factor).
+#pragma once
+#include <float.h>
+
+#include "common.h"
+
+namespace moe {
+
+// Order-preserving map of a float to uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kFastMaxE = 1024;  // experts per token of the register path: 4 per thread of a 256-thread block
+constexpr int kFastMaxK = 16;    // its top-k: the four waves' k candidates are one per lane of one wave
+
+// 64-bit max over the wave, returned to every lane. DPP moves (quad permutations, then
+// the half-row and row mirrors) give each lane the maximum of its row of 16 lanes without
+// going through LDS; the four row maxima are then combined through readlane.
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long x, unsigned long long y) {
+  return y > x ? y : x;
+}
+template <int Ctrl>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, Ctrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), Ctrl, 0xf, 0xf, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)), max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+// The k largest of the composites held by a wave (N per lane), as k successive wave
+// maxima; lane j < k gets the j-th largest (0 when the wave holds fewer than k non-zero
+// composites) and the score stored beside it.
+template <int N>
+__device__ __forceinline__ void wave_top(unsigned long long (&c)[N], const float (&sc)[N], int k, int lane,
+                                         unsigned long long& my_c, float& my_s) {
+  my_c = 0ull;
+  my_s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    unsigned long long m = c[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) m = max_u64(m, c[i]);
+    m = wave_max_u64(m);
+    // the owner (composites are unique, apart from zeros) clears its slot and hands over
+    // the score through readlane from the lowest lane holding m
+    float v = 0.f;
+    bool own = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (c[i] == m && !own) {
+        v = sc[i];
+        c[i] = 0ull;
+        own = true;
+      }
+    }
+    const unsigned long long ownmask = __ballot(own);
+    const int src = ownmask ? __ffsll((long long)ownmask) - 1 : 0;
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+    if (lane == j) {
+      my_c = m;
+      my_s = v;
+    }
+  }
+}
+
+// Route one token with a 256-thread block: thread t holds experts e = t + 256 i; each wave
+// keeps its top k, then wave 0 takes the top k of the 4k candidates and writes the winners in
+// ascending id order with weights s_e / sum(s_selected) * rsf, the sum taken in ascending id
+// order. E <= kFastMaxE, k <= kFastMaxK. Every thread of the block must call it (one block
+// barrier inside); only wave 0 writes.
+struct RouteFastSmem {
+  unsigned long long cand_c[4][kFastMaxK];
+  float cand_s[4][kFastMaxK];
+  int sel_e[kFastMaxK];
+  float sel_s[kFastMaxK];
+};
+__device__ __forceinline__ void route_token_fast(const float* __restrict__ logits_row, const float* __restrict__ bias,
+                                                 int E, int k, float rsf, int32_t* __restrict__ ids_out,
+                                                 float* __restrict__ w_out, RouteFastSmem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // every logit and bias load is issued before any is used (a load under a branch would wait
+  // for the previous one): experts past E and a missing bias read as zeros
+  const __amdgpu_buffer_rsrc_t lg_rs = make_rsrc(logits_row, (uint32_t)E * 4);
+  const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(bias ? bias : logits_row, bias ? (uint32_t)E * 4 : 0u);
+  float lg[4], bs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t off = (uint32_t)(tid + 256 * i) * 4;
+    lg[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lg_rs, off, 0, 0));
+    bs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs_rs, off, 0, 0));
+  }
+  unsigned long long c[4];
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    const float s = sigmoidf_dev(lg[i]);
+    float kv = s + bs[i];
+    kv = (kv == kv) ? kv : -FLT_MAX;  // a NaN key ranks below every real key
+    // experts past E get composite 0, below every real composite
+    c[i] = e < E ? ((unsigned long long)ordered_bits(kv) << 32) | (0xffffffffu - (uint32_t)e) : 0ull;
+    sc[i] = e < E ? s : 0.f;
+  }
+  unsigned long long my_c;
+  float my_s;
+  wave_top<4>(c, sc, k, lane, my_c, my_s);
+  if (lane < k) {
+    sm.cand_c[wave][lane] = my_c;
+    sm.cand_s[wave][lane] = my_s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    unsigned long long c1[1] = {lane < 4 * k ? sm.cand_c[lane / k][lane % k] : 0ull};
+    const float s1[1] = {lane < 4 * k ? sm.cand_s[lane / k][lane % k] : 0.f};
+    wave_top<1>(c1, s1, k, lane, my_c, my_s);
+    const int my_e = (int)(0xffffffffu - (uint32_t)(my_c & 0xffffffffull));
+    // ascending id order
+    if (lane < k) {
+      int p = 0;
+      for (int j = 0; j < k; ++j) p += __builtin_amdgcn_readlane(my_e, j) < my_e ? 1 : 0;
+      sm.sel_e[p] = my_e;
+      sm.sel_s[p] = my_s;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float tot = 0.f;
+    for (int p = 0; p < k; ++p) tot += sm.sel_s[p];  // ascending id order: a fixed rounding order
+    if (lane < k) {
+      ids_out[lane] = sm.sel_e[lane];
+      w_out[lane] = sm.sel_s[lane] / tot * rsf;
+    }
+  }
+}
+
+}  // namespace moe

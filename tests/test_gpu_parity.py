@@ -52,6 +52,12 @@ SMALL = [
     ("single_token", dict(T=1, hidden=256, latent=256, n_experts=10, topk=2, inter=256, shared_inter=256)),
     ("rsf_and_bias", dict(T=23, hidden=256, latent=256, n_experts=24, topk=5, inter=256, shared_inter=256,
                           routed_scaling_factor=2.446, zipf_s=1.1, zipf_c=0.05)),
+    # decode batches outside the one-launch routing (E > 1024, k > 16): separate split-K sums,
+    # the sorting router and align, then the column-spread combine
+    ("experts_over_1024", dict(T=12, hidden=256, latent=512, n_experts=1100, topk=8, inter=256, shared_inter=0)),
+    ("topk_over_16", dict(T=9, hidden=256, latent=256, n_experts=64, topk=24, inter=256, shared_inter=256)),
+    # the widest latent the boundary takes: 32 column blocks per token in the combine
+    ("latent_8192", dict(T=5, hidden=256, latent=8192, n_experts=6, topk=2, inter=256, shared_inter=0)),
 ]
 
 
