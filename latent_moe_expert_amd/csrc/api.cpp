@@ -24,6 +24,7 @@ int hip_fail(hipError_t e) {
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopk = 64;
 constexpr int kMaxLatent = 8192;
+constexpr int kNumCu = 256;  // MI355X compute units: the split-K GEMM sizes its grid for them
 
 // ------------------------------------------------------------------ stage timing
 enum Stage { kProjRouter, kTopk, kAlign, kActEncode, kExpGateUp, kExpDown, kCombine, kUpProj, kNumStages };
@@ -68,10 +69,11 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Plan {
   int T, H, L, E, I, Is, k, B, cap, pairs;
   bool small;      // T <= 64: split-K streaming projections
+  bool mid;        // 64 < T < 2048: the 128 x 128 GEMM, split over K where its tiles leave compute units idle
   bool mfma;       // expert contractions on the scaled MFMA (MOE_PATH_MFMA)
   bool fp8;        // MXFP8 activations of the routed experts (MOE_ACT_MXFP8)
   int max_jobs;    // mfma: capacity of the job table
-  int sz, sr, su;  // K slices of the down-projection, the router and the up-projection
+  int sz, sr, su;  // K slices of the down-projection, the router and the up-projection (1: none)
   size_t z, z8, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
   size_t z_part, r_part, y_part;
   size_t zq, zqs, xq, xqs, hq, hqs, hsq, hsqs, jobs, n_jobs;  // mfma: FP6 activations and the job table
@@ -144,9 +146,22 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
            (d->expert_path == MOE_PATH_AUTO && mfma_sizes_ok(d) && (long long)p.pairs >= 12ll * p.E);
   p.fp8 = d->act_format == MOE_ACT_MXFP8;
   p.max_jobs = p.mfma ? moe::mx_max_jobs(p.pairs, p.E, moe::kMfmaSlotsPerJob) : 0;
-  p.sz = slices(p.H, 2);
-  p.sr = slices(p.H, 4);
-  p.su = slices(p.L, 2);
+  p.mid = !p.small && p.T < 2048;
+  if (p.small) {
+    p.sz = slices(p.H, 2);
+    p.sr = slices(p.H, 4);
+    p.su = slices(p.L, 2);
+  } else if (p.mid) {
+    int sp[2];
+    const int n1[2] = {p.L, p.E}, k1[2] = {p.H, 3 * p.H};
+    moe::gemm_split_plan(p.T, 2, n1, k1, kNumCu, sp);
+    p.sz = sp[0], p.sr = sp[1];
+    const int n2[1] = {p.H}, k2[1] = {p.L};
+    moe::gemm_split_plan(p.T, 1, n2, k2, kNumCu, sp);
+    p.su = sp[0];
+  } else {
+    p.sz = p.sr = p.su = 1;
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -170,10 +185,11 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.cn = take((size_t)p.T * p.L * 2);
   p.hs = take(p.mfma ? 0 : (size_t)p.T * p.Is * 2);
   p.ys = take((size_t)p.T * p.H * 4);
-  const size_t ts = p.small ? (size_t)p.T : 0;
-  p.z_part = take((size_t)p.sz * ts * p.L * 4);
-  p.r_part = take((size_t)p.sr * ts * p.E * 4);
-  p.y_part = take((size_t)p.su * ts * p.H * 4);
+  // split-K partial planes (the GEMV always; the GEMM only for segments it splits)
+  auto planes = [&](int sl) { return p.small || sl > 1 ? (size_t)sl * p.T : (size_t)0; };
+  p.z_part = take(planes(p.sz) * p.L * 4);
+  p.r_part = take(planes(p.sr) * p.E * 4);
+  p.y_part = take(planes(p.su) * p.H * 4);
   // FP6 sizes (MXFP8 rows are smaller); h and the shared h are tiled (a multiple of 16 rows)
   const size_t tq = p.mfma ? (size_t)p.T : 0, cq = p.mfma ? (size_t)p.cap : 0, tq16 = (tq + 15) / 16 * 16;
   p.zq = take(tq * p.L * 3 / 2);
@@ -378,8 +394,11 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     a.lda = p.H;
     a.M = p.T;
     a.nseg = 2;
-    a.seg[0] = {(const uint16_t*)down, p.L, p.H, p.H, moe::kStoreBf16, z, p.L, nullptr, 0, nullptr, 0};
-    a.seg[1] = {wr3, p.E, 3 * p.H, p.H, moe::kStoreF32, logits, p.E, nullptr, 0, nullptr, 0};
+    // segments split over K write fp32 partial planes, summed by the route launch
+    a.seg[0] = {(const uint16_t*)down, p.L, p.H, p.H, p.sz > 1 ? moe::kPartF32 : moe::kStoreBf16,
+                p.sz > 1 ? (void*)at<float>(ws, p.z_part) : (void*)z, p.L, nullptr, 0, nullptr, 0, p.sz};
+    a.seg[1] = {wr3, p.E, 3 * p.H, p.H, p.sr > 1 ? moe::kPartF32 : moe::kStoreF32,
+                p.sr > 1 ? (void*)at<float>(ws, p.r_part) : (void*)logits, p.E, nullptr, 0, nullptr, 0, p.sr};
     MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
   STAGE_MARK(1);
@@ -387,13 +406,14 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
   {
     moe::RouteArgs r{};
     r.logits = logits;
-    r.r_part = p.small ? at<float>(ws, p.r_part) : nullptr;
-    r.sr = p.small ? p.sr : 0;
-    r.z_part = p.small ? at<float>(ws, p.z_part) : nullptr;
+    const bool rp = p.small || p.sr > 1, zp = p.small || p.sz > 1;
+    r.r_part = rp ? at<float>(ws, p.r_part) : nullptr;
+    r.sr = rp ? p.sr : 0;
+    r.z_part = zp ? at<float>(ws, p.z_part) : nullptr;
     r.sz = p.sz;
     r.L = p.L;
     r.z_out = z;
-    r.logits_out = p.small ? logits : nullptr;
+    r.logits_out = rp ? logits : nullptr;
     r.bias = router->select_bias;
     r.T = p.T;
     r.E = p.E;
@@ -642,6 +662,17 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     g.nseg = 1;
     g.seg[0] = {up, p.H, 0, p.su, at<float>(ws, p.y_part)};
     MOE_HIP(moe::launch_dense_gemv(g, s));
+    MOE_HIP(moe::launch_finish_up(at<float>(ws, p.y_part), p.su, p.T, p.H, shared ? ys : nullptr, (uint16_t*)y,
+                                  taps ? taps->y_routed : nullptr, s));
+  } else if (p.su > 1) {
+    moe::GemmArgs a{};
+    a.A = cn;
+    a.lda = p.L;
+    a.M = p.T;
+    a.nseg = 1;
+    a.seg[0] = {(const uint16_t*)up, p.H, p.L, p.L, moe::kPartF32, at<float>(ws, p.y_part), p.H, nullptr, 0, nullptr, 0,
+                p.su};
+    MOE_HIP(moe::launch_gemm_bf16(a, s));
     MOE_HIP(moe::launch_finish_up(at<float>(ws, p.y_part), p.su, p.T, p.H, shared ? ys : nullptr, (uint16_t*)y,
                                   taps ? taps->y_routed : nullptr, s));
   } else {

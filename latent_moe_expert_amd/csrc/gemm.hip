@@ -66,6 +66,27 @@ __device__ __forceinline__ void dma16g(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wa
 // LDS position of 16-byte chunk c (0..7) of tile row r
 __host__ __device__ constexpr int g_pos(int c, int r) { return c ^ ((r >> 1) & 7); }
 
+// One of the two segments as a value, chosen field by field (a select between references to
+// the kernel argument makes the compiler copy the arguments to scratch and index them there).
+__device__ __forceinline__ GemmSeg pick_seg(const GemmArgs& a, bool second) {
+  const GemmSeg& x = a.seg[0];
+  const GemmSeg& y = a.seg[1];
+  GemmSeg r;
+  r.W = second ? y.W : x.W;
+  r.N = second ? y.N : x.N;
+  r.K = second ? y.K : x.K;
+  r.kwrap = second ? y.kwrap : x.kwrap;
+  r.mode = second ? y.mode : x.mode;
+  r.out = second ? y.out : x.out;
+  r.ldo = second ? y.ldo : x.ldo;
+  r.addend = second ? y.addend : x.addend;
+  r.ld_add = second ? y.ld_add : x.ld_add;
+  r.tap = second ? y.tap : x.tap;
+  r.ld_tap = second ? y.ld_tap : x.ld_tap;
+  r.splits = second ? y.splits : x.splits;
+  return r;
+}
+
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[2 * kTile];
   __shared__ __attribute__((aligned(16))) uint8_t st1[2 * kTile];
@@ -82,26 +103,40 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   const int nl = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- block -> (segment, M tile, N tile)
+  // ---- block -> (segment, K slice, M tile, N tile): segment 0's blocks first, each
+  // segment's K slices one after another
   const int tm = (args.M + kBM - 1) / kBM;
-  const int tn0 = (args.seg[0].N + kBN - 1) / kBN;
-  const int tn1 = args.nseg > 1 ? (args.seg[1].N + kBN - 1) / kBN : 0;
-  const int tn = tn0 + tn1;
-  const int total = tm * tn;
+  int tns[2] = {0, 0}, nbs[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i < args.nseg) {
+      tns[i] = (args.seg[i].N + kBN - 1) / kBN;
+      nbs[i] = tm * tns[i] * max(1, args.seg[i].splits);
+    }
+  }
+  const int total = nbs[0] + nbs[1];
   const int per = (total + 7) >> 3;
   const int lb = (int)blockIdx.x >> 3;
   if (lb >= per) return;
   const int L = ((int)blockIdx.x & 7) * per + lb;
   if (L >= total) return;
+  const bool second = L >= nbs[0];
+  const GemmSeg sg = pick_seg(args, second);
+  const int tn = second ? tns[1] : tns[0];
+  const int local = second ? L - nbs[0] : L;
+  const int slice = local / (tm * tn), tl = local % (tm * tn);
   // grouped order: groups of kGM M tiles, M fastest inside a group, so the blocks that run
   // together on an XCD share their W tiles (and each A tile is reused across N in L2)
-  const int grp = L / (kGM * tn), rem = L % (kGM * tn);
+  const int grp = tl / (kGM * tn), rem = tl % (kGM * tn);
   const int gm = min(kGM, tm - grp * kGM);
   const int mt = grp * kGM + rem % gm, nt = rem / gm;
-  const bool second = nt >= tn0;
-  const GemmSeg& sg = args.seg[second ? 1 : 0];
-  const int m0 = mt * kBM, n0 = (second ? nt - tn0 : nt) * kBN;
+  const int m0 = mt * kBM, n0 = nt * kBN;
   const int K = sg.K, kwrap = sg.kwrap;
+  // this block's k-steps: [kb0, kb0 + nks) (a K slice, or all of K)
+  const int nks_all = K / kBK, nsl = max(1, sg.splits);
+  const int kper = (nks_all + nsl - 1) / nsl;
+  const int kb0 = slice * kper;
+  const int nks = max(0, min(nks_all, kb0 + kper) - kb0);
 
   // ---- LDS-DMA of one k-step: chunk t = tid + 256 i; i < 4: A, else W; row t/8 of the
   // tile (t taken mod 1024), LDS position t % 8, global chunk g_pos^-1 = same XOR
@@ -121,7 +156,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
       goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
     }
   }
-  auto dma = [&](uint8_t* st, int ks, bool on) {  // kGemmDma loads
+  auto dma = [&](uint8_t* st, int j, bool on) {  // kGemmDma loads of the block's k-step j
+    const int ks = kb0 + j;
     const uint32_t ka = (uint32_t)((ks * kBK) % kwrap) * 2u, kw = (uint32_t)(ks * kBK) * 2u;
 #pragma unroll
     for (int i = 0; i < kGemmDma; ++i)
@@ -159,9 +195,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   };
 
   // ring: k-step ks reads stage ks % 4; it issues the loads of ks + 3 into the stage read
-  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x 8 loads follow it)
-  const int nks = K / kBK;  // a multiple of 4
-  dma(stage(icg<0>{}), 0, true);
+  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x 8 loads follow it). Steps
+  // past nks load zeros (a K slice need not be a multiple of 4 steps).
+  dma(stage(icg<0>{}), 0, nks > 0);
   dma(stage(icg<1>{}), 1, nks > 1);
   dma(stage(icg<2>{}), 2, nks > 2);
   MOE_GEMM_WAIT_VM_LGKM0(2 * kGemmDma);
@@ -222,7 +258,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
         }
       }
   } else {
-    const bool f32 = sg.mode == kStoreF32;
+    const bool f32 = sg.mode == kStoreF32 || sg.mode == kPartF32;
+    float* outf = (float*)sg.out + (sg.mode == kPartF32 ? (size_t)slice * args.M * sg.ldo : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -233,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
           if (!colok[j]) continue;
           const size_t o = (size_t)rows[i][r] * sg.ldo + colb + 16 * j;
           if (f32)
-            ((float*)sg.out)[o] = acc[i][j][r];
+            outf[o] = acc[i][j][r];
           else
             ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
         }
@@ -275,22 +312,36 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   const int nl = lane & 15, q = lane >> 4;
   const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- block -> (segment, M tile, N tile)
+  // ---- block -> (segment, K slice, M tile, N tile): the segment with the longer K slices
+  // first, each segment's K slices one after another
   const int tm = (args.M + kBM2 - 1) / kBM2;
-  const int f = (args.nseg > 1 && args.seg[1].K > args.seg[0].K) ? 1 : 0;  // longer K first
-  const int tnf = (args.seg[f].N + kBN2 - 1) / kBN2;
-  const int tno = args.nseg > 1 ? (args.seg[1 - f].N + kBN2 - 1) / kBN2 : 0;
+  const GemmSeg& s0 = args.seg[0];
+  const GemmSeg& s1 = args.seg[1];
+  const int sl0 = max(1, s0.splits), sl1 = args.nseg > 1 ? max(1, s1.splits) : 1;
+  const int st0 = (s0.K / kBK2 + sl0 - 1) / sl0, st1 = args.nseg > 1 ? (s1.K / kBK2 + sl1 - 1) / sl1 : 0;
+  const bool f1 = st1 > st0;  // segment 1 first
+  const int tnf = ((f1 ? s1.N : s0.N) + kBN2 - 1) / kBN2;
+  const int tno = args.nseg > 1 ? ((f1 ? s0.N : s1.N) + kBN2 - 1) / kBN2 : 0;
+  const int nbf = tm * tnf * (f1 ? sl1 : sl0);
+  const int nbo = args.nseg > 1 ? tm * tno * (f1 ? sl0 : sl1) : 0;
   int L = (int)blockIdx.x;
-  if (L >= tm * (tnf + tno)) return;
-  const bool first = L < tm * tnf;
-  if (!first) L -= tm * tnf;
+  if (L >= nbf + nbo) return;
+  const bool first = L < nbf;
+  if (!first) L -= nbf;
   const int tn = first ? tnf : tno;
+  const int slice = L / (tm * tn);
+  L %= tm * tn;
   const int grp = L / (kGM * tn), rem = L % (kGM * tn);
   const int gm = min(kGM, tm - grp * kGM);
   const int mt = grp * kGM + rem % gm, nt = rem / gm;
-  const GemmSeg& sg = args.seg[first ? f : 1 - f];
+  const GemmSeg sg = pick_seg(args, first == f1);
   const int m0 = mt * kBM2, n0 = nt * kBN2;
   const int K = sg.K, kwrap = sg.kwrap;
+  // this block's k-steps: [kb0, kb0 + nks) (a K slice, or all of K)
+  const int nks_all = K / kBK2, nsl = max(1, sg.splits);
+  const int kper = (nks_all + nsl - 1) / nsl;
+  const int kb0 = slice * kper;
+  const int nks = max(0, min(nks_all, kb0 + kper) - kb0);
 
   // ---- LDS-DMA of one k-step: load i < 2 carries A chunk t = tid + 512 i, else W chunk
   // t = tid + 512 (i - 2); chunk t is row t / 4 of its tile at LDS position t % 4
@@ -310,7 +361,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
       goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
     }
   }
-  auto dma = [&](uint8_t* st, int ks, bool on) {  // kDma2 loads
+  auto dma = [&](uint8_t* st, int j, bool on) {  // kDma2 loads of the block's k-step j
+    const int ks = kb0 + j;
     const uint32_t ka = (uint32_t)((ks * kBK2) % kwrap) * 2u, kw = (uint32_t)(ks * kBK2) * 2u;
 #pragma unroll
     for (int i = 0; i < kDma2; ++i)
@@ -344,11 +396,11 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   };
 
   // ring: k-step ks reads stage ks % 4; it issues the loads of ks + 3 into the stage read
-  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x kDma2 loads follow it)
-  const int nks = K / kBK2;  // a multiple of 8
-  dma(stage(icg<0>{}), 0, true);
-  dma(stage(icg<1>{}), 1, true);
-  dma(stage(icg<2>{}), 2, true);
+  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x kDma2 loads follow it).
+  // Steps past nks load zeros (a K slice need not be a multiple of 4 steps).
+  dma(stage(icg<0>{}), 0, nks > 0);
+  dma(stage(icg<1>{}), 1, nks > 1);
+  dma(stage(icg<2>{}), 2, nks > 2);
   MOE_GEMM_WAIT_VM_LGKM0(2 * kDma2);
   gemm_barrier();
   for (int k4 = 0; k4 < nks; k4 += 4) {
@@ -376,6 +428,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) colok[j] = n0 + wn * 64 + 16 * j + nl < sg.N;
   const int colb = n0 + wn * 64 + nl;
+  const bool f32 = sg.mode == kStoreF32 || sg.mode == kPartF32;
+  float* outf = (float*)sg.out + (sg.mode == kPartF32 ? (size_t)slice * args.M * sg.ldo : 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float add[4][4];
@@ -400,8 +454,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
         if (sg.mode == kAddStoreBf16) {
           ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(v + add[r][j]);
           if (sg.tap) sg.tap[(size_t)row * sg.ld_tap + colb + 16 * j] = v;
-        } else if (sg.mode == kStoreF32) {
-          ((float*)sg.out)[o] = v;
+        } else if (f32) {
+          outf[o] = v;
         } else {
           ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(v);
         }
@@ -429,25 +483,57 @@ __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ W
 
 }  // namespace
 
+// The 256 x 256 tile for large batches, the 128 x 128 tile (split over K where its tiles
+// leave compute units idle) below: with splits the larger tile's partial planes cost more to
+// write than its lower load traffic per flop saves.
+bool use_tile256(int M) { return M >= kLargeM; }
+
+void gemm_split_plan(int M, int nseg, const int* N, const int* K, int num_cu, int* splits) {
+  // every block one compute unit (either tile's LDS ring takes 128 KB): the fewest k-steps
+  // per block for which all blocks fit at once, each segment's K cut into slices of about
+  // that many steps
+  const bool big = use_tile256(M);
+  const int bm = big ? kBM2 : kBM, bn = big ? kBN2 : kBN, bk = big ? kBK2 : kBK;
+  const long long tm = (M + bm - 1) / bm;
+  long long tiles[2] = {0, 0}, steps[2] = {0, 0};
+  for (int i = 0; i < nseg; ++i) {
+    tiles[i] = tm * ((N[i] + bn - 1) / bn);
+    steps[i] = K[i] / bk;
+  }
+  for (long long spb = 4;; spb += 4) {
+    long long blocks = 0;
+    for (int i = 0; i < nseg; ++i) blocks += tiles[i] * ((steps[i] + spb - 1) / spb);
+    if (blocks <= num_cu || spb >= steps[0] + steps[1]) {
+      for (int i = 0; i < nseg; ++i) splits[i] = (int)((steps[i] + spb - 1) / spb);
+      return;
+    }
+  }
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.nseg < 1 || a.nseg > 2 || a.M < 0 || a.lda % 8) return hipErrorInvalidValue;
-  long long tiles = 0;
-  const long long tm = (a.M + kBM - 1) / kBM;
+  const bool big = use_tile256(a.M);
+  const int bm = big ? kBM2 : kBM, bn = big ? kBN2 : kBN, bk = big ? kBK2 : kBK;
+  long long blocks = 0;
+  bool split = false;
+  const long long tm = (a.M + bm - 1) / bm;
   for (int i = 0; i < a.nseg; ++i) {
     const GemmSeg& g = a.seg[i];
     if (g.K % (4 * kBK) || g.kwrap % kBK || g.kwrap > a.lda || g.K % g.kwrap || g.N <= 0) return hipErrorInvalidValue;
     if ((long long)g.N * g.K * 2 >= (1ll << 31)) return hipErrorInvalidValue;
-    tiles += tm * ((g.N + kBN - 1) / kBN);
+    if (g.splits < 0 || g.splits > g.K / bk || (g.mode == kPartF32) != (g.splits > 1)) return hipErrorInvalidValue;
+    split |= g.splits > 1;
+    blocks += tm * ((g.N + bn - 1) / bn) * (g.splits > 1 ? g.splits : 1);
   }
   if ((long long)a.M * a.lda * 2 >= (1ll << 31)) return hipErrorInvalidValue;
-  if (tiles == 0) return hipSuccess;
-  if (a.M >= kLargeM) {  // enough 256 x 256 tiles to fill the chip
-    long long tiles2 = 0;
-    for (int i = 0; i < a.nseg; ++i) tiles2 += (long long)((a.M + kBM2 - 1) / kBM2) * ((a.seg[i].N + kBN2 - 1) / kBN2);
-    hipLaunchKernelGGL(gemm256_kernel, dim3((unsigned)tiles2), dim3(512), 0, s, a);
+  if (blocks == 0) return hipSuccess;
+  if (a.M >= kLargeM && split) return hipErrorInvalidValue;
+  if (blocks > 0x7ffffff0ll) return hipErrorInvalidValue;
+  if (big) {
+    hipLaunchKernelGGL(gemm256_kernel, dim3((unsigned)blocks), dim3(512), 0, s, a);
     return hipGetLastError();
   }
-  const long long grid = (tiles + 7) / 8 * 8;
+  const long long grid = (blocks + 7) / 8 * 8;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -14,6 +14,7 @@ enum DenseOut : int {
   kStoreBf16 = 0,       // out bf16 [M, ldo]
   kStoreF32 = 1,        // out f32  [M, ldo]
   kAddStoreBf16 = 2,    // out bf16 = bf16(acc + addend[m][n]) (addend may be null); tap f32 = acc
+  kPartF32 = 3,         // out f32 planes [splits][M][ldo]: plane s = the sum over K slice s
 };
 
 struct DenseSeg {
@@ -51,6 +52,7 @@ struct GemmSeg {
   int ld_add;
   float* tap;           // kAddStoreBf16 only, optional
   int ld_tap;
+  int splits;           // kPartF32: K slices (M below the 256 x 256 tile's threshold); else 0 or 1
 };
 struct GemmArgs {
   const uint16_t* A;
@@ -59,6 +61,9 @@ struct GemmArgs {
   int nseg;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// K slices per segment (N[i] x K[i], nseg <= 2) for a split-K launch of M < 2048 rows that
+// puts one block on each of num_cu compute units
+void gemm_split_plan(int M, int nseg, const int* N, const int* K, int num_cu, int* splits);
 // fp32 [N, K] -> bf16 [N, 3K] rows hi | mid | lo with w = hi + mid + lo exactly
 hipError_t launch_split3(const float* W, int N, int K, uint16_t* out, hipStream_t s);
 
