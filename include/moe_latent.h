@@ -92,7 +92,7 @@ extern "C" {
 
 /* Layer sizes. Limits checked by every call (else MOE_EUNSUPPORTED):
  * hidden, latent, inter, shared_inter multiples of 256 (512 for MOE_PATH_MFMA);
- * 1 <= n_experts <= 4096; latent <= 8192; align_block 0 (library choice, 16) or
+ * 1 <= n_experts <= 65535; latent <= 8192; align_block 0 (library choice, 16) or
  * a multiple of 16; the expert-sorted intermediate (capacity x inter bf16) and
  * x (T x hidden bf16) below 2 GiB each. */
 typedef struct moe_latent_dims {
@@ -243,6 +243,7 @@ int moe_align_workspace_size(int T, int topk, int n_experts, size_t* bytes);
  *   num_post   [1]: padded entry count; inv_pos [T*topk]; counts [E]
  *   scratch    >= moe_align_workspace_size bytes
  * capacity as in moe_latent_align_layout. Integer-only and bit-exact.
+ * 1 <= n_experts <= 65535; above 4096 experts topk <= 64 (else MOE_EUNSUPPORTED).
  */
 int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts, int block, int32_t* sorted_ids,
                          int32_t* expert_ids, int32_t* num_post, int32_t* inv_pos, int32_t* counts, void* scratch,

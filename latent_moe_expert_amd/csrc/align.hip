@@ -18,6 +18,9 @@
 //           exclusive scan over experts, expert_ids and all padding.
 //   scatter one block per chunk rebuilds the masks; a slot's rank inside its
 //           expert is (chunk prefix) + popcount(mask & lower tokens).
+// Above 4096 experts the per-expert masks of a chunk do not fit LDS as an array indexed by
+// expert; they are kept in an LDS hash table of the experts the chunk's tokens list (at most
+// 64 * k <= 4096 of them in 8192 slots), with the same counts, scan and ranks.
 // Each token lists an expert at most once (the router's ids are distinct), so
 // token order inside an expert equals flat-index order. An id a token repeats is
 // kept at its first slot only; the later slots are treated like ids out of range
@@ -117,6 +120,53 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   }
 }
 
+// Count and scatter for many experts (E > kLdsExperts): the same per-chunk masks, kept in the
+// LDS hash table; the count kernel first clears its chunk's row of counts (experts absent from
+// the chunk keep 0).
+__global__ __launch_bounds__(256) void align_count_hash_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                               int32_t* __restrict__ chunk_cnt) {
+  __shared__ int32_t keys[kHashSlots];
+  __shared__ unsigned long long masks[kHashSlots];
+  int32_t* row = chunk_cnt + (size_t)blockIdx.x * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) row[e] = 0;
+  build_masks_hash(ids, T, k, E, blockIdx.x, keys, masks, nullptr);  // its barriers order the clears first
+  for (int h = threadIdx.x; h < kHashSlots; h += blockDim.x)
+    if (keys[h] >= 0) row[keys[h]] = __popcll(masks[h]);
+}
+
+__global__ __launch_bounds__(256) void align_scatter_hash_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                                 const int32_t* __restrict__ chunk_pre,
+                                                                 const int32_t* __restrict__ offs,
+                                                                 int32_t* __restrict__ sorted_ids,
+                                                                 int32_t* __restrict__ inv_pos) {
+  __shared__ int32_t keys[kHashSlots];
+  __shared__ unsigned long long masks[kHashSlots];
+  __shared__ int32_t ids_l[kIdsLds];
+  build_masks_hash(ids, T, k, E, blockIdx.x, keys, masks, ids_l);
+  const int t0 = blockIdx.x * kChunk;
+  const int nt = min(kChunk, T - t0);
+  const int np = nt * k;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const int flat = t0 * k + i;
+    const int e = ids[flat];
+    const int tl = i / k;
+    if (e < 0 || e >= E ||
+        repeated_in_token(ids_l + tl * k, ids + (size_t)(t0 + tl) * k, np <= kIdsLds, i - tl * k, e)) {
+      inv_pos[flat] = -1;
+      continue;
+    }
+    const int h = hash_slot(keys, e);  // present: found, not inserted
+    if (h < 0) {                       // not reached for k <= 64 (the table stays half empty)
+      inv_pos[flat] = -1;
+      continue;
+    }
+    const unsigned long long below = tl ? (masks[h] & ((1ull << tl) - 1ull)) : 0ull;
+    const int pos = offs[e] + chunk_pre[(size_t)blockIdx.x * E + e] + __popcll(below);
+    sorted_ids[pos] = flat;
+    inv_pos[flat] = pos;
+  }
+}
+
 // All T tokens in one chunk (T <= 64): masks, counts, scan, padding and scatter
 // in a single block, so decode pays one launch instead of three.
 __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -153,6 +203,16 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t*
   int32_t* chunk = (int32_t*)scratch;
   int32_t* offs = chunk + (size_t)nchunks * E;
   const size_t lds = (size_t)E * sizeof(unsigned long long);
+  if (E > kLdsExperts) {  // masks in an LDS hash table (k <= 64)
+    if (k > 64) return hipErrorInvalidValue;
+    if (nchunks > 0) hipLaunchKernelGGL(align_count_hash_kernel, dim3(nchunks), dim3(256), 0, s, ids, T, k, E, chunk);
+    hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks, E, B, T * k, cap, chunk, counts, offs,
+                       sorted_ids, expert_ids, num_post);
+    if (nchunks > 0)
+      hipLaunchKernelGGL(align_scatter_hash_kernel, dim3(nchunks), dim3(256), 0, s, ids, T, k, E, chunk, offs,
+                         sorted_ids, inv_pos);
+    return hipGetLastError();
+  }
   if (nchunks <= 1) {
     hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(1024), lds + (size_t)E * sizeof(int), s, ids, T, k, E, B,
                        cap, counts, sorted_ids, expert_ids, num_post, inv_pos);

@@ -19,7 +19,7 @@ __device__ __forceinline__ void build_masks(const int32_t* __restrict__ ids, int
   const int t0 = chunk * kChunk;
   const int nt = min(kChunk, T - t0);
   const int np = nt * k;
-  const bool stage = np <= kIdsLds;
+  const bool stage = ids_l != nullptr && np <= kIdsLds;
   for (int i = threadIdx.x; i < np; i += blockDim.x) {
     const int e = ids[(size_t)t0 * k + i];
     if (stage) ids_l[i] = e;
@@ -41,6 +41,45 @@ __device__ __forceinline__ bool repeated_in_token(const int32_t* tok_l, const in
       if (tok[u] == e) return true;
   }
   return false;
+}
+
+// Many experts (their per-expert LDS masks would not fit): the chunk's masks live in an LDS hash
+// table keyed by expert id. A chunk of 64 tokens with k <= 64 lists at most 4096 distinct experts,
+// so the table (8192 slots, linear probing) is at most half full and every probe sequence ends.
+constexpr int kHashSlots = 8192;
+constexpr int kLdsExperts = 4096;  // up to this many experts the masks are an LDS array indexed by expert
+
+// slot of expert e, inserting it if absent (-1 never happens for k <= 64)
+__device__ __forceinline__ int hash_slot(int32_t* keys, int e) {
+  uint32_t h = ((uint32_t)e * 2654435761u) >> 19;  // 13 bits
+  for (int p = 0; p < kHashSlots; ++p) {
+    const int old = atomicCAS(&keys[h], -1, e);
+    if (old == -1 || old == e) return (int)h;
+    h = (h + 1) & (kHashSlots - 1);
+  }
+  return -1;
+}
+
+__device__ __forceinline__ void build_masks_hash(const int32_t* __restrict__ ids, int T, int k, int E, int chunk,
+                                                 int32_t* keys, unsigned long long* masks, int32_t* ids_l) {
+  for (int i = threadIdx.x; i < kHashSlots; i += blockDim.x) {
+    keys[i] = -1;
+    masks[i] = 0ull;
+  }
+  __syncthreads();
+  const int t0 = chunk * kChunk;
+  const int nt = min(kChunk, T - t0);
+  const int np = nt * k;
+  const bool stage = ids_l != nullptr && np <= kIdsLds;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    const int e = ids[(size_t)t0 * k + i];
+    if (stage) ids_l[i] = e;
+    if (e >= 0 && e < E) {
+      const int h = hash_slot(keys, e);
+      if (h >= 0) atomicOr(&masks[h], 1ull << (i / k));
+    }
+  }
+  __syncthreads();
 }
 
 // All T <= 64 tokens in one chunk, by one block of NT threads: masks, counts, the scan over

@@ -21,8 +21,10 @@ int hip_fail(hipError_t e) {
     if (e_ != hipSuccess) return hip_fail(e_); \
   } while (0)
 
-constexpr int kMaxExperts = 4096;
+constexpr int kMaxExperts = 65535;  // expert ids are int32 throughout; the router and align switch to
+                                     // their large-E forms above 4096
 constexpr int kMaxTopk = 64;
+constexpr int kMaxQbExperts = 4096;  // Quantile Balancing: one wave holds a token's scores, 64 per lane
 constexpr int kMaxLatent = 8192;
 constexpr int kNumCu = 256;  // MI355X compute units: the split-K GEMM sizes its grid for them
 
@@ -822,6 +824,7 @@ int moe_align_block_size(const int32_t* topk_ids, int T, int topk, int n_experts
                          size_t scratch_bytes, void* stream) {
   if (T < 0 || topk < 1 || n_experts < 1 || block < 1) return MOE_EINVAL;
   if (n_experts > kMaxExperts || (long long)T * topk > (1ll << 30)) return MOE_EUNSUPPORTED;
+  if (n_experts > 4096 && topk > 64) return MOE_EUNSUPPORTED;
   if (!sorted_ids || !expert_ids || !num_post || !counts || (T > 0 && (!topk_ids || !inv_pos))) return MOE_EINVAL;
   if (scratch_bytes < moe::align_scratch_bytes(T, n_experts) || (!scratch && scratch_bytes)) return MOE_EWORKSPACE;
   MOE_HIP(moe::launch_align(topk_ids, T, topk, n_experts, block, counts, sorted_ids, expert_ids, num_post, inv_pos,
@@ -843,7 +846,7 @@ namespace {
 int qb_check(const float* scores, const float* bias, int m, int n, int topk, const float* alpha, const int32_t* hist,
              const float* new_bias) {
   if (m < 0 || n < 2 || topk < 1 || topk >= n) return MOE_EINVAL;
-  if (n > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (n > kMaxQbExperts) return MOE_EUNSUPPORTED;
   if (!hist || (m > 0 && (!scores || !alpha)) || ((uintptr_t)scores & 15)) return MOE_EINVAL;
   const size_t sb = (size_t)m * n * sizeof(float), hb = (size_t)n * moe::kQbBins * sizeof(int32_t);
   const size_t ab = (size_t)m * sizeof(float), bb = bias ? (size_t)n * sizeof(float) : 0;
@@ -887,7 +890,7 @@ int moe_qb_bias(const int32_t* hist, int n, long long m_total, int topk, float* 
   long long q = 0;
   const int rc = moe_qb_target(m_total, n, topk, &q);
   if (rc != MOE_OK) return rc;
-  if (n > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (n > kMaxQbExperts) return MOE_EUNSUPPORTED;
   if (!hist || !new_bias) return MOE_EINVAL;
   if (overlap(new_bias, (size_t)n * sizeof(float), hist, (size_t)n * moe::kQbBins * sizeof(int32_t)))
     return MOE_EALIAS;

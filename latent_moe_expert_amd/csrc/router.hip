@@ -9,8 +9,10 @@
 // with ties going to the lower id. For up to 1024 experts and k <= 16 a block's
 // threads hold a token's composites in registers; each wave takes its k largest
 // as k successive wave-wide maxima, then one wave takes the k largest of those.
-// Otherwise a bitonic sort in LDS orders all of them. Either way the winners are written in
-// ascending id order with weights s_e / sum(s_selected) * rsf from the unbiased
+// Up to 4096 experts a bitonic sort in LDS orders all of them; beyond that (up to 65535) a
+// radix select over the keys' 32-bit images finds the k-th largest key and an ordered pass
+// takes the keys above it and the lowest ids among those equal to it. Every path writes the
+// winners in ascending id order with weights s_e / sum(s_selected) * rsf from the unbiased
 // scores, summed in ascending id order.
 //
 // When the down-projection and router logits arrive as partial sums over K
@@ -134,6 +136,129 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
 }
 
+// Experts beyond the LDS sort (E > kMaxE): one block per token finds the k-th largest key by a
+// radix select on the keys' order-preserving 32-bit images (four passes over 8-bit digits, each
+// a 256-bin LDS histogram of the keys that match the digits found so far, read from the logits
+// row in L2), then takes every key above it and, of the keys equal to it, the lowest ids, in
+// one ordered pass over the experts (block prefix sums), which also yields ascending id order.
+__device__ __forceinline__ uint32_t radix_key(const RouteArgs& a, const float* lg, int e, float* sig) {
+  const float s = sigmoidf_dev(lg[e]);
+  float kv = s + (a.bias ? a.bias[e] : 0.f);
+  kv = (kv == kv) ? kv : -FLT_MAX;  // a NaN key ranks below every real key
+  *sig = s;
+  return ordered_bits(kv);
+}
+
+// exclusive prefix of f over the block (256 threads, in thread order) and the block total
+__device__ __forceinline__ int block_prefix(bool f, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned long long b = __ballot(f);
+  const int in_wave = __popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[w] = __popcll(b);
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += wsum[i];
+  *total = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  __syncthreads();
+  return off + in_wave;
+}
+
+__global__ __launch_bounds__(256) void route_radix_kernel(RouteArgs a) {
+  __shared__ int hist[256];
+  __shared__ int wsum[4];
+  __shared__ int sel_e[64];
+  __shared__ float sel_s[64];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_rem;
+  __shared__ float s_tot;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int E = a.E, k = a.k;
+  const float* lg = a.logits + (size_t)t * E;
+  uint32_t prefix = 0u, mask = 0u;
+  int rem = k;  // how many of the keys matching prefix under mask are still to be taken
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      float sg;
+      const uint32_t u = radix_key(a, lg, e, &sg);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds digits 4l..4l+3; cum(d) = number of matching keys with digit >= d; the digit
+      // taken is the largest d with cum(d) >= rem
+      int h[4], lsum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = hist[4 * tid + i];
+        lsum += h[i];
+      }
+      int above = lsum;  // inclusive suffix sum over lanes >= tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_down(above, o, 64);
+        if (tid + o < 64) above += v;
+      }
+      above -= lsum;  // keys with digits in higher lanes
+      int best = -1, best_above = 0;
+      int cum = above;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (best < 0 && cum + h[i] >= rem) {
+          best = 4 * tid + i;
+          best_above = cum;
+        }
+        cum += h[i];
+      }
+      int d = best;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) d = max(d, __shfl_xor(d, o, 64));
+      if (best == d && d >= 0) {
+        s_prefix = prefix | ((uint32_t)d << shift);
+        s_rem = rem - best_above;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    rem = s_rem;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  // prefix is the k-th largest image; every key above it is taken, and the first rem keys equal
+  // to it in id order
+  int eq_seen = 0, sel_seen = 0;
+  for (int c0 = 0; c0 < E && sel_seen < k; c0 += 256) {
+    const int e = c0 + tid;
+    float sg = 0.f;
+    const uint32_t u = e < E ? radix_key(a, lg, e, &sg) : 0u;
+    const bool eq = e < E && u == prefix;
+    int n_eq;
+    const int eq_rank = block_prefix(eq, wsum, &n_eq);
+    const bool sel = e < E && (u > prefix || (eq && eq_seen + eq_rank < rem));
+    int n_sel;
+    const int idx = sel_seen + block_prefix(sel, wsum, &n_sel);
+    if (sel && idx < k) {
+      sel_e[idx] = e;
+      sel_s[idx] = sg;
+    }
+    eq_seen += n_eq;
+    sel_seen += n_sel;
+  }
+  __syncthreads();
+  if (tid == 0) {  // ascending id order: a fixed rounding order
+    float tot = 0.f;
+    for (int p = 0; p < k; ++p) tot += sel_s[p];
+    s_tot = tot;
+  }
+  __syncthreads();
+  if (tid < k) {
+    const float tot = s_tot;
+    a.ids[(size_t)t * k + tid] = sel_e[tid];
+    a.w[(size_t)t * k + tid] = sel_s[tid] / tot * a.rsf;
+  }
+}
+
 // One token per block (E <= kFastMaxE, k <= kFastMaxK).
 __global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
   __shared__ RouteFastSmem sm;
@@ -151,10 +276,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     const size_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(reduce_planes_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, a);
   }
+  if (a.k > 64) return hipErrorInvalidValue;
   if (a.E <= kFastMaxE && a.k <= kFastMaxK)
     hipLaunchKernelGGL(route_fast_kernel, dim3(a.T), dim3(256), 0, s, a);
-  else
+  else if (a.E <= kMaxE)
     hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(route_radix_kernel, dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -67,7 +67,8 @@ def test_workspace_size_and_layout(lib):
 
 @pytest.mark.parametrize("kw,k,code", [
     (dict(hidden=100), 16, -2), (dict(latent=3600), 16, -2), (dict(inter=3200), 16, -2),
-    (dict(n_experts=5000), 16, -2), (dict(T=200000), 16, -2),
+    (dict(n_experts=65536, hidden=256), 16, -2), (dict(n_experts=65535, hidden=256), 16, 0),
+    (dict(n_experts=5000), 16, 0), (dict(T=200000), 16, -2),
     (dict(align_block=24), 16, -2), (dict(T=-1), 16, -1), (dict(n_experts=8), 9, -1),
     (dict(), 0, -1), (dict(), 65, -2), (dict(rms_eps=-1.0), 16, -1),
     (dict(act_format=2), 16, -1), (dict(act_format=-1), 16, -1),
@@ -170,7 +171,9 @@ def test_rmsnorm_argument_errors(lib):
 def test_align_argument_errors(lib):
     n = ctypes.c_size_t()
     assert lib.moe_align_workspace_size(16, 16, 896, ctypes.byref(n)) == 0 and n.value > 0
-    assert lib.moe_align_workspace_size(16, 16, 5000, ctypes.byref(n)) == -2
+    assert lib.moe_align_workspace_size(16, 16, 65536, ctypes.byref(n)) == -2
+    assert lib.moe_align_workspace_size(16, 16, 65535, ctypes.byref(n)) == 0 and n.value == (65535 + 65535) * 4
+    assert lib.moe_align_workspace_size(16, 16, 896, ctypes.byref(n)) == 0
     P = 0x100000
     assert lib.moe_align_block_size(P, 16, 16, 896, 0, P, P, P, P, P, P, n.value, None) == -1
     assert lib.moe_align_block_size(P, 16, 16, 896, 16, None, P, P, P, P, P, n.value, None) == -1
@@ -264,7 +267,7 @@ def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_launch(lib):
     assert _ws(lib, _dims(T=64))[1] > _lib.STATIC_SCRATCH_BYTES >= _ws(lib, _dims(T=16))[1]
     assert call(_dims(T=64)) == -4
     assert call(_dims(T=0)) == 0
-    assert call(_dims(n_experts=5000)) == -2
+    assert call(_dims(n_experts=65536)) == -2
     bad = _dims()
     bad.struct_size = 8
     assert call(bad) == -6

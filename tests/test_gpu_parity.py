@@ -58,6 +58,10 @@ SMALL = [
     ("topk_over_16", dict(T=9, hidden=256, latent=256, n_experts=64, topk=24, inter=256, shared_inter=256)),
     # the widest latent the boundary takes: 32 column blocks per token in the combine
     ("latent_8192", dict(T=5, hidden=256, latent=8192, n_experts=6, topk=2, inter=256, shared_inter=0)),
+    # above 4096 experts: the radix-select router and the hash-table align (one chunk, then several)
+    ("experts_over_4096", dict(T=20, hidden=256, latent=256, n_experts=5000, topk=16, inter=256, shared_inter=0)),
+    ("experts_over_4096_chunks", dict(T=100, hidden=256, latent=256, n_experts=5000, topk=8, inter=256,
+                                      shared_inter=256)),
 ]
 
 
@@ -214,7 +218,10 @@ def test_determinism_bitwise():
 
 @pytest.mark.parametrize("T,k,E,B,seed", [(5, 2, 8, 16, 0), (300, 16, 896, 16, 1), (1000, 4, 37, 32, 2),
                                           (8192, 16, 896, 16, 3), (64, 8, 4096, 16, 4), (1, 1, 1, 1, 5),
-                                          (130, 3, 3, 64, 6)])
+                                          (130, 3, 3, 64, 6),
+                                          # above 4096 experts the chunk masks live in an LDS hash table
+                                          (48, 16, 65535, 16, 7), (300, 64, 20000, 16, 8), (1000, 8, 4097, 32, 9),
+                                          (70, 2, 65535, 1, 10)])
 def test_moe_align_block_size_bit_exact_on_oracle_ids(T, k, E, B, seed):
     """The align entry point on ids the oracle routed (here: random distinct ids),
     bit-exact on every array including the padded tail."""
@@ -241,11 +248,14 @@ def test_moe_align_block_size_bit_exact_on_oracle_ids(T, k, E, B, seed):
     assert np.array_equal(counts.cpu().numpy(), ref["counts"])
 
 
-def test_moe_route_entry_point():
+@pytest.mark.parametrize("T,E,k", [(50, 64, 8),
+                                   # above 4096 experts: the radix-select router
+                                   (20, 5000, 16), (6, 65535, 64)])
+def test_moe_route_entry_point(T, E, k):
     from latent_moe_expert_amd import layer as L
     from oracle.layer import route
     H = _harness()
-    c = li.small_config(T=50, n_experts=64, topk=8, hidden=512, latent=256, inter=256, shared_inter=256)
+    c = li.small_config(T=T, n_experts=E, topk=k, hidden=512, latent=256, inter=256, shared_inter=256)
     d = li.build(c, experts=False)
     dims = L.make_dims(c.T, c.hidden, c.latent, c.n_experts, c.inter, c.shared_inter)
     x = H.to_dev_bf16(d["x"])
