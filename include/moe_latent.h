@@ -182,6 +182,12 @@ int moe_latent_align_layout(const moe_latent_dims* d, int topk, int32_t* capacit
  * win, ties to the lower expert id; weights w = s / sum(s_selected) * rsf. The
  * experts' GLU activation is d->glu_act (SiLU(gate) * up or SiTU). Near-ties of the key at the k-th place
  * can route differently from a float64 evaluation (fp32 here).
+ *
+ * Debugging: when the environment variable MOE_DUMP_ROUTE names a file, moe_latent_forward
+ * and moe_latent_forward_ex synchronize the stream after their launches and append one record
+ * per call: the 4 bytes "MOER", int32 T, k, E, then int32 topk_ids [T, k] and float topk_w
+ * [T, k], little-endian. The variable is read on every call; leave it unset under graph
+ * capture. A record that cannot be written does not fail the call.
  */
 int moe_latent_forward(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
                        const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,

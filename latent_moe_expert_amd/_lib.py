@@ -5,7 +5,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_latent.so")
+# MOE_LATENT_LIB names another build of the same library (the CPU tests load a sanitized copy)
+LIB_PATH = os.environ.get("MOE_LATENT_LIB") or os.path.join(_HERE, "libmoe_latent.so")
 
 MOE_OK = 0
 QB_BINS = 1000

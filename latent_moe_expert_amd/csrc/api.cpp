@@ -1,6 +1,8 @@
 // C ABI of the latent-MoE layer library: validation, workspace plan, launches.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -322,6 +324,28 @@ namespace {
 
 // The forward of every entry point; with record_stages false it records no stage events
 // (the entry point that allocates nothing must not create events either).
+// MOE_DUMP_ROUTE=path: append this call's routing to a file (debugging; synchronizes the stream)
+void dump_route(const int32_t* ids, const float* w, int T, int k, int E, hipStream_t s) {
+  const char* path = std::getenv("MOE_DUMP_ROUTE");
+  if (!path || !*path) return;
+  const size_t n = (size_t)T * k;
+  std::vector<int32_t> hid(n);
+  std::vector<float> hw(n);
+  if (hipStreamSynchronize(s) != hipSuccess || hipMemcpy(hid.data(), ids, n * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(hw.data(), w, n * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return;
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lk(mu);
+  FILE* f = std::fopen(path, "ab");
+  if (!f) return;
+  const int32_t head[3] = {T, k, E};
+  std::fwrite("MOER", 1, 4, f);
+  std::fwrite(head, 4, 3, f);
+  std::fwrite(hid.data(), 4, n, f);
+  std::fwrite(hw.data(), 4, n, f);
+  std::fclose(f);
+}
+
 int forward_impl(const moe_latent_dims* d, const void* x, const void* down, const void* norm,
                  const moe_router* router, const uint8_t* experts_packed, const uint8_t* experts_scales,
                  const void* up, const moe_shared* shared, int topk, void* y, void* workspace, size_t ws_bytes,
@@ -692,6 +716,7 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     std::lock_guard<std::mutex> lk(g_timing.mu);
     if (ev_idx < (int)g_timing.done.size()) g_timing.done[(size_t)ev_idx] = 1;
   }
+  if (record_stages) dump_route(ids, w, p.T, p.k, p.E, s);
 
   if (taps) {
     int r;

@@ -251,3 +251,21 @@ def moe_rmsnorm(x, y, weight=None, eps: float = 1e-6, stream=None) -> None:
     rc = _lib.load().moe_rmsnorm(_ptr(x, _BF16, "x"), x.shape[0], x.shape[1], _ptr(weight, _BF16, "weight"), eps,
                                  _ptr(y, _BF16, "y"), _stream(stream))
     _check("moe_rmsnorm", rc)
+
+
+def read_route_dump(path: str) -> list:
+    """Records a forward appended to the file named by MOE_DUMP_ROUTE: one dict per call with
+    topk_ids int32 [T, k], topk_w float32 [T, k] and n_experts."""
+    import numpy as np
+    data = open(path, "rb").read()
+    out, o = [], 0
+    while o < len(data):
+        if data[o:o + 4] != b"MOER":
+            raise ValueError(f"{path}: no record at byte {o}")
+        T, k, E = (int(v) for v in np.frombuffer(data, dtype="<i4", count=3, offset=o + 4))
+        n = T * k
+        ids = np.frombuffer(data, dtype="<i4", count=n, offset=o + 16).reshape(T, k)
+        w = np.frombuffer(data, dtype="<f4", count=n, offset=o + 16 + 4 * n).reshape(T, k)
+        out.append({"topk_ids": ids.copy(), "topk_w": w.copy(), "n_experts": E})
+        o += 16 + 8 * n
+    return out

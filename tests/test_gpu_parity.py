@@ -271,6 +271,27 @@ def test_moe_route_entry_point(T, E, k):
     assert np.abs(lg.cpu().numpy() - r["logits"]).max() <= 1e-5 * np.abs(r["logits"]).max()
 
 
+def test_route_dump_appends_each_forward(tmp_path, monkeypatch):
+    """MOE_DUMP_ROUTE=path: every forward appends its top-k ids and weights, equal to the taps."""
+    from latent_moe_expert_amd import layer as L
+    H = _harness()
+    c = li.small_config(T=21, n_experts=40, topk=6, hidden=512, latent=256, inter=256, shared_inter=256)
+    d = li.build(c)
+    dl = H.DeviceLayer(c, dense={k: d[k] for k in ("down", "up", "norm", "router", "select_bias")},
+                       experts=(d["exp_packed"], d["exp_scales"]))
+    path = tmp_path / "route.bin"
+    monkeypatch.setenv("MOE_DUMP_ROUTE", str(path))
+    outs = [dl.run(d["x"]), dl.run(d["x"][:9])]
+    monkeypatch.delenv("MOE_DUMP_ROUTE")
+    dl.run(d["x"])  # unset: nothing appended
+    recs = L.read_route_dump(str(path))
+    assert len(recs) == 2
+    for rec, out in zip(recs, outs):
+        assert rec["n_experts"] == c.n_experts
+        assert np.array_equal(rec["topk_ids"], out["topk_ids"])
+        assert np.array_equal(rec["topk_w"], out["topk_w"])
+
+
 def test_tiny_named_config_full_width():
     """T=4, hidden 7168, latent 3584, 16 experts, top-4, intermediate 3072, no norm, no shared."""
     H = _harness()
