@@ -271,6 +271,35 @@ def test_moe_route_entry_point(T, E, k):
     assert np.abs(lg.cpu().numpy() - r["logits"]).max() <= 1e-5 * np.abs(r["logits"]).max()
 
 
+@pytest.mark.parametrize("E,n_top", [(128, 70), (128, 40), (896, 0), (1024, 17)])
+def test_decode_route_exact_ties(E, n_top):
+    """Keys tied exactly at the top (zero router: every score 0.5; bias 1 on n_top experts, 0
+    elsewhere): the 16 lowest ids among the top keys win (all 16 lowest ids when nothing is
+    biased), each with weight rsf / 16, and the layout is the oracle's align of those ids. The
+    near-tie rule of the other parity tests excludes exactly these tokens, so here the expected
+    ids follow from the tie rule itself."""
+    from oracle.layer import align
+    H = _harness()
+    c = li.small_config(T=5, n_experts=E, topk=16, hidden=256, latent=256, inter=256, shared_inter=0)
+    d = li.build(c)
+    rng = np.random.default_rng(E + n_top)
+    top = np.sort(rng.choice(E, size=n_top, replace=False)) if n_top else np.arange(0)
+    bias = np.zeros(E, np.float32)
+    bias[top] = 1.0
+    dense = {"down": d["down"], "up": d["up"], "norm": d["norm"], "router": np.zeros_like(d["router"]),
+             "select_bias": bias}
+    dl = H.DeviceLayer(c, dense=dense, experts=(d["exp_packed"], d["exp_scales"]))
+    out = dl.run(d["x"])
+    want = top[:16] if n_top >= 16 else np.arange(16)
+    assert (out["topk_ids"] == want[None, :].astype(np.int32)).all()
+    assert (out["topk_w"] == np.float32(c.routed_scaling_factor / 16)).all()
+    ref = align(out["topk_ids"].astype(np.int64), E, out["B"])
+    n = ref["num_post"]
+    assert int(out["num_post"][0]) == n
+    assert np.array_equal(out["sorted_ids"][:n], ref["sorted_ids"][:n])
+    assert np.array_equal(out["inv_pos"], ref["inv_pos"])
+
+
 def test_route_dump_appends_each_forward(tmp_path, monkeypatch):
     """MOE_DUMP_ROUTE=path: every forward appends its top-k ids and weights, equal to the taps."""
     from latent_moe_expert_amd import layer as L
