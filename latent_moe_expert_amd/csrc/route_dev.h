@@ -93,21 +93,35 @@ struct RouteFastSmem {
   int sel_e[kFastMaxK];
   float sel_s[kFastMaxK];
 };
+// The selection itself, on the logits of experts tid + 256 i (i < 4) already in registers.
+__device__ __forceinline__ void route_select_fast(const float (&lg)[4], const float* __restrict__ bias, int E, int k,
+                                                  float rsf, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                                  RouteFastSmem& sm);
+
 __device__ __forceinline__ void route_token_fast(const float* __restrict__ logits_row, const float* __restrict__ bias,
                                                  int E, int k, float rsf, int32_t* __restrict__ ids_out,
                                                  float* __restrict__ w_out, RouteFastSmem& sm) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // every logit and bias load is issued before any is used (a load under a branch would wait
-  // for the previous one): experts past E and a missing bias read as zeros
+  // every logit load is issued before any is used (a load under a branch would wait for the
+  // previous one): experts past E read as zeros
   const __amdgpu_buffer_rsrc_t lg_rs = make_rsrc(logits_row, (uint32_t)E * 4);
-  const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(bias ? bias : logits_row, bias ? (uint32_t)E * 4 : 0u);
-  float lg[4], bs[4];
+  float lg[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t off = (uint32_t)(tid + 256 * i) * 4;
-    lg[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lg_rs, off, 0, 0));
-    bs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs_rs, off, 0, 0));
-  }
+  for (int i = 0; i < 4; ++i)
+    lg[i] = __builtin_bit_cast(float,
+                               __builtin_amdgcn_raw_buffer_load_b32(lg_rs, (uint32_t)(threadIdx.x + 256 * i) * 4, 0, 0));
+  route_select_fast(lg, bias, E, k, rsf, ids_out, w_out, sm);
+}
+
+__device__ __forceinline__ void route_select_fast(const float (&lg)[4], const float* __restrict__ bias, int E, int k,
+                                                  float rsf, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                                  RouteFastSmem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // a missing bias reads as zeros
+  const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(bias, bias ? (uint32_t)E * 4 : 0u);
+  float bs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    bs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs_rs, (uint32_t)(tid + 256 * i) * 4, 0, 0));
   unsigned long long c[4];
   float sc[4];
 #pragma unroll

@@ -267,10 +267,52 @@ __global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
                    a.w + (size_t)t * a.k, sm);
 }
 
+// Decode batches with split-K planes (E <= kFastMaxE, k <= kFastMaxK): one launch. Blocks
+// 0..T-1 each sum their token's logits over the slices (slice order, as reduce_planes does),
+// keep them in registers for the selection and store them; the blocks after them sum the
+// latent rows.
+__global__ __launch_bounds__(256) void route_fast_planes_kernel(RouteArgs a) {
+  __shared__ RouteFastSmem sm;
+  const int t = blockIdx.x;
+  if (t >= a.T) {
+    const size_t nz = (size_t)a.T * a.L / 4;
+    for (size_t i = (size_t)(t - a.T) * 256 + threadIdx.x; i < nz; i += (size_t)(gridDim.x - a.T) * 256) sum_z_group(a, i);
+    return;
+  }
+  const size_t rplane = (size_t)a.T * a.E, row = (size_t)t * a.E;
+  float lg[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < a.sr; s0 += 8) {
+    float v[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = threadIdx.x + 256 * i;
+        v[u][i] = s0 + u < a.sr && e < a.E ? a.r_part[(s0 + u) * rplane + row + e] : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[i] += v[u][i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    if (e < a.E) a.logits_out[row + e] = lg[i];
+  }
+  route_select_fast(lg, a.bias, a.E, a.k, a.rsf, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, sm);
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (a.r_part && a.z_part && a.E <= kFastMaxE && a.k <= kFastMaxK && a.logits_out == a.logits) {
+    // one launch: T routing blocks, then a latent-summing block per 256 float4 groups
+    const size_t zb = ((size_t)a.T * a.L / 4 + 255) / 256;
+    hipLaunchKernelGGL(route_fast_planes_kernel, dim3((unsigned)(a.T + (zb < 4096 ? zb : 4096))), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.r_part || a.z_part) {  // finish split-K sums first, in parallel over all elements
     const size_t n = (a.z_part ? (size_t)a.T * a.L / 4 : 0) + (a.r_part ? (size_t)a.T * a.E : 0);
     const size_t blocks = (n + 255) / 256;
