@@ -139,7 +139,10 @@ typedef struct moe_latent_taps {
   int32_t* num_post;      /* [1] */
   int32_t* inv_pos;       /* [T*k]        position of slot t*k+j in sorted_ids */
   float* c;               /* fp32 [T, L]  weighted aggregate before the norm */
-  uint16_t* c_norm;       /* bf16 [T, L]  input of the up-projection */
+  uint16_t* c_norm;       /* bf16 [T, L]  the normalised aggregate RMSNorm(c) (for T > 64 the
+                                           up-projection's input; for T <= 64 the
+                                           up-projection reads bf16(g * c) and its output
+                                           is scaled by 1 / rms(c), the same function) */
   float* y_routed;        /* fp32 [T, H]  up-projection output */
   float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none) */
   float* O;               /* fp32 [T*k, L] the routed expert's output of slot t*k+j (token t's

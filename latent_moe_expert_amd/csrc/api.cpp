@@ -80,6 +80,7 @@ struct Plan {
   int sz, sr, su;  // K slices of the down-projection, the router and the up-projection (1: none)
   size_t z, z8, logits, ids, w, counts, sorted, expert_ids, num_post, inv_pos, align_scratch, h, O, cn, hs, ys;
   size_t z_part, r_part, y_part;
+  size_t cf, psq;  // small: c fp32 [T, L] and each column block's sum of c^2 [T, L/256]
   size_t zq, zqs, xq, xqs, hq, hqs, hsq, hsqs, jobs, n_jobs;  // mfma: FP6 activations and the job table
   size_t wr3;      // T > 64: router weight split into three bf16 planes [E, 3H]
   size_t total;
@@ -194,6 +195,8 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.z_part = take(planes(p.sz) * p.L * 4);
   p.r_part = take(planes(p.sr) * p.E * 4);
   p.y_part = take(planes(p.su) * p.H * 4);
+  p.cf = take(p.small ? (size_t)p.T * p.L * 4 : 0);
+  p.psq = take(p.small ? (size_t)p.T * (p.L / 256) * 4 : 0);
   // FP6 sizes (MXFP8 rows are smaller); h and the shared h are tiled (a multiple of 16 rows)
   const size_t tq = p.mfma ? (size_t)p.T : 0, cq = p.mfma ? (size_t)p.cap : 0, tq16 = (tq + 15) / 16 * 16;
   p.zq = take(tq * p.L * 3 / 2);
@@ -674,9 +677,15 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
   }
   STAGE_MARK(6);
   }
-  // a7 + a8: weighted combine and RMSNorm
-  MOE_HIP(moe::launch_combine_norm(O, p.L, p.mfma ? inv_pos : nullptr, w, p.T, p.k, (const uint16_t*)norm,
-                                   d->rms_eps, taps ? taps->c : nullptr, cn, s));
+  // a7 + a8: weighted combine and RMSNorm. Decode batches spread each token over column blocks
+  // and leave the norm's 1 / rms factor to the up-projection's output (finish_up).
+  float* cf = taps && taps->c ? taps->c : at<float>(ws, p.cf);
+  if (p.small)
+    MOE_HIP(moe::launch_combine_cols(O, p.L, p.mfma ? inv_pos : nullptr, w, p.T, p.k, (const uint16_t*)norm, cf, cn,
+                                     at<float>(ws, p.psq), s));
+  else
+    MOE_HIP(moe::launch_combine_norm(O, p.L, p.mfma ? inv_pos : nullptr, w, p.T, p.k, (const uint16_t*)norm,
+                                     d->rms_eps, taps ? taps->c : nullptr, cn, s));
   STAGE_MARK(7);
   // a9: up-projection, plus the shared output, rounded to bf16
   if (p.small) {
@@ -688,8 +697,9 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     g.nseg = 1;
     g.seg[0] = {up, p.H, 0, p.su, at<float>(ws, p.y_part)};
     MOE_HIP(moe::launch_dense_gemv(g, s));
+    const moe::RowScale rs{norm ? at<float>(ws, p.psq) : nullptr, p.L / 256, p.L, d->rms_eps};
     MOE_HIP(moe::launch_finish_up(at<float>(ws, p.y_part), p.su, p.T, p.H, shared ? ys : nullptr, (uint16_t*)y,
-                                  taps ? taps->y_routed : nullptr, s));
+                                  taps ? taps->y_routed : nullptr, rs, s));
   } else if (p.su > 1) {
     moe::GemmArgs a{};
     a.A = cn;
@@ -700,7 +710,7 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
                 p.su};
     MOE_HIP(moe::launch_gemm_bf16(a, s));
     MOE_HIP(moe::launch_finish_up(at<float>(ws, p.y_part), p.su, p.T, p.H, shared ? ys : nullptr, (uint16_t*)y,
-                                  taps ? taps->y_routed : nullptr, s));
+                                  taps ? taps->y_routed : nullptr, moe::RowScale{nullptr, 0, 0, 0.f}, s));
   } else {
     moe::GemmArgs a{};
     a.A = cn;
@@ -729,7 +739,12 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     if ((r = copy_tap(taps->expert_ids, expert_ids, (size_t)(p.cap / p.B) * 4, s))) return r;
     if ((r = copy_tap(taps->num_post, num_post, 4, s))) return r;
     if ((r = copy_tap(taps->inv_pos, inv_pos, (size_t)p.pairs * 4, s))) return r;
-    if ((r = copy_tap(taps->c_norm, cn, (size_t)p.T * p.L * 2, s))) return r;
+    if (taps->c_norm && p.small && norm) {  // the up-projection read bf16(g * c): normalise c itself
+      MOE_HIP(moe::launch_norm_from_parts(cf, at<float>(ws, p.psq), p.T, p.L, (const uint16_t*)norm, d->rms_eps,
+                                          (uint16_t*)taps->c_norm, s));
+    } else if ((r = copy_tap(taps->c_norm, cn, (size_t)p.T * p.L * 2, s))) {
+      return r;
+    }
     if (taps->O) {
       if (p.mfma)
         MOE_HIP(moe::launch_gather_rows_f32(O, p.L, inv_pos, p.pairs, taps->O, s));

@@ -97,6 +97,71 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restri
   }
 }
 
+// Decode batches: block (t, q) owns columns 256q .. 256q + 255 of token t, one per thread,
+// and sums the k slots in slot order as above. It writes c (fp32) and, for the up-projection,
+// bf16(c * g) (bf16(c) without a norm weight); with the norm it also writes the block's sum
+// of c^2 (fixed-order wave and block reduction). The 1 / rms(c) factor is applied to the
+// up-projection's output (finish_up), so no block needs another block's columns.
+__global__ __launch_bounds__(256) void combine_cols_kernel(const float* __restrict__ O, int L,
+                                                           const int32_t* __restrict__ inv_pos,
+                                                           const float* __restrict__ w, int k,
+                                                           const uint16_t* __restrict__ norm, float* __restrict__ c,
+                                                           uint16_t* __restrict__ cg, float* __restrict__ part_sq) {
+  constexpr int G = 16;
+  __shared__ int pos[kMaxSlots];
+  __shared__ float wt[kMaxSlots];
+  __shared__ float red[4];
+  const int Q = L >> 8;
+  const int t = (int)blockIdx.x / Q, qb = (int)blockIdx.x % Q;
+  if (threadIdx.x < k) {
+    const size_t f = (size_t)t * k + threadIdx.x;
+    pos[threadIdx.x] = inv_pos ? inv_pos[f] : (int)f;
+    wt[threadIdx.x] = w[f];
+  }
+  __syncthreads();
+  const int col = qb * 256 + threadIdx.x;
+  float acc = 0.f;
+  for (int j0 = 0; j0 < k; j0 += G) {
+    float v[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int j = j0 + g;
+      const int p = j < k ? pos[j] : -1;
+      v[g] = p >= 0 ? O[(size_t)p * L + col] : 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int j = j0 + g;
+      acc += (j < k ? wt[j] : 0.f) * v[g];
+    }
+  }
+  const size_t o = (size_t)t * L + col;
+  c[o] = acc;
+  cg[o] = (uint16_t)f32_to_bf16_bits(norm ? acc * bf16_bits_to_f32(norm[col]) : acc);
+  if (norm) {
+    const float ss = wave_sum(acc * acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) part_sq[(size_t)t * Q + qb] = ((red[0] + red[1]) + red[2]) + red[3];
+  }
+}
+
+// The normalised aggregate itself, bf16(c * s * g) with s = 1 / sqrt(sum of the partial sums
+// in column-block order / L + eps): the c_norm tap of the decode path.
+__global__ __launch_bounds__(256) void norm_from_parts_kernel(const float* __restrict__ c,
+                                                              const float* __restrict__ part_sq, int L,
+                                                              const uint16_t* __restrict__ norm, float eps,
+                                                              uint16_t* __restrict__ out) {
+  const int t = blockIdx.x, Q = L >> 8;
+  float tot = 0.f;
+  for (int i = 0; i < Q; ++i) tot += part_sq[(size_t)t * Q + i];
+  const float scale = rsqrtf(tot / (float)L + eps);
+  for (int col = threadIdx.x; col < L; col += 256) {
+    const size_t o = (size_t)t * L + col;
+    out[o] = (uint16_t)f32_to_bf16_bits(c[o] * scale * bf16_bits_to_f32(norm[col]));
+  }
+}
+
 // RMSNorm of bf16 rows: y = x / sqrt(mean(x^2) + eps) * g (g = 1 without a weight), one
 // block per row. Pass 1 sums the squares (each thread its columns in ascending order,
 // then a fixed-order wave and block reduction); pass 2 re-reads the row (from L2) and
@@ -172,6 +237,23 @@ hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, co
     hipLaunchKernelGGL(combine_norm_kernel<4>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
   else
     hipLaunchKernelGGL(combine_norm_kernel<8>, dim3(T), dim3(256), 0, s, O, L, inv_pos, w, k, norm, eps, c_tap, c_norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_cols(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
+                               const uint16_t* norm, float* c, uint16_t* cg, float* part_sq, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (L % 256 || k > kMaxSlots || !c || !cg || (norm && !part_sq)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_cols_kernel, dim3(T * (L / 256)), dim3(256), 0, s, O, L, inv_pos, w, k, norm, c, cg,
+                     part_sq);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_from_parts(const float* c, const float* part_sq, int T, int L, const uint16_t* norm, float eps,
+                                  uint16_t* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (L % 256 || !norm) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(norm_from_parts_kernel, dim3(T), dim3(256), 0, s, c, part_sq, L, norm, eps, out);
   return hipGetLastError();
 }
 

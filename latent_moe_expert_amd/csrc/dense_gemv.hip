@@ -189,12 +189,18 @@ __global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int bloc
 
 __global__ __launch_bounds__(256) void finish_up_kernel(const float* __restrict__ part, int splits, int M, int N,
                                                         const float* __restrict__ addend, uint16_t* __restrict__ y,
-                                                        float* __restrict__ tap) {
+                                                        float* __restrict__ tap, RowScale rs) {
   const size_t total = (size_t)M * N / 4;
   const size_t plane = (size_t)M * N;
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < splits; ++s) acc += *(const f32x4_t*)(part + s * plane + 4 * i);
+    if (rs.part_sq) {  // the row's RMSNorm factor, from its column blocks' sums of squares
+      const size_t m = 4 * i / N;
+      float tot = 0.f;
+      for (int q = 0; q < rs.nq; ++q) tot += rs.part_sq[m * rs.nq + q];
+      acc *= rsqrtf(tot / (float)rs.L + rs.eps);
+    }
     if (tap) *(f32x4_t*)(tap + 4 * i) = acc;
     if (addend) acc += *(const f32x4_t*)(addend + 4 * i);
     *(uint2*)(y + 4 * i) = uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
@@ -226,12 +232,12 @@ hipError_t launch_dense_gemv(const GemvArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_finish_up(const float* part, int splits, int M, int N, const float* addend, uint16_t* y, float* tap,
-                            hipStream_t s) {
+                            RowScale rs, hipStream_t s) {
   const size_t total = (size_t)M * N / 4;
   if (!total) return hipSuccess;
   const size_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(finish_up_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, s, part, splits,
-                     M, N, addend, y, tap);
+                     M, N, addend, y, tap, rs);
   return hipGetLastError();
 }
 

@@ -83,9 +83,15 @@ struct GemvArgs {
   int nseg;
 };
 hipError_t launch_dense_gemv(const GemvArgs& a, hipStream_t s);
-// y = bf16(sum_s part[s] + addend); tap = sum_s part[s] (fp32), both [M, N]; N % 4 == 0
+// y = bf16(r * sum_s part[s] + addend); tap = r * sum_s part[s] (fp32), both [M, N]; N % 4 == 0.
+// r = 1, or with part_sq [M, nq] the row's 1 / sqrt(sum_i part_sq[m][i] / L + eps) (sum in i order)
+struct RowScale {
+  const float* part_sq;
+  int nq, L;
+  float eps;
+};
 hipError_t launch_finish_up(const float* part, int splits, int M, int N, const float* addend, uint16_t* y, float* tap,
-                            hipStream_t s);
+                            RowScale rs, hipStream_t s);
 
 // ---------------------------------------------------------------- router
 struct RouteArgs {
@@ -217,6 +223,17 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
 // (inv_pos null) or by layout position (row = inv_pos[t * k + j])
 hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
                                const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
+
+// Decode batches: c [T, L] fp32 (required) and cg = bf16(c * g) (bf16(c) without a norm
+// weight) for the up-projection, token t's columns spread over L / 256 blocks; with the norm,
+// part_sq [T, L / 256] = each block's sum of c^2, from which finish_up applies 1 / rms(c) to
+// the up-projection's output. L % 256 == 0, k <= 64.
+hipError_t launch_combine_cols(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
+                               const uint16_t* norm, float* c, uint16_t* cg, float* part_sq, hipStream_t s);
+// out = bf16(c * s * g) per row with s = 1 / sqrt(sum(part_sq row) / L + eps) (the normalised
+// aggregate, for the c_norm tap of the decode path)
+hipError_t launch_norm_from_parts(const float* c, const float* part_sq, int T, int L, const uint16_t* norm, float eps,
+                                  uint16_t* out, hipStream_t s);
 
 // y = x / sqrt(mean(x^2) + eps) * g per row (g null: no weight); bf16 [rows, cols], cols % 4 == 0; y may be x
 hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t* g, float eps, uint16_t* y,
