@@ -35,6 +35,7 @@ __device__ __forceinline__ void split3x2(float f0, float f1, uint32_t& hi, uint3
 // in flight; a branch or a loop back edge between a load and its use makes it wait for all.
 constexpr int kRun = 8;
 constexpr int kStepBytes = 256;  // bytes of each weight row per step
+constexpr int kGemvCus = 256;    // MI355X compute units
 
 template <int MT, bool F32>
 __device__ __forceinline__ void gemv_body(const GemvArgs& args, const GemvSeg& sg, int slice, int row0, int wave,
@@ -169,18 +170,22 @@ __device__ __forceinline__ void gemv_body(const GemvArgs& args, const GemvSeg& s
     }
 }
 
-template <int MT>
-__global__ __launch_bounds__(256) void dense_gemv_kernel(GemvArgs args, int blocks0, int bands0, int bands1) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][32 * kStepBytes];
+// WPB waves per block, each 32 rows of one K slice. The waves share nothing (each has its own
+// LDS tile and no barrier). Four-wave blocks when the launch has at most one per compute unit;
+// otherwise single-wave blocks, which the dispatcher spreads evenly (with a few hundred 4-wave
+// blocks of equal bytes, some units got two blocks' work and the rest one).
+template <int MT, int WPB>
+__global__ __launch_bounds__(64 * WPB) void dense_gemv_kernel(GemvArgs args, int blocks0, int bands0, int bands1) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[WPB][32 * kStepBytes];
   const int wave = threadIdx.x >> 6;
   const bool second = (int)blockIdx.x >= blocks0;
   const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
   const GemvSeg& sg = args.seg[second ? 1 : 0];
   const int bands = second ? bands1 : bands0;
   const int band = local % bands, slice = local / bands;
-  const int row0 = (band * 4 + wave) * 32;
+  const int row0 = (band * WPB + wave) * 32;
   if (row0 >= sg.N) return;  // wave-uniform; no block barrier in this kernel
-  // block-uniform weight format, taken once outside the step loop
+  // weight format uniform over the block, taken once outside the step loop
   if (sg.w_f32)
     gemv_body<MT, true>(args, sg, slice, row0, wave, lds_all[wave]);
   else
@@ -207,14 +212,15 @@ __global__ __launch_bounds__(256) void finish_up_kernel(const float* __restrict_
   }
 }
 
+template <int WPB>
 hipError_t launch_kind(const GemvArgs& a, int blocks0, int bands0, int bands1, int total, hipStream_t s) {
   const int mt = (a.M + 15) / 16;
   if (mt <= 1)
-    hipLaunchKernelGGL(dense_gemv_kernel<1>, dim3(total), dim3(256), 0, s, a, blocks0, bands0, bands1);
+    hipLaunchKernelGGL((dense_gemv_kernel<1, WPB>), dim3(total), dim3(64 * WPB), 0, s, a, blocks0, bands0, bands1);
   else if (mt <= 2)
-    hipLaunchKernelGGL(dense_gemv_kernel<2>, dim3(total), dim3(256), 0, s, a, blocks0, bands0, bands1);
+    hipLaunchKernelGGL((dense_gemv_kernel<2, WPB>), dim3(total), dim3(64 * WPB), 0, s, a, blocks0, bands0, bands1);
   else
-    hipLaunchKernelGGL(dense_gemv_kernel<4>, dim3(total), dim3(256), 0, s, a, blocks0, bands0, bands1);
+    hipLaunchKernelGGL((dense_gemv_kernel<4, WPB>), dim3(total), dim3(64 * WPB), 0, s, a, blocks0, bands0, bands1);
   return hipGetLastError();
 }
 
@@ -228,7 +234,12 @@ hipError_t launch_dense_gemv(const GemvArgs& a, hipStream_t s) {
     bands[i] = (a.seg[i].N + 127) / 128;
     blocks[i] = bands[i] * a.seg[i].splits;
   }
-  return launch_kind(a, blocks[0], bands[0], bands[1], blocks[0] + blocks[1], s);
+  if (blocks[0] + blocks[1] <= kGemvCus) return launch_kind<4>(a, blocks[0], bands[0], bands[1], blocks[0] + blocks[1], s);
+  for (int i = 0; i < a.nseg; ++i) {
+    bands[i] = (a.seg[i].N + 31) / 32;
+    blocks[i] = bands[i] * a.seg[i].splits;
+  }
+  return launch_kind<1>(a, blocks[0], bands[0], bands[1], blocks[0] + blocks[1], s);
 }
 
 hipError_t launch_finish_up(const float* part, int splits, int M, int N, const float* addend, uint16_t* y, float* tap,
