@@ -158,6 +158,8 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
     p.su = slices(p.L, 2);
   } else if (p.mid) {
     int sp[2];
+    // the fp32 router's k-steps cost three MFMAs per fragment (its three bf16 planes): the
+    // blocks are balanced on that work (weighting its bytes instead measured slower)
     const int n1[2] = {p.L, p.E}, k1[2] = {p.H, 3 * p.H};
     moe::gemm_split_plan(p.T, 2, n1, k1, kNumCu, sp);
     p.sz = sp[0], p.sr = sp[1];
@@ -209,7 +211,7 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
   p.hsqs = take(tq * p.Is / 16);
   p.jobs = take((size_t)p.max_jobs * 16);
   p.n_jobs = take(p.mfma ? 4 : 0);
-  p.wr3 = take(p.small ? 0 : (size_t)p.E * 3 * p.H * 2);
+  p.wr3 = take(p.small || p.mid ? 0 : (size_t)p.E * 3 * p.H * 2);  // the router's bf16 planes (T >= 2048)
   p.total = o;
   return p;
 }
@@ -416,8 +418,6 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     g.seg[1] = {router->weight, p.E, 1, p.sr, at<float>(ws, p.r_part)};
     MOE_HIP(moe::launch_dense_gemv(g, s));
   } else {
-    uint16_t* wr3 = at<uint16_t>(ws, p.wr3);
-    MOE_HIP(moe::launch_split3(router->weight, p.E, p.H, wr3, s));
     moe::GemmArgs a{};
     a.A = (const uint16_t*)x;
     a.lda = p.H;
@@ -425,9 +425,16 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     a.nseg = 2;
     // segments split over K write fp32 partial planes, summed by the route launch
     a.seg[0] = {(const uint16_t*)down, p.L, p.H, p.H, p.sz > 1 ? moe::kPartF32 : moe::kStoreBf16,
-                p.sz > 1 ? (void*)at<float>(ws, p.z_part) : (void*)z, p.L, nullptr, 0, nullptr, 0, p.sz};
-    a.seg[1] = {wr3, p.E, 3 * p.H, p.H, p.sr > 1 ? moe::kPartF32 : moe::kStoreF32,
-                p.sr > 1 ? (void*)at<float>(ws, p.r_part) : (void*)logits, p.E, nullptr, 0, nullptr, 0, p.sr};
+                p.sz > 1 ? (void*)at<float>(ws, p.z_part) : (void*)z, p.L, nullptr, 0, nullptr, 0, p.sz, 0};
+    if (p.mid) {  // the 128 x 128 tile splits the fp32 router into bf16 planes as it stages it
+      a.seg[1] = {(const uint16_t*)router->weight, p.E, p.H, p.H, p.sr > 1 ? moe::kPartF32 : moe::kStoreF32,
+                  p.sr > 1 ? (void*)at<float>(ws, p.r_part) : (void*)logits, p.E, nullptr, 0, nullptr, 0, p.sr, 1};
+    } else {  // the 256 x 256 tile reads the router as three bf16 planes [E, 3H]
+      uint16_t* wr3 = at<uint16_t>(ws, p.wr3);
+      MOE_HIP(moe::launch_split3(router->weight, p.E, p.H, wr3, s));
+      a.seg[1] = {wr3, p.E, 3 * p.H, p.H, p.sr > 1 ? moe::kPartF32 : moe::kStoreF32,
+                  p.sr > 1 ? (void*)at<float>(ws, p.r_part) : (void*)logits, p.E, nullptr, 0, nullptr, 0, p.sr, 0};
+    }
     MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
   STAGE_MARK(1);

@@ -86,6 +86,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Two fp32 values split exactly into three bf16 planes each (truncation: f = hi + mid + lo, every
+// term a bf16 value, 24 significand bits = 3 x 8), packed two per dword (first value low).
+__device__ __forceinline__ void split3x2(float f0, float f1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t h0 = __float_as_uint(f0) & 0xffff0000u, h1 = __float_as_uint(f1) & 0xffff0000u;
+  const float r0 = f0 - __uint_as_float(h0), r1 = f1 - __uint_as_float(h1);
+  const uint32_t m0 = __float_as_uint(r0) & 0xffff0000u, m1 = __float_as_uint(r1) & 0xffff0000u;
+  const float l0 = r0 - __uint_as_float(m0), l1 = r1 - __uint_as_float(m1);
+  hi = (h0 >> 16) | h1;
+  mid = (m0 >> 16) | m1;
+  lo = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xffff0000u);
+}
+
 // Streaming 16-byte load that bypasses nothing but marks the data as read-once.
 __device__ __forceinline__ u32x4_t load_nt_u32x4(const void* p) {
   return __builtin_nontemporal_load((const u32x4_t*)p);

@@ -19,16 +19,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ void split3x2(float f0, float f1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  const uint32_t h0 = __float_as_uint(f0) & 0xffff0000u, h1 = __float_as_uint(f1) & 0xffff0000u;
-  const float r0 = f0 - __uint_as_float(h0), r1 = f1 - __uint_as_float(h1);
-  const uint32_t m0 = __float_as_uint(r0) & 0xffff0000u, m1 = __float_as_uint(r1) & 0xffff0000u;
-  const float l0 = r0 - __uint_as_float(m0), l1 = r1 - __uint_as_float(m1);
-  hi = (h0 >> 16) | h1;
-  mid = (m0 >> 16) | m1;
-  lo = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xffff0000u);
-}
-
 // Steps of a slice run in blocks of kRun straight-line steps through a ring of three register
 // stages. Every step issues its loads (a step past the slice reads zeros from a zero-size
 // resource), so no load sits under a branch and the compiler's waits count exactly the loads

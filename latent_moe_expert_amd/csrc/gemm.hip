@@ -66,6 +66,10 @@ __device__ __forceinline__ void dma16g(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wa
 // LDS position of 16-byte chunk c (0..7) of tile row r
 __host__ __device__ constexpr int g_pos(int c, int r) { return c ^ ((r >> 1) & 7); }
 
+// LDS position of 16-byte chunk c (0..3) of a 64-byte tile row r: rows 4 apart share a bank
+// cycle, so the chunk is XOR-rotated by (r / 4) % 4
+__host__ __device__ constexpr int g_pos2(int c, int r) { return c ^ ((r >> 2) & 3); }
+
 // One of the two segments as a value, chosen field by field (a select between references to
 // the kernel argument makes the compiler copy the arguments to scratch and index them there).
 __device__ __forceinline__ GemmSeg pick_seg(const GemmArgs& a, bool second) {
@@ -84,6 +88,7 @@ __device__ __forceinline__ GemmSeg pick_seg(const GemmArgs& a, bool second) {
   r.tap = second ? y.tap : x.tap;
   r.ld_tap = second ? y.ld_tap : x.ld_tap;
   r.splits = second ? y.splits : x.splits;
+  r.w_f32 = second ? y.w_f32 : x.w_f32;
   return r;
 }
 
@@ -132,94 +137,139 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   const int mt = grp * kGM + rem % gm, nt = rem / gm;
   const int m0 = mt * kBM, n0 = nt * kBN;
   const int K = sg.K, kwrap = sg.kwrap;
-  // this block's k-steps: [kb0, kb0 + nks) (a K slice, or all of K)
-  const int nks_all = K / kBK, nsl = max(1, sg.splits);
-  const int kper = (nks_all + nsl - 1) / nsl;
-  const int kb0 = slice * kper;
-  const int nks = max(0, min(nks_all, kb0 + kper) - kb0);
-
-  // ---- LDS-DMA of one k-step: chunk t = tid + 256 i; i < 4: A, else W; row t/8 of the
-  // tile (t taken mod 1024), LDS position t % 8, global chunk g_pos^-1 = same XOR
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, (uint32_t)args.M * (uint32_t)args.lda * 2u);
-  const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * (uint32_t)K * 2u);
-  const __amdgpu_buffer_rsrc_t none = make_rsrc(sg.W, 0u);
-  uint32_t goff[kGemmDma];
-#pragma unroll
-  for (int i = 0; i < kGemmDma; ++i) {
-    const int t = (tid + 256 * i) & 1023, r = t >> 3, pos = t & 7;
-    const int c = g_pos(pos, r);  // the XOR is its own inverse
-    if (i < 4) {
-      const int row = m0 + r;
-      goff[i] = row < args.M ? ((uint32_t)row * (uint32_t)args.lda + 8u * c) * 2u : kOob;
-    } else {
-      const int row = n0 + r;
-      goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
-    }
-  }
-  auto dma = [&](uint8_t* st, int j, bool on) {  // kGemmDma loads of the block's k-step j
-    const int ks = kb0 + j;
-    const uint32_t ka = (uint32_t)((ks * kBK) % kwrap) * 2u, kw = (uint32_t)(ks * kBK) * 2u;
-#pragma unroll
-    for (int i = 0; i < kGemmDma; ++i)
-      dma16g(on ? (i < 4 ? a_rs : w_rs) : none, st + (i < 4 ? 0 : kTile) + (i & 3) * 4096 + wave * 1024, goff[i],
-             i < 4 ? ka : kw);
-  };
-
-  // fragment reads: lane (nl, q) of A tile mi reads row 64 wm + 16 mi + nl, chunk 4 kk + q
-  uint32_t ard[2], brd[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    ard[kk] = (uint32_t)((wm * 64 + nl) * 128 + g_pos(4 * kk + q, nl) * 16);
-    brd[kk] = (uint32_t)(kTile + (wn * 64 + nl) * 128 + g_pos(4 * kk + q, nl) * 16);
-  }
+  // The ring, shared by both weight formats. K-step ks reads stage ks % 4; it issues the loads
+  // of ks + 3 into the stage read by ks - 1, then waits for stage ks + 1 (issued in ks - 2: two
+  // k-steps' loads follow it). Steps past nks load zeros (a K slice need not be a multiple of 4
+  // steps). bf16 weights: k-steps of 64 K, A and W rows of 128 bytes (4 + 4 loads per thread).
+  // fp32 weights: k-steps of 32 K, A rows of 64 bytes and W rows of 128 bytes (2 + 4 loads);
+  // each fp32 fragment pair is split exactly into three bf16 planes, one MFMA each.
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto core = [&](auto F32_) {
+    constexpr bool F32 = decltype(F32_)::value;
+    constexpr int kKs = F32 ? 32 : 64;        // K values per k-step
+    constexpr int kAL = F32 ? 2 : 4;          // A loads per thread per k-step
+    constexpr int kDma = kAL + 4;             // + 4 W loads
+    constexpr uint32_t kWes = F32 ? 4u : 2u;  // bytes per weight
+    // this block's k-steps: [kb0, kb0 + nks) (a K slice, or all of K)
+    const int nks_all = K / kKs, nsl = max(1, sg.splits);
+    const int kper = (nks_all + nsl - 1) / nsl;
+    const int kb0 = slice * kper;
+    const int nks = max(0, min(nks_all, kb0 + kper) - kb0);
 
-  auto compute = [&](const uint8_t* st) {
+    // LDS-DMA of one k-step: A chunk t = tid + 256 i (i < kAL) is row t / (kKs / 8) of the A
+    // tile at LDS byte 16 t; W chunk t = tid + 256 i is row t / 8 of the W tile at byte
+    // kTile + 16 t; the global chunk of each LDS position undoes the XOR (its own inverse).
+    const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, (uint32_t)args.M * (uint32_t)args.lda * 2u);
+    const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * (uint32_t)K * kWes);
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(sg.W, 0u);
+    uint32_t goff[kDma];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4_t av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = *(const u32x4_t*)(st + ard[kk] + i * 16 * 128);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = *(const u32x4_t*)(st + brd[kk] + j * 16 * 128);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+    for (int i = 0; i < kDma; ++i) {
+      if (i < kAL) {
+        const int t = tid + 256 * i;
+        const int r = F32 ? t >> 2 : t >> 3, pos = F32 ? t & 3 : t & 7;
+        const int c = F32 ? g_pos2(pos, r) : g_pos(pos, r);
+        const int row = m0 + r;
+        goff[i] = row < args.M ? ((uint32_t)row * (uint32_t)args.lda + 8u * c) * 2u : kOob;
+      } else {
+        const int t = tid + 256 * (i - kAL), r = t >> 3, pos = t & 7;
+        const int c = g_pos(pos, r);
+        const int row = n0 + r;
+        goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + (16u / kWes) * c) * kWes : kOob;
+      }
     }
-  };
-
-  // ring: k-step ks reads stage ks % 4; it issues the loads of ks + 3 into the stage read
-  // by ks - 1, then waits for stage ks + 1 (issued in ks - 2: 2 x 8 loads follow it). Steps
-  // past nks load zeros (a K slice need not be a multiple of 4 steps).
-  dma(stage(icg<0>{}), 0, nks > 0);
-  dma(stage(icg<1>{}), 1, nks > 1);
-  dma(stage(icg<2>{}), 2, nks > 2);
-  MOE_GEMM_WAIT_VM_LGKM0(2 * kGemmDma);
-  gemm_barrier();
-  for (int k4 = 0; k4 < nks; k4 += 4) {
-    auto step = [&](auto S_) {
-      constexpr int S = decltype(S_)::value;
-      const int ks = k4 + S;
-      dma(stage(icg<S + 3>{}), ks + 3, ks + 3 < nks);
-      issue_fence();
-      compute(stage(S_));
-      MOE_GEMM_WAIT_VM_LGKM0(2 * kGemmDma);
-      gemm_barrier();
+    auto dma = [&](uint8_t* st, int j, bool on) {  // kDma loads of the block's k-step j
+      const int ks = kb0 + j;
+      const uint32_t ka = (uint32_t)((ks * kKs) % kwrap) * 2u, kw = (uint32_t)(ks * kKs) * kWes;
+#pragma unroll
+      for (int i = 0; i < kDma; ++i)
+        dma16g(on ? (i < kAL ? a_rs : w_rs) : none,
+               st + (i < kAL ? 0 : kTile) + (i < kAL ? i : i - kAL) * 4096 + wave * 1024, goff[i],
+               i < kAL ? ka : kw);
     };
-    step(icg<0>{});
-    step(icg<1>{});
-    step(icg<2>{});
-    step(icg<3>{});
-  }
-  // the last k-steps issued zero-filling loads into the ring: they must land before the
-  // block ends and its LDS goes to another block
-  MOE_GEMM_WAIT_VM_LGKM0(0);
+
+    auto compute = [&](const uint8_t* st) {
+      if constexpr (!F32) {
+        // lane (nl, q) of A tile mi reads row 64 wm + 16 mi + nl, chunk 4 kk + q
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint32_t ard = (uint32_t)((wm * 64 + nl) * 128 + g_pos(4 * kk + q, nl) * 16);
+          const uint32_t brd = (uint32_t)(kTile + (wn * 64 + nl) * 128 + g_pos(4 * kk + q, nl) * 16);
+          u32x4_t av[4], bv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[i] = *(const u32x4_t*)(st + ard + i * 16 * 128);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bv[j] = *(const u32x4_t*)(st + brd + j * 16 * 128);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+        }
+      } else {
+        // A: row 64 wm + 16 mi + nl of 64-byte rows, chunk q (K 8q .. 8q + 7); W: the same K of
+        // row 64 wn + 16 nj + nl as fp32, chunks 2q and 2q + 1 of its 128-byte row
+        const uint32_t ard = (uint32_t)((wm * 64 + nl) * 64 + g_pos2(q, nl) * 16);
+        const uint32_t brd0 = (uint32_t)(kTile + (wn * 64 + nl) * 128 + g_pos(2 * q, nl) * 16);
+        const uint32_t brd1 = (uint32_t)(kTile + (wn * 64 + nl) * 128 + g_pos(2 * q + 1, nl) * 16);
+        u32x4_t av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = *(const u32x4_t*)(st + ard + i * 16 * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t w0 = *(const u32x4_t*)(st + brd0 + j * 16 * 128);
+          const u32x4_t w1 = *(const u32x4_t*)(st + brd1 + j * 16 * 128);
+          uint32_t h4[4], m4[4], l4[4];
+          split3x2(__uint_as_float(w0[0]), __uint_as_float(w0[1]), h4[0], m4[0], l4[0]);
+          split3x2(__uint_as_float(w0[2]), __uint_as_float(w0[3]), h4[1], m4[1], l4[1]);
+          split3x2(__uint_as_float(w1[0]), __uint_as_float(w1[1]), h4[2], m4[2], l4[2]);
+          split3x2(__uint_as_float(w1[2]), __uint_as_float(w1[3]), h4[3], m4[3], l4[3]);
+          const u32x4_t hi = {h4[0], h4[1], h4[2], h4[3]};
+          const u32x4_t mi = {m4[0], m4[1], m4[2], m4[3]};
+          const u32x4_t lo = {l4[0], l4[1], l4[2], l4[3]};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(hi), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(mi), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(lo), acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    dma(stage(icg<0>{}), 0, nks > 0);
+    dma(stage(icg<1>{}), 1, nks > 1);
+    dma(stage(icg<2>{}), 2, nks > 2);
+    MOE_GEMM_WAIT_VM_LGKM0(2 * kDma);
+    gemm_barrier();
+    for (int k4 = 0; k4 < nks; k4 += 4) {
+      auto step = [&](auto S_) {
+        constexpr int S = decltype(S_)::value;
+        const int ks = k4 + S;
+        dma(stage(icg<S + 3>{}), ks + 3, ks + 3 < nks);
+        issue_fence();
+        compute(stage(S_));
+        MOE_GEMM_WAIT_VM_LGKM0(2 * kDma);
+        gemm_barrier();
+      };
+      step(icg<0>{});
+      step(icg<1>{});
+      step(icg<2>{});
+      step(icg<3>{});
+    }
+    // the last k-steps issued zero-filling loads into the ring: they must land before the
+    // block ends and its LDS goes to another block
+    MOE_GEMM_WAIT_VM_LGKM0(0);
+  };
+  if (sg.w_f32)
+    core(std::true_type{});
+  else
+    core(std::false_type{});
 
   // epilogue: lane holds D[m = 4q + r][n = nl] of each 16 x 16 tile. Rows past M and
   // columns past N are skipped; all addend loads are issued before any store.
@@ -292,9 +342,6 @@ constexpr int kTile2 = kBM2 * kBK2 * 2;            // 16 KB: one operand tile of
 constexpr int kDma2 = 2 * kTile2 / 16 / 512;       // 16-byte LDS-DMA chunks per thread per k-step
 static_assert(kDma2 == 4, "");
 
-// LDS position of 16-byte chunk c (0..3) of a 64-byte tile row r: rows 4 apart share a bank
-// cycle, so the chunk is XOR-rotated by (r / 4) % 4
-__host__ __device__ constexpr int g_pos2(int c, int r) { return c ^ ((r >> 2) & 3); }
 
 __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t sa0[2 * kTile2];
@@ -520,8 +567,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   for (int i = 0; i < a.nseg; ++i) {
     const GemmSeg& g = a.seg[i];
     if (g.K % (4 * kBK) || g.kwrap % kBK || g.kwrap > a.lda || g.K % g.kwrap || g.N <= 0) return hipErrorInvalidValue;
-    if ((long long)g.N * g.K * 2 >= (1ll << 31)) return hipErrorInvalidValue;
-    if (g.splits < 0 || g.splits > g.K / bk || (g.mode == kPartF32) != (g.splits > 1)) return hipErrorInvalidValue;
+    if ((long long)g.N * g.K * (g.w_f32 ? 4 : 2) >= (1ll << 31)) return hipErrorInvalidValue;
+    if (g.w_f32 && (big || g.kwrap != g.K)) return hipErrorInvalidValue;  // fp32 weights: the 128 x 128 tile
+    if (g.splits < 0 || g.splits > g.K / (g.w_f32 ? 32 : bk) || (g.mode == kPartF32) != (g.splits > 1))
+      return hipErrorInvalidValue;
     split |= g.splits > 1;
     blocks += tm * ((g.N + bn - 1) / bn) * (g.splits > 1 ? g.splits : 1);
   }
