@@ -166,4 +166,109 @@ __device__ __forceinline__ void route_select_fast(const float (&lg)[4], const fl
   }
 }
 
+
+// ---- One wave per token: up to 64 * NPL experts (expert e = lane + 64 i in register i).
+//
+// The k-th largest of the 64 lane maxima, tau, bounds the k-th largest composite from below
+// (k lanes hold a composite >= tau), so the k winners are among the composites >= tau. Those
+// are compacted into 64 LDS slots (usually a few dozen) and bitonic-sorted across the wave;
+// when more than 64 reach tau, k successive wave maxima over all composites are taken instead.
+// The selected set is the same as route_select_fast's (the k largest unique composites), and
+// the winners are written the same way.
+
+// lane ^ X within the wave: DPP for 1, 2 and 8 (quad permutations, row rotation by 8),
+// ds_swizzle for 4 and 16, a permute for 32
+template <int X>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  if constexpr (X == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+  else if constexpr (X == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+  else if constexpr (X == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+  else if constexpr (X == 4 || X == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (X << 10));
+  else return (uint32_t)__shfl_xor((int)v, X, 64);
+}
+
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ unsigned long long bitonic_step_u64(unsigned long long v, int lane) {
+  const uint32_t lo = xor_lane_u32<STRIDE>((uint32_t)v);
+  const uint32_t hi = xor_lane_u32<STRIDE>((uint32_t)(v >> 32));
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  // the lower lane of a pair keeps the larger value in a descending run (lane & SIZE == 0)
+  const bool keep_max = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);
+  return (keep_max == (o > v)) ? o : v;
+}
+
+// One composite per lane, returned sorted descending across the 64 lanes.
+template <int SIZE = 2, int STRIDE = 1>
+__device__ __forceinline__ unsigned long long wave_sort_desc_u64(unsigned long long v, int lane) {
+  if constexpr (SIZE > 64) {
+    return v;
+  } else {
+    v = bitonic_step_u64<SIZE, STRIDE>(v, lane);
+    if constexpr (STRIDE > 1)
+      return wave_sort_desc_u64<SIZE, STRIDE / 2>(v, lane);
+    else
+      return wave_sort_desc_u64<SIZE * 2, SIZE>(v, lane);
+  }
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct RouteWaveSmem {
+  unsigned long long cand[64];
+  int sel_e[kFastMaxK];
+  float sel_s[kFastMaxK];
+};
+
+// Top-k (k <= kFastMaxK) of one token's composites c (zero past E) with their unbiased scores
+// sc; writes the winners in ascending id order with weights s_e / sum(s_selected) * rsf, the
+// sum taken in ascending id order. s_lds holds the wave's scores by expert id afterwards.
+template <int NPL>
+__device__ __forceinline__ void route_select_wave(unsigned long long (&c)[NPL], const float (&sc)[NPL], int k,
+                                                  float rsf, int lane, float* __restrict__ s_lds,
+                                                  RouteWaveSmem& sm, int32_t* __restrict__ ids_out,
+                                                  float* __restrict__ w_out) {
+  unsigned long long m = c[0];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    s_lds[lane + 64 * i] = sc[i];
+    if (i) m = max_u64(m, c[i]);
+  }
+  const unsigned long long tau = readlane_u64(wave_sort_desc_u64(m, lane), k - 1);
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool cand = c[i] >= tau;  // tau is a real composite: padding (zero) never qualifies
+    const unsigned long long b = __ballot(cand);
+    const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+    if (cand && pos < 64) sm.cand[pos] = c[i];
+    n += __popcll(b);
+  }
+  wave_sync_lds();
+  unsigned long long my_c;
+  if (n <= 64) {
+    my_c = wave_sort_desc_u64(lane < n ? sm.cand[lane] : 0ull, lane);
+  } else {
+    float unused;
+    wave_top<NPL>(c, sc, k, lane, my_c, unused);
+  }
+  const int my_e = (int)(0xffffffffu - (uint32_t)(my_c & 0xffffffffull));
+  if (lane < k) {
+    int p = 0;
+    for (int j = 0; j < k; ++j) p += __builtin_amdgcn_readlane(my_e, j) < my_e ? 1 : 0;
+    sm.sel_e[p] = my_e;
+    sm.sel_s[p] = s_lds[my_e];
+  }
+  wave_sync_lds();
+  float tot = 0.f;
+  for (int p = 0; p < k; ++p) tot += sm.sel_s[p];  // ascending id order: a fixed rounding order
+  if (lane < k) {
+    ids_out[lane] = sm.sel_e[lane];
+    w_out[lane] = sm.sel_s[lane] / tot * rsf;
+  }
+}
+
 }  // namespace moe

@@ -259,6 +259,41 @@ __global__ __launch_bounds__(256) void route_radix_kernel(RouteArgs a) {
   }
 }
 
+// One token per wave, four per block (E <= 64 * NPL <= kFastMaxE, k <= kFastMaxK): the waves
+// share nothing but the block's LDS arrays, each its own part, and need no block barrier.
+template <int NPL>
+__global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
+  __shared__ float s_lds[4][64 * NPL];
+  __shared__ RouteWaveSmem sm[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = (int)blockIdx.x * 4 + wave;
+  if (t >= a.T) return;  // wave-uniform
+  const int E = a.E;
+  // every load is issued before any is used; experts past E read as zeros
+  const __amdgpu_buffer_rsrc_t lg_rs = make_rsrc(a.logits + (size_t)t * E, (uint32_t)E * 4);
+  const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(a.bias, a.bias ? (uint32_t)E * 4 : 0u);
+  float lg[NPL], bs[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const uint32_t off = (uint32_t)(lane + 64 * i) * 4;
+    lg[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lg_rs, off, 0, 0));
+    bs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs_rs, off, 0, 0));
+  }
+  unsigned long long c[NPL];
+  float sc[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    const float sg = sigmoidf_dev(lg[i]);
+    float kv = sg + bs[i];
+    kv = (kv == kv) ? kv : -FLT_MAX;  // a NaN key ranks below every real key
+    c[i] = e < E ? ((unsigned long long)ordered_bits(kv) << 32) | (0xffffffffu - (uint32_t)e) : 0ull;
+    sc[i] = e < E ? sg : 0.f;
+  }
+  route_select_wave<NPL>(c, sc, a.k, a.rsf, lane, s_lds[wave], sm[wave], a.ids + (size_t)t * a.k,
+                         a.w + (size_t)t * a.k);
+}
+
 // One token per block (E <= kFastMaxE, k <= kFastMaxK).
 __global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
   __shared__ RouteFastSmem sm;
@@ -269,17 +304,26 @@ __global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
 
 // Decode batches with split-K planes (E <= kFastMaxE, k <= kFastMaxK): one launch. Blocks
 // 0..T-1 each sum their token's logits over the slices (slice order, as reduce_planes does),
-// keep them in registers for the selection and store them; the blocks after them sum the
-// latent rows.
+// store them, and form the keys, which one wave of the block then selects from; the blocks
+// after them sum the latent rows.
 __global__ __launch_bounds__(256) void route_fast_planes_kernel(RouteArgs a) {
-  __shared__ RouteFastSmem sm;
+  __shared__ unsigned long long c_lds[kFastMaxE];
+  __shared__ float s_lds[kFastMaxE];
+  __shared__ RouteWaveSmem wsm;
   const int t = blockIdx.x;
   if (t >= a.T) {
     const size_t nz = (size_t)a.T * a.L / 4;
     for (size_t i = (size_t)(t - a.T) * 256 + threadIdx.x; i < nz; i += (size_t)(gridDim.x - a.T) * 256) sum_z_group(a, i);
     return;
   }
-  const size_t rplane = (size_t)a.T * a.E, row = (size_t)t * a.E;
+  const int E = a.E;
+  const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(a.bias, a.bias ? (uint32_t)E * 4 : 0u);
+  float bs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    bs[i] = __builtin_bit_cast(float,
+                               __builtin_amdgcn_raw_buffer_load_b32(bs_rs, (uint32_t)(threadIdx.x + 256 * i) * 4, 0, 0));
+  const size_t rplane = (size_t)a.T * E, row = (size_t)t * E;
   float lg[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.sr; s0 += 8) {
     float v[8][4];
@@ -288,19 +332,38 @@ __global__ __launch_bounds__(256) void route_fast_planes_kernel(RouteArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = threadIdx.x + 256 * i;
-        v[u][i] = s0 + u < a.sr && e < a.E ? a.r_part[(s0 + u) * rplane + row + e] : 0.f;
+        v[u][i] = s0 + u < a.sr && e < E ? a.r_part[(s0 + u) * rplane + row + e] : 0.f;
       }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lg[i] += v[u][i];
   }
+  // keys in the summing layout (expert tid + 256 i), handed to one wave through LDS
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = threadIdx.x + 256 * i;
-    if (e < a.E) a.logits_out[row + e] = lg[i];
+    if (e < E) {
+      a.logits_out[row + e] = lg[i];
+      const float sg = sigmoidf_dev(lg[i]);
+      float kv = sg + bs[i];
+      kv = (kv == kv) ? kv : -FLT_MAX;  // a NaN key ranks below every real key
+      c_lds[e] = ((unsigned long long)ordered_bits(kv) << 32) | (0xffffffffu - (uint32_t)e);
+      s_lds[e] = sg;
+    }
   }
-  route_select_fast(lg, a.bias, a.E, a.k, a.rsf, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, sm);
+  __syncthreads();
+  if (threadIdx.x >= 64) return;  // one wave selects
+  const int lane = threadIdx.x;
+  unsigned long long c[16];
+  float sc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    c[i] = e < E ? c_lds[e] : 0ull;
+    sc[i] = e < E ? s_lds[e] : 0.f;
+  }
+  route_select_wave<16>(c, sc, a.k, a.rsf, lane, s_lds, wsm, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k);
 }
 
 }  // namespace
@@ -319,8 +382,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(reduce_planes_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, a);
   }
   if (a.k > 64) return hipErrorInvalidValue;
-  if (a.E <= kFastMaxE && a.k <= kFastMaxK)
-    hipLaunchKernelGGL(route_fast_kernel, dim3(a.T), dim3(256), 0, s, a);
+  if (a.E <= kFastMaxE && a.k <= kFastMaxK) {
+    const dim3 grid((unsigned)((a.T + 3) / 4));
+    if (a.E <= 128)
+      hipLaunchKernelGGL(route_wave_kernel<2>, grid, dim3(256), 0, s, a);
+    else if (a.E <= 256)
+      hipLaunchKernelGGL(route_wave_kernel<4>, grid, dim3(256), 0, s, a);
+    else if (a.E <= 512)
+      hipLaunchKernelGGL(route_wave_kernel<8>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(route_wave_kernel<16>, grid, dim3(256), 0, s, a);
+  }
   else if (a.E <= kMaxE)
     hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(256), 0, s, a);
   else

@@ -249,6 +249,11 @@ def test_moe_align_block_size_bit_exact_on_oracle_ids(T, k, E, B, seed):
 
 
 @pytest.mark.parametrize("T,E,k", [(50, 64, 8),
+                                   # one wave per token, 2 / 4 / 8 / 16 keys per lane
+                                   (37, 100, 6), (200, 256, 16), (130, 500, 16), (300, 896, 16),
+                                   (65, 1024, 16),
+                                   # 17 to 4096 experts or k above 16: the LDS bitonic sort
+                                   (40, 300, 24),
                                    # above 4096 experts: the radix-select router
                                    (20, 5000, 16), (6, 65535, 64)])
 def test_moe_route_entry_point(T, E, k):
@@ -298,6 +303,48 @@ def test_decode_route_exact_ties(E, n_top):
     assert int(out["num_post"][0]) == n
     assert np.array_equal(out["sorted_ids"][:n], ref["sorted_ids"][:n])
     assert np.array_equal(out["inv_pos"], ref["inv_pos"])
+
+
+@pytest.mark.parametrize("E,case", [(128, "tied"), (896, "tied"), (896, "biased"), (1024, "biased"),
+                                    (1024, "over_64_candidates"), (300, "over_64_candidates")])
+def test_route_entry_exact_ties(E, case):
+    """moe_route with a zero router (every score 0.5) and a selection bias that ties keys
+    exactly: the 16 lowest ids among the largest keys win, each with weight 1/16.
+    "over_64_candidates": the 16 lanes holding experts e % 64 < 16 get biases 2 + 0.01 * (e % 64),
+    equal within a lane, so the keys at or above the 16th-largest lane maximum number more than
+    64 and the one-wave router takes its successive-maxima path; the winners are all the experts
+    with e % 64 == 15 (the largest key), lowest ids first."""
+    from latent_moe_expert_amd import layer as L
+    H = _harness()
+    T, k = 70, 16
+    c = li.small_config(T=T, n_experts=E, topk=k, hidden=256, latent=256, inter=256, shared_inter=0)
+    d = li.build(c, experts=False)
+    bias = np.zeros(E, np.float32)
+    if case == "biased":
+        top = np.sort(np.random.default_rng(E).choice(E, size=40, replace=False))
+        bias[top] = 1.0
+        want = top[:k]
+    elif case == "over_64_candidates":
+        e = np.arange(E)
+        lanes = e % 64
+        bias[lanes < 16] = (2.0 + 0.01 * lanes[lanes < 16]).astype(np.float32)
+        want = e[lanes == 15][:k]
+        assert len(want) == k or E < 64 * k
+    else:
+        want = np.arange(k)
+    dims = L.make_dims(c.T, c.hidden, c.latent, c.n_experts, c.inter, c.shared_inter)
+    x = H.to_dev_bf16(d["x"])
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    router = torch.zeros((E, c.hidden), dtype=torch.float32, device="cuda")
+    L.moe_route(dims, x, router, torch.from_numpy(bias).cuda(), k, ids, w, lg)
+    torch.cuda.synchronize()
+    if len(want) < k:  # fewer experts with the largest key than k: the next lane's follow
+        order = sorted(range(E), key=lambda i: (-float(np.float32(0.5) + bias[i]), i))
+        want = np.sort(np.array(order[:k]))
+    assert (ids.cpu().numpy() == np.asarray(want, np.int32)[None, :]).all()
+    assert (w.cpu().numpy() == np.float32(1.0 / k)).all()
 
 
 def test_route_dump_appends_each_forward(tmp_path, monkeypatch):
