@@ -49,13 +49,24 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, in
                                                           int32_t* __restrict__ num_post) {
   __shared__ int part[1024];
   const int tid = threadIdx.x;
-  // per-expert prefix over chunks
+  // per-expert prefix over chunks, 16 chunks' loads in flight at a time (a load past the
+  // last chunk reads zero from the buffer resource, so none of them sits under a branch)
+  constexpr int kBatch = 16;
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_cnt[(size_t)c * E + e];
-      chunk_cnt[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      // this batch's rows only (kBatch * E * 4 bytes < 2^32 for E <= 65535)
+      const __amdgpu_buffer_rsrc_t cc =
+          make_rsrc(chunk_cnt + (size_t)c0 * E, (uint32_t)min(kBatch, nchunks - c0) * (uint32_t)E * 4u);
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b32(cc, ((uint32_t)u * (uint32_t)E + (uint32_t)e) * 4u, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c0 + u < nchunks) chunk_cnt[(size_t)(c0 + u) * E + e] = run;
+        run += v[u];
+      }
     }
     counts[e] = run;
   }
@@ -167,20 +178,23 @@ __global__ __launch_bounds__(256) void align_scatter_hash_kernel(const int32_t* 
   }
 }
 
-// All T tokens in one chunk (T <= 64): masks, counts, scan, padding and scatter
-// in a single block, so decode pays one launch instead of three.
+// Batches of up to kFewChunks chunks (T <= 64 * kFewChunks) in a single block: masks, counts,
+// scan, padding and scatter, so small batches pay one launch instead of three.
+constexpr int kFewChunks = 8;
+constexpr size_t kFewLds = 64 * 1024;  // dynamic LDS for the masks and the expert offsets
+
 __global__ __launch_bounds__(1024) void align_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                            int B, int cap, int32_t* __restrict__ counts,
+                                                            int B, int cap, int nc, int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ sorted_ids,
                                                             int32_t* __restrict__ expert_ids,
                                                             int32_t* __restrict__ num_post,
                                                             int32_t* __restrict__ inv_pos) {
-  extern __shared__ unsigned long long mask[];      // [E]
-  int* offs = (int*)(mask + E);                      // [E]
+  extern __shared__ unsigned long long mask[];      // [nc * E]
+  int* offs = (int*)(mask + (size_t)nc * E);         // [E]
   __shared__ int part[1024];
   __shared__ int32_t ids_l[kIdsLds];
-  align_one_chunk<1024>(ids, T, k, E, B, cap, counts, sorted_ids, expert_ids, num_post, inv_pos, mask, offs, part,
-                        ids_l);
+  align_chunks<1024>(ids, T, k, E, B, cap, nc, counts, sorted_ids, expert_ids, num_post, inv_pos, mask, offs, part,
+                     ids_l);
 }
 
 }  // namespace
@@ -213,9 +227,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int B, int32_t*
                          sorted_ids, inv_pos);
     return hipGetLastError();
   }
-  if (nchunks <= 1) {
-    hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(1024), lds + (size_t)E * sizeof(int), s, ids, T, k, E, B,
-                       cap, counts, sorted_ids, expert_ids, num_post, inv_pos);
+  const size_t few = (size_t)nchunks * lds + (size_t)E * sizeof(int);
+  if (nchunks <= 1 || (nchunks <= kFewChunks && few <= kFewLds)) {
+    const int nc = nchunks > 1 ? nchunks : 1;
+    hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(1024), (size_t)nc * lds + (size_t)E * sizeof(int), s, ids,
+                       T, k, E, B, cap, nc, counts, sorted_ids, expert_ids, num_post, inv_pos);
     return hipGetLastError();
   }
   if (nchunks > 0) hipLaunchKernelGGL(align_count_kernel, dim3(nchunks), dim3(256), lds, s, ids, T, k, E, chunk);

@@ -82,22 +82,34 @@ __device__ __forceinline__ void build_masks_hash(const int32_t* __restrict__ ids
   __syncthreads();
 }
 
-// All T <= 64 tokens in one chunk, by one block of NT threads: masks, counts, the scan over
-// experts, padding and scatter. mask and offs hold E entries, part NT, ids_l kIdsLds.
+// All T <= 64 * nc tokens in one block of NT threads: the nc chunks' masks, counts, the scan
+// over experts, padding and scatter. mask holds nc * E entries (chunk-major), offs E, part NT,
+// ids_l kIdsLds. A slot's rank inside its expert is the popcounts of the earlier chunks' masks
+// plus popcount(mask & lower tokens) in its own chunk, as in the multi-block form.
 template <int NT>
-__device__ __forceinline__ void align_one_chunk(const int32_t* __restrict__ ids, int T, int k, int E, int B, int cap,
-                                                int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
-                                                int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_post,
-                                                int32_t* __restrict__ inv_pos, unsigned long long* mask, int* offs,
-                                                int* part, int32_t* ids_l) {
+__device__ __forceinline__ void align_chunks(const int32_t* __restrict__ ids, int T, int k, int E, int B, int cap,
+                                             int nc, int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
+                                             int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_post,
+                                             int32_t* __restrict__ inv_pos, unsigned long long* mask, int* offs,
+                                             int* part, int32_t* ids_l) {
   const int tid = threadIdx.x;
-  build_masks(ids, T, k, E, 0, mask, ids_l);
   const int pairs = T * k;
+  const bool stage = pairs <= kIdsLds;
+  for (int i = tid; i < nc * E; i += NT) mask[i] = 0ull;
+  __syncthreads();
+  for (int i = tid; i < pairs; i += NT) {
+    const int e = ids[i];
+    if (stage) ids_l[i] = e;
+    const int t = i / k;
+    if (e >= 0 && e < E) atomicOr(&mask[(t >> 6) * E + e], 1ull << (t & 63));
+  }
+  __syncthreads();
   const int per = (E + NT - 1) / NT;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int local = 0;
   for (int e = e0; e < e1; ++e) {
-    const int c = __popcll(mask[e]);
+    int c = 0;
+    for (int q = 0; q < nc; ++q) c += __popcll(mask[q * E + e]);
     counts[e] = c;
     local += (c + B - 1) / B * B;
   }
@@ -112,7 +124,8 @@ __device__ __forceinline__ void align_one_chunk(const int32_t* __restrict__ ids,
   int run = part[tid] - local;
   for (int e = e0; e < e1; ++e) {
     offs[e] = run;
-    const int c = __popcll(mask[e]);
+    int c = 0;
+    for (int q = 0; q < nc; ++q) c += __popcll(mask[q * E + e]);
     const int p = (c + B - 1) / B * B;
     for (int b = 0; b < p / B; ++b) expert_ids[run / B + b] = e;
     for (int i = c; i < p; ++i) sorted_ids[run + i] = pairs;
@@ -124,14 +137,16 @@ __device__ __forceinline__ void align_one_chunk(const int32_t* __restrict__ ids,
   for (int b = total / B + tid; b < cap / B; b += NT) expert_ids[b] = -1;
   __syncthreads();
   for (int i = tid; i < pairs; i += NT) {
-    const int e = ids[i];
-    const int tl = i / k;
-    if (e < 0 || e >= E || repeated_in_token(ids_l + tl * k, ids + (size_t)tl * k, pairs <= kIdsLds, i - tl * k, e)) {
+    const int e = stage ? ids_l[i] : ids[i];
+    const int t = i / k;
+    if (e < 0 || e >= E || repeated_in_token(ids_l + t * k, ids + (size_t)t * k, stage, i - t * k, e)) {
       inv_pos[i] = -1;
       continue;
     }
-    const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
-    const int pos = offs[e] + __popcll(below);
+    const int q = t >> 6, tl = t & 63;
+    int pos = offs[e];
+    for (int u = 0; u < q; ++u) pos += __popcll(mask[u * E + e]);
+    pos += tl ? __popcll(mask[q * E + e] & ((1ull << tl) - 1ull)) : 0;
     sorted_ids[pos] = i;
     inv_pos[i] = pos;
   }

@@ -1,5 +1,5 @@
-// Top-k selection of one token's router keys in registers (gfx950, wave64), shared by the
-// per-token route kernel and the fused decode route + align kernel.
+// Top-k selection of one token's router keys by one wave (gfx950, wave64), used by the
+// per-token route kernel and the decode route launch that also sums split-K planes.
 //
 // Keys key_e = sigmoid(logit_e) + bias_e become unique 64-bit composites (ordered key bits,
 // then the inverted expert id), so the larger composite is the larger key with ties going to
@@ -19,8 +19,8 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kFastMaxE = 1024;  // experts per token of the register path: 4 per thread of a 256-thread block
-constexpr int kFastMaxK = 16;    // its top-k: the four waves' k candidates are one per lane of one wave
+constexpr int kFastMaxE = 1024;  // experts per token of the register path: 16 per lane of one wave
+constexpr int kFastMaxK = 16;    // its top-k
 
 // 64-bit max over the wave, returned to every lane. DPP moves (quad permutations, then
 // the half-row and row mirrors) give each lane the maximum of its row of 16 lanes without
@@ -82,99 +82,13 @@ __device__ __forceinline__ void wave_top(unsigned long long (&c)[N], const float
   }
 }
 
-// Route one token with a 256-thread block: thread t holds experts e = t + 256 i; each wave
-// keeps its top k, then wave 0 takes the top k of the 4k candidates and writes the winners in
-// ascending id order with weights s_e / sum(s_selected) * rsf, the sum taken in ascending id
-// order. E <= kFastMaxE, k <= kFastMaxK. Every thread of the block must call it (one block
-// barrier inside); only wave 0 writes.
-struct RouteFastSmem {
-  unsigned long long cand_c[4][kFastMaxK];
-  float cand_s[4][kFastMaxK];
-  int sel_e[kFastMaxK];
-  float sel_s[kFastMaxK];
-};
-// The selection itself, on the logits of experts tid + 256 i (i < 4) already in registers.
-__device__ __forceinline__ void route_select_fast(const float (&lg)[4], const float* __restrict__ bias, int E, int k,
-                                                  float rsf, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                                                  RouteFastSmem& sm);
-
-__device__ __forceinline__ void route_token_fast(const float* __restrict__ logits_row, const float* __restrict__ bias,
-                                                 int E, int k, float rsf, int32_t* __restrict__ ids_out,
-                                                 float* __restrict__ w_out, RouteFastSmem& sm) {
-  // every logit load is issued before any is used (a load under a branch would wait for the
-  // previous one): experts past E read as zeros
-  const __amdgpu_buffer_rsrc_t lg_rs = make_rsrc(logits_row, (uint32_t)E * 4);
-  float lg[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    lg[i] = __builtin_bit_cast(float,
-                               __builtin_amdgcn_raw_buffer_load_b32(lg_rs, (uint32_t)(threadIdx.x + 256 * i) * 4, 0, 0));
-  route_select_fast(lg, bias, E, k, rsf, ids_out, w_out, sm);
-}
-
-__device__ __forceinline__ void route_select_fast(const float (&lg)[4], const float* __restrict__ bias, int E, int k,
-                                                  float rsf, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                                                  RouteFastSmem& sm) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // a missing bias reads as zeros
-  const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(bias, bias ? (uint32_t)E * 4 : 0u);
-  float bs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    bs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs_rs, (uint32_t)(tid + 256 * i) * 4, 0, 0));
-  unsigned long long c[4];
-  float sc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i;
-    const float s = sigmoidf_dev(lg[i]);
-    float kv = s + bs[i];
-    kv = (kv == kv) ? kv : -FLT_MAX;  // a NaN key ranks below every real key
-    // experts past E get composite 0, below every real composite
-    c[i] = e < E ? ((unsigned long long)ordered_bits(kv) << 32) | (0xffffffffu - (uint32_t)e) : 0ull;
-    sc[i] = e < E ? s : 0.f;
-  }
-  unsigned long long my_c;
-  float my_s;
-  wave_top<4>(c, sc, k, lane, my_c, my_s);
-  if (lane < k) {
-    sm.cand_c[wave][lane] = my_c;
-    sm.cand_s[wave][lane] = my_s;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    unsigned long long c1[1] = {lane < 4 * k ? sm.cand_c[lane / k][lane % k] : 0ull};
-    const float s1[1] = {lane < 4 * k ? sm.cand_s[lane / k][lane % k] : 0.f};
-    wave_top<1>(c1, s1, k, lane, my_c, my_s);
-    const int my_e = (int)(0xffffffffu - (uint32_t)(my_c & 0xffffffffull));
-    // ascending id order
-    if (lane < k) {
-      int p = 0;
-      for (int j = 0; j < k; ++j) p += __builtin_amdgcn_readlane(my_e, j) < my_e ? 1 : 0;
-      sm.sel_e[p] = my_e;
-      sm.sel_s[p] = my_s;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float tot = 0.f;
-    for (int p = 0; p < k; ++p) tot += sm.sel_s[p];  // ascending id order: a fixed rounding order
-    if (lane < k) {
-      ids_out[lane] = sm.sel_e[lane];
-      w_out[lane] = sm.sel_s[lane] / tot * rsf;
-    }
-  }
-}
-
-
 // ---- One wave per token: up to 64 * NPL experts (expert e = lane + 64 i in register i).
 //
 // The k-th largest of the 64 lane maxima, tau, bounds the k-th largest composite from below
 // (k lanes hold a composite >= tau), so the k winners are among the composites >= tau. Those
 // are compacted into 64 LDS slots (usually a few dozen) and bitonic-sorted across the wave;
 // when more than 64 reach tau, k successive wave maxima over all composites are taken instead.
-// The selected set is the same as route_select_fast's (the k largest unique composites), and
-// the winners are written the same way.
+// The selected set is the k largest (unique) composites.
 
 // lane ^ X within the wave: DPP for 1, 2 and 8 (quad permutations, row rotation by 8),
 // ds_swizzle for 4 and 16, a permute for 32

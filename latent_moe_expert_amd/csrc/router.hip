@@ -6,9 +6,8 @@
 //
 // Keys key_e = sigmoid(logit_e) + bias_e become unique 64-bit composites (key
 // bits, then the inverted expert id), so the larger composite is the larger key
-// with ties going to the lower id. For up to 1024 experts and k <= 16 a block's
-// threads hold a token's composites in registers; each wave takes its k largest
-// as k successive wave-wide maxima, then one wave takes the k largest of those.
+// with ties going to the lower id. For up to 1024 experts and k <= 16 one wave holds
+// a token's composites in registers and selects the k largest (route_dev.h).
 // Up to 4096 experts a bitonic sort in LDS orders all of them; beyond that (up to 65535) a
 // radix select over the keys' 32-bit images finds the k-th largest key and an ordered pass
 // takes the keys above it and the lowest ids among those equal to it. Every path writes the
@@ -292,14 +291,6 @@ __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
   }
   route_select_wave<NPL>(c, sc, a.k, a.rsf, lane, s_lds[wave], sm[wave], a.ids + (size_t)t * a.k,
                          a.w + (size_t)t * a.k);
-}
-
-// One token per block (E <= kFastMaxE, k <= kFastMaxK).
-__global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
-  __shared__ RouteFastSmem sm;
-  const int t = blockIdx.x;
-  route_token_fast(a.logits + (size_t)t * a.E, a.bias, a.E, a.k, a.rsf, a.ids + (size_t)t * a.k,
-                   a.w + (size_t)t * a.k, sm);
 }
 
 // Decode batches with split-K planes (E <= kFastMaxE, k <= kFastMaxK): one launch. Blocks

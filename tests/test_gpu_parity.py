@@ -221,7 +221,11 @@ def test_determinism_bitwise():
                                           (130, 3, 3, 64, 6),
                                           # above 4096 experts the chunk masks live in an LDS hash table
                                           (48, 16, 65535, 16, 7), (300, 64, 20000, 16, 8), (1000, 8, 4097, 32, 9),
-                                          (70, 2, 65535, 1, 10)])
+                                          (70, 2, 65535, 1, 10),
+                                          # one block for up to 8 chunks of 64 tokens (masks in LDS)
+                                          (512, 16, 896, 16, 11), (190, 8, 1500, 48, 13),
+                                          # past the one-block limits: 9 chunks, or masks above 64 KB
+                                          (520, 16, 896, 16, 14), (200, 8, 2000, 16, 12)])
 def test_moe_align_block_size_bit_exact_on_oracle_ids(T, k, E, B, seed):
     """The align entry point on ids the oracle routed (here: random distinct ids),
     bit-exact on every array including the padded tail."""

@@ -91,14 +91,18 @@ def test_rmsnorm_entry_point(rows, cols, weighted, inplace):
     assert (d > 0).mean() <= 1e-3
 
 
-@pytest.mark.parametrize("E,scale", [(6, 1), (5000, 800)])  # 5000: the hash-table align
-def test_align_repeated_ids_keep_first_slot(E, scale):
+@pytest.mark.parametrize("E,scale,reps", [(6, 1, 1), (5000, 800, 1),  # 5000: the hash-table align
+                                          (6, 1, 40),    # 200 tokens: one block over 4 chunks
+                                          (6, 1, 120)])  # 600 tokens: count, scan and scatter kernels
+def test_align_repeated_ids_keep_first_slot(E, scale, reps):
     """A token that lists an expert twice: the first slot is placed, later ones are dropped
-    (inv_pos -1), like ids out of range. Expected arrays by brute force on a tiny case."""
+    (inv_pos -1), like ids out of range. Expected arrays by brute force on a small case (five
+    tokens, repeated reps times)."""
     from latent_moe_expert_amd import layer as L
-    T, k, B = 5, 3, 4
+    k, B = 3, 4
     ids = np.array([[0, 2, 2], [5, 5, 5], [1, 3, 9], [3, 0, 3], [4, -1, 4]], np.int32)
-    ids = np.where(ids >= 0, ids * scale, ids).astype(np.int32)
+    ids = np.tile(np.where(ids >= 0, ids * scale, ids).astype(np.int32), (reps, 1))
+    T = ids.shape[0]
     keep = np.zeros_like(ids, dtype=bool)
     for t in range(T):
         seen = set()
