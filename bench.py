@@ -284,7 +284,7 @@ def main():
                     help="before the steps, run 3 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; runs on more than one GPU are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU; runs on more than one GPU are not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

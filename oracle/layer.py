@@ -21,7 +21,7 @@ Dataflow, from the pages:
     expert-sorted layout whose row alignment is the LCM of the consumers' tile
     widths, with expert ids per tile; expert ids above 255 must work.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1  the RMSNorm acts on the aggregated latent, after the combine.
   R2  RMSNorm(c) = c / sqrt(mean(c^2) + eps) * g (eps inside the root).
   R4  the GLU activation is SiLU(gate) * up by default; SiTU's formula is not printed.

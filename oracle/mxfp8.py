@@ -18,7 +18,7 @@ Microscaling v1.0 definitions:
   element  each value v becomes the E4M3 value nearest to v / X (ties to the
            even mantissa), magnitudes past 448 saturating to 448.
 
-Reading taken (listed in the design doc): the quantizer reads the activation the
+Reading taken: the quantizer reads the activation the
 expert receives, the latent row rounded to bf16 for the gate/up projections and
 the GLU output (not rounded) for the down projection; the bf16 path of the
 layer is the graded reference and this mode is reported beside it.
