@@ -76,20 +76,12 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(int nchunks, int E, in
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int local = 0;
   for (int e = e0; e < e1; ++e) local += (counts[e] + B - 1) / B * B;
-  part[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - local;
+  int total;
+  int run = block_exclusive_scan<1024>(local, part, &total);
   for (int e = e0; e < e1; ++e) {
     offs[e] = run;
     run += (counts[e] + B - 1) / B * B;
   }
-  const int total = part[1023];
   if (tid == 0) *num_post = total;
   __syncthreads();
   // expert ids per block and padding entries of each segment

@@ -82,6 +82,31 @@ __device__ __forceinline__ void build_masks_hash(const int32_t* __restrict__ ids
   __syncthreads();
 }
 
+// Exclusive prefix sum of v over the NT threads of the block (thread order), and the block's
+// total: an inclusive scan inside each wave, the wave totals through part (NT / 64 entries),
+// one block barrier. Integer sums: the order of additions does not change the result.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* part, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int u = part[w];
+    before += w < wave ? u : 0;
+    all += u;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
 // All T <= 64 * nc tokens in one block of NT threads: the nc chunks' masks, counts, the scan
 // over experts, padding and scatter. mask holds nc * E entries (chunk-major), offs E, part NT,
 // ids_l kIdsLds. A slot's rank inside its expert is the popcounts of the earlier chunks' masks
@@ -113,15 +138,8 @@ __device__ __forceinline__ void align_chunks(const int32_t* __restrict__ ids, in
     counts[e] = c;
     local += (c + B - 1) / B * B;
   }
-  part[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < NT; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - local;
+  int total;
+  int run = block_exclusive_scan<NT>(local, part, &total);
   for (int e = e0; e < e1; ++e) {
     offs[e] = run;
     int c = 0;
@@ -131,7 +149,6 @@ __device__ __forceinline__ void align_chunks(const int32_t* __restrict__ ids, in
     for (int i = c; i < p; ++i) sorted_ids[run + i] = pairs;
     run += p;
   }
-  const int total = part[NT - 1];
   if (tid == 0) *num_post = total;
   for (int i = total + tid; i < cap; i += NT) sorted_ids[i] = pairs;
   for (int b = total / B + tid; b < cap / B; b += NT) expert_ids[b] = -1;
