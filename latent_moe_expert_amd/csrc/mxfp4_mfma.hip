@@ -9,10 +9,15 @@
 //
 // Operands. v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a 16x128 A tile by a
 // 128x16 B tile, each lane holding 32 consecutive K values of one row (lane
-// group q = lane/16 owns K block q) and one E8M0 scale for them. The weights are
-// the B operand straight from their shipped layout: a lane's 32 weights are one
-// E8M0 group, 16 bytes of a row, so the MXFP4 bytes and their scale bytes go
-// into the MFMA unchanged. The activations are the A operand, per problem either
+// group q = lane/16 owns K block q) and one E8M0 scale for them; both operands
+// have this lane layout, so either can take the weights. The weights go into the
+// MFMA straight from their shipped layout: a lane's 32 weights are one E8M0 group,
+// 16 bytes of a row, so the MXFP4 bytes and their scale bytes are used unchanged.
+// The GLU contraction passes the activations as A (a lane's outputs are four slots
+// of one h column, so the gate and up of a column meet in one lane); the plain one
+// passes the weights as A (a lane's outputs are four consecutive columns of one
+// slot: 16-byte stores; its epilogue measured 5.2 us against 5.8 us per block with
+// 4-byte stores at an 8192-token prefill). The activations are, per problem, either
 // in the FP6 E2M3 hi/lo encoding (mxfp6.h; hi and lo each take one MFMA at the
 // FP4 rate) or, with MXFP8 activations, as E4M3 codes (mxfp8.h; one MFMA at the
 // FP8 rate, two thirds of the bytes per k-step).
@@ -363,9 +368,17 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
         for (int nf = 0; nf < 2; ++nf) {
           const u32x4_t bw = b[S][nf];
           const i32x8_t bv = {(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], 0, 0, 0, 0};
-          // A format: 0 = FP8 E4M3, 2 = FP6 E2M3; B format 4 = FP4 E2M1
-          acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av[mf & 1][p], bv, acc[mf][nf], FP8 ? 0 : 2, 4, S, (int)sA[mf][p], S, (int)sb[nf]);
+          // Formats: 0 = FP8 E4M3, 2 = FP6 E2M3 (activations), 4 = FP4 E2M1 (weights).
+          // GLU: activations as the MFMA's A operand, so a lane's four outputs are four slots of
+          // one h column (the gate and up of that column sit in the same lane). Plain: weights
+          // as the A operand, so a lane's four outputs are four consecutive output columns of one
+          // slot and the epilogue writes 16 bytes per lane.
+          if constexpr (GLU)
+            acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                av[mf & 1][p], bv, acc[mf][nf], FP8 ? 0 : 2, 4, S, (int)sA[mf][p], S, (int)sb[nf]);
+          else
+            acc[mf][nf] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bv, av[mf & 1][p], acc[mf][nf], 4, FP8 ? 0 : 2, S, (int)sb[nf], S, (int)sA[mf][p]);
         }
       // The memory clobber pins the LDS reads (IR passes may move loads across the
       // scheduling barrier, which touches no memory); the scheduling barrier then keeps
@@ -466,18 +479,16 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
   ring_barrier();
 
   if (!GLU) {
+    // lane (nl, q) of tile (mf, nf) holds slot 16 mf + nl, output columns 16 nf + 4 q .. + 3
     const int col0 = row0;
 #pragma unroll
     for (int mf = 0; mf < NT; ++mf) {
+      const int j = 16 * mf + nl;
+      if (j < nvalid) {
+        const int orow = a.routed && a.out_flat ? a.sorted_ids[first + j] : first + j;
+        float* o = a.outf + (size_t)orow * a.ldo + col0 + 4 * q;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * mf + 4 * q + r;
-        if (j < nvalid) {
-          const int orow = a.routed && a.out_flat ? a.sorted_ids[first + j] : first + j;
-          float* o = a.outf + (size_t)orow * a.ldo + col0 + nl;
-#pragma unroll
-          for (int nf = 0; nf < 2; ++nf) o[16 * nf] = acc[mf][nf][r];
-        }
+        for (int nf = 0; nf < 2; ++nf) *(f32x4_t*)(o + 16 * nf) = acc[mf][nf];
       }
     }
   } else {
@@ -598,8 +609,12 @@ __global__ __launch_bounds__(kThreads) void mx_mfma_kernel(MfmaArgs args) {
     return;
   }
   if constexpr (FMTS == kAllFp8) return;
-  if (nmf <= 4)
+  if (nmf <= 2)
+    mx_job<GLU, 2, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+  else if (nmf <= 4)
     mx_job<GLU, 4, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+  else if (nmf <= 6)
+    mx_job<GLU, 6, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else if (nmf <= 8)
     mx_job<GLU, 8, false>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
   else if (nmf <= 10)

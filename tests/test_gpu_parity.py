@@ -85,6 +85,10 @@ MFMA_SMALL = [
     # about 128 slots per expert: jobs of 5 to 12 row tiles (every row-count bucket)
     ("jobs_of_5_to_12_tiles", dict(T=512, hidden=512, latent=512, n_experts=8, topk=2, inter=512,
                                    shared_inter=512)),
+    # a Zipf-skewed router: jobs of 1, 2, 3, 4, 5, 7 and 12 row tiles, so the 2-, 4-, 6-, 8- and
+    # 12-tile kernels each run jobs with fewer valid tiles than they cover
+    ("jobs_of_1_to_12_tiles_zipf", dict(T=224, hidden=512, latent=512, n_experts=20, topk=4, inter=512,
+                                        shared_inter=512, zipf_s=1.1, zipf_c=0.5)),
 ]
 
 
