@@ -429,7 +429,7 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     if (p.mid) {  // the 128 x 128 tile splits the fp32 router into bf16 planes as it stages it
       a.seg[1] = {(const uint16_t*)router->weight, p.E, p.H, p.H, p.sr > 1 ? moe::kPartF32 : moe::kStoreF32,
                   p.sr > 1 ? (void*)at<float>(ws, p.r_part) : (void*)logits, p.E, nullptr, 0, nullptr, 0, p.sr, 1};
-    } else {  // the 256 x 256 tile reads the router as three bf16 planes [E, 3H]
+    } else {  // the 256 x 224 tile reads the router as three bf16 planes [E, 3H]
       uint16_t* wr3 = at<uint16_t>(ws, p.wr3);
       MOE_HIP(moe::launch_split3(router->weight, p.E, p.H, wr3, s));
       a.seg[1] = {wr3, p.E, 3 * p.H, p.H, p.sr > 1 ? moe::kPartF32 : moe::kStoreF32,

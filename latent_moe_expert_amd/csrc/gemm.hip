@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kGM = 8;  // M tiles per group of the grid order
-constexpr int kLargeM = 2048;  // from this many rows on, the 256 x 256 tile
+constexpr int kLargeM = 2048;  // from this many rows on, the 256 x 224 tile
 constexpr int kTile = kBM * kBK * 2;           // bytes of one operand tile in a stage
 constexpr int kGemmDma = 2 * kTile / 16 / 256;  // 16-byte LDS-DMA chunks per thread per k-step (A and W)
 static_assert(kGemmDma == 8, "");
@@ -328,16 +328,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   }
 }
 
-// ---- Large batches: 256 x 256 outputs per block, 8 waves (2 per SIMD) in 2 x 4, each
-// 128 x 64 (8 x 4 MFMA tiles). Per 64 K the block moves 64 KB for 8.4 MFLOP, half the
+// ---- Large batches: 256 x 224 outputs per block, 8 waves (2 per SIMD) in 4 x 2, each
+// 64 x 112 (4 x 7 MFMA tiles). Per 64 K the block moves 60 KB for 7.3 MFLOP, about half the
 // bytes per flop of the 128 x 128 tile, whose four waves (one per SIMD) need more load
-// bandwidth per compute unit than the memory path gives. K goes in steps of 32 (64 bytes
-// of every row) through a ring of four 32 KB stages, three k-steps ahead, so 96 KB stay in
-// flight per compute unit. Tiles are dealt to the XCDs round-robin (tile = grid position),
-// the segment with the longer K first, and inside a segment in groups of 8 M tiles with M
-// fastest, so one XCD holds the tiles of one M residue class and reuses their A rows
-// across N from its L2.
-constexpr int kBM2 = 256, kBN2 = 256, kBK2 = 32;
+// bandwidth per compute unit than the memory path gives. 224 columns divide the layer's
+// widths (7168 = 32 x 224, 3584 = 16 x 224, 896 = 4 x 224): at an 8192-token prefill the
+// up-projection is 1024 tiles, four full rounds of the 256 compute units, where 256-column
+// tiles made 896 (3.5 rounds, the last half idle), and the router's 896 rows need no
+// half-empty tile. K goes in steps of 32 (64 bytes of every row) through a ring of four
+// 32 KB stages, three k-steps ahead, so 96 KB stay in flight per compute unit. Tiles are
+// dealt to the XCDs round-robin (tile = grid position), the segment with the longer K
+// first, and inside a segment in groups of 8 M tiles with M fastest, so one XCD holds the
+// tiles of one M residue class and reuses their A rows across N from its L2.
+constexpr int kBM2 = 256, kBN2 = 224, kBK2 = 32;
 constexpr int kTile2 = kBM2 * kBK2 * 2;            // 16 KB: one operand tile of a stage
 constexpr int kDma2 = 2 * kTile2 / 16 / 512;       // 16-byte LDS-DMA chunks per thread per k-step
 static_assert(kDma2 == 4, "");
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nl = lane & 15, q = lane >> 4;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
 
   // ---- block -> (segment, K slice, M tile, N tile): the segment with the longer K slices
   // first, each segment's K slices one after another
@@ -391,7 +394,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   const int nks = max(0, min(nks_all, kb0 + kper) - kb0);
 
   // ---- LDS-DMA of one k-step: load i < 2 carries A chunk t = tid + 512 i, else W chunk
-  // t = tid + 512 (i - 2); chunk t is row t / 4 of its tile at LDS position t % 4
+  // t = tid + 512 (i - 2); chunk t is row t / 4 of its tile at LDS position t % 4. The W
+  // tile has 224 rows: the chunks of rows 224..255 load zeros into the unused LDS rows.
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(args.A, (uint32_t)args.M * (uint32_t)args.lda * 2u);
   const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(sg.W, (uint32_t)sg.N * (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t none = make_rsrc(sg.W, 0u);
@@ -405,7 +409,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
       goff[i] = row < args.M ? ((uint32_t)row * (uint32_t)args.lda + 8u * c) * 2u : kOob;
     } else {
       const int row = n0 + r;
-      goff[i] = row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
+      goff[i] = r < kBN2 && row < sg.N ? ((uint32_t)row * (uint32_t)K + 8u * c) * 2u : kOob;
     }
   }
   auto dma = [&](uint8_t* st, int j, bool on) {  // kDma2 loads of the block's k-step j
@@ -417,27 +421,29 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
              i < 2 ? ka : kw);
   };
 
-  // fragment reads: lane (nl, q) of A tile mi reads row 128 wm + 16 mi + nl, chunk q
-  const uint32_t ard = (uint32_t)((wm * 128 + nl) * 64 + g_pos2(q, nl) * 16);
-  const uint32_t brd = (uint32_t)(kTile2 + (wn * 64 + nl) * 64 + g_pos2(q, nl) * 16);
-  f32x4_t acc[8][4];
+  // fragment reads: lane (nl, q) of A tile mi reads row 64 wm + 16 mi + nl, chunk q; of W
+  // tile j row 112 wn + 16 j + nl
+  constexpr int kMI = 4, kNJ = 7;
+  const uint32_t ard = (uint32_t)((wm * 64 + nl) * 64 + g_pos2(q, nl) * 16);
+  const uint32_t brd = (uint32_t)(kTile2 + (wn * 112 + nl) * 64 + g_pos2(q, nl) * 16);
+  f32x4_t acc[kMI][kNJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kNJ; ++j) {
       acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       asm volatile("" : "+a"(acc[i][j]));
     }
 
   auto compute = [&](const uint8_t* st) {
-    u32x4_t bv[4];
+    u32x4_t bv[kNJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = *(const u32x4_t*)(st + brd + j * 16 * 64);
+    for (int j = 0; j < kNJ; ++j) bv[j] = *(const u32x4_t*)(st + brd + j * 16 * 64);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kMI; ++i) {
       const u32x4_t av = *(const u32x4_t*)(st + ard + i * 16 * 64);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kNJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
     }
   };
@@ -471,30 +477,30 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
 
   // epilogue: lane holds D[m = 4q + r][n = nl] of each 16 x 16 tile; rows past M and
   // columns past N are skipped
-  bool colok[4];
+  bool colok[kNJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) colok[j] = n0 + wn * 64 + 16 * j + nl < sg.N;
-  const int colb = n0 + wn * 64 + nl;
+  for (int j = 0; j < kNJ; ++j) colok[j] = n0 + wn * 112 + 16 * j + nl < sg.N;
+  const int colb = n0 + wn * 112 + nl;
   const bool f32 = sg.mode == kStoreF32 || sg.mode == kPartF32;
   float* outf = (float*)sg.out + (sg.mode == kPartF32 ? (size_t)slice * args.M * sg.ldo : 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float add[4][4];
+  for (int i = 0; i < kMI; ++i) {
+    float add[4][kNJ];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 128 + 16 * i + 4 * q + r;
+      const int row = m0 + wm * 64 + 16 * i + 4 * q + r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kNJ; ++j)
         add[r][j] = (sg.mode == kAddStoreBf16 && sg.addend && row < args.M && colok[j])
                         ? sg.addend[(size_t)row * sg.ld_add + colb + 16 * j]
                         : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 128 + 16 * i + 4 * q + r;
+      const int row = m0 + wm * 64 + 16 * i + 4 * q + r;
       if (row >= args.M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kNJ; ++j) {
         if (!colok[j]) continue;
         const float v = acc[i][j][r];
         const size_t o = (size_t)row * sg.ldo + colb + 16 * j;
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ W
 
 }  // namespace
 
-// The 256 x 256 tile for large batches, the 128 x 128 tile (split over K where its tiles
+// The 256 x 224 tile for large batches, the 128 x 128 tile (split over K where its tiles
 // leave compute units idle) below: with splits the larger tile's partial planes cost more to
 // write than its lower load traffic per flop saves.
 bool use_tile256(int M) { return M >= kLargeM; }

@@ -52,7 +52,7 @@ struct GemmSeg {
   int ld_add;
   float* tap;           // kAddStoreBf16 only, optional
   int ld_tap;
-  int splits;           // kPartF32: K slices (M below the 256 x 256 tile's threshold); else 0 or 1
+  int splits;           // kPartF32: K slices (M below the 256 x 224 tile's threshold); else 0 or 1
   int w_f32;            // 1: W is fp32 [N, K], split into three bf16 planes as it is staged (M < 2048)
 };
 struct GemmArgs {

@@ -158,9 +158,10 @@ def test_align_block_multiple_of_16(B):
 
 
 def test_dense_projections_256_tiles_all_rows():
-    """T = 2100 tokens take the 256 x 256 dense-projection tiles (M >= 2048): a ragged last
-    M tile (52 rows), a partial router N tile (40 of 256 rows, K = 3 x hidden), the
-    up-projection with the shared addend; every token compared."""
+    """T = 2100 tokens take the 256 x 224 dense-projection tiles (M >= 2048): a ragged last
+    M tile (52 rows), partial N tiles (z: 768 = 3 x 224 + 96 columns; the router's 40 of 224
+    rows, K = 3 x hidden; the up-projection's 1024 = 4 x 224 + 128 with the shared addend);
+    every token compared."""
     H = _harness()
     c = li.small_config(T=2100, hidden=1024, latent=768, n_experts=40, topk=3, inter=256, shared_inter=256)
     out, ref, _ = _run_small(c)
