@@ -94,7 +94,11 @@ __device__ __forceinline__ uint32_t qb_search_chunks(const uint32_t* keys, int c
 // 3. A bitwise search over the remaining bits: the largest U with #{keys >= U}
 //    >= k1. Restricting the count to keys >= tau changes no decision: for
 //    U > tau it drops nothing, and for U <= tau both counts are >= k1.
-template <int PL, bool BIAS>
+// VEC (n a multiple of 4): lane l holds keys 256 i + 4 l + c, read as 16-byte loads (a row of
+// 896 scores is 4 load instructions instead of 14; the kernel is bound by its load
+// instructions); else keys 64 i + l, read as 4-byte loads. The searches below depend only on
+// the multiset of keys, not on which lane holds which.
+template <int PL, bool BIAS, bool VEC>
 __global__ __launch_bounds__(256) void qb_alpha_kernel(const float* __restrict__ s, const float* __restrict__ bias,
                                                        int m, int n, int k1, float* __restrict__ alpha) {
   __shared__ uint32_t cand_keys[4][kCandCap];
@@ -106,17 +110,34 @@ __global__ __launch_bounds__(256) void qb_alpha_kernel(const float* __restrict__
   // they return 0 without a memory access), one lane offset and constant offsets.
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(s + (size_t)t * n, (uint32_t)n * 4u);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, BIAS ? (uint32_t)n * 4u : 0u);
-  float sv[PL], bv[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i)
-    sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, i * 256, 0));
-#pragma unroll
-  for (int i = 0; i < PL; ++i)
-    bv[i] = BIAS ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * 4, i * 256, 0)) : 0.0f;
   uint32_t u[PL];
+  if constexpr (VEC) {
+    constexpr int P4 = PL / 4;
+    u32x4_t sv[P4], bv[P4];
 #pragma unroll
-  for (int i = 0; i < PL; ++i)  // 0 lies below the image of every key (that of -inf is 0x007fffff)
-    u[i] = i * 64 + lane < n ? qb_ordered(sv[i] + bv[i]) : 0u;
+    for (int i = 0; i < P4; ++i) sv[i] = buf_load16(rs, lane * 16, i * 1024);
+#pragma unroll
+    for (int i = 0; i < P4; ++i) bv[i] = BIAS ? buf_load16(rb, lane * 16, i * 1024) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < P4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)  // 0 lies below the image of every key (that of -inf is 0x007fffff)
+        u[4 * i + c] = 256 * i + 4 * lane + c < n
+                           ? qb_ordered(__uint_as_float(sv[i][c]) + __uint_as_float(bv[i][c]))
+                           : 0u;
+  } else {
+    float sv[PL], bv[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, i * 256, 0));
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      bv[i] =
+          BIAS ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * 4, i * 256, 0)) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)  // 0 lies below the image of every key (that of -inf is 0x007fffff)
+      u[i] = i * 64 + lane < n ? qb_ordered(sv[i] + bv[i]) : 0u;
+  }
   uint32_t mx = 0u;
 #pragma unroll
   for (int i = 0; i < PL; ++i) mx = max(mx, u[i]);
@@ -274,8 +295,11 @@ hipError_t launch_qb_histogram(const float* scores, const float* bias, int m, in
                                int32_t* hist, long long q, float* new_bias, hipStream_t st) {
   if (m > 0) {
     const dim3 grid((m + 3) / 4);
-    auto* f = n <= 1024 ? (bias ? qb_alpha_kernel<16, true> : qb_alpha_kernel<16, false>)
-                        : (bias ? qb_alpha_kernel<64, true> : qb_alpha_kernel<64, false>);
+    const bool vec = n % 4 == 0;
+    auto* f = n <= 1024 ? (bias ? (vec ? qb_alpha_kernel<16, true, true> : qb_alpha_kernel<16, true, false>)
+                                : (vec ? qb_alpha_kernel<16, false, true> : qb_alpha_kernel<16, false, false>))
+                        : (bias ? (vec ? qb_alpha_kernel<64, true, true> : qb_alpha_kernel<64, true, false>)
+                                : (vec ? qb_alpha_kernel<64, false, true> : qb_alpha_kernel<64, false, false>));
     hipLaunchKernelGGL(f, grid, dim3(256), 0, st, scores, bias, m, n, k + 1, alpha);
   }
   const int groups = (n + kHistExperts - 1) / kHistExperts;
