@@ -600,10 +600,16 @@ __global__ __launch_bounds__(kThreads) void mx_mfma_kernel(MfmaArgs args) {
   const int nmf = (nvalid + 15) >> 4;
   const bool fp8 = FMTS == kAllFp8 || (FMTS == kFp6ThenFp8 && second);
   if (FMTS != kAllFp6 && fp8) {
-    if (nmf <= 4)
+    if (nmf <= 2)
+      mx_job<GLU, 2, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    else if (nmf <= 4)
       mx_job<GLU, 4, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    else if (nmf <= 6)
+      mx_job<GLU, 6, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
     else if (nmf <= 8)
       mx_job<GLU, 8, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
+    else if (nmf <= 10)
+      mx_job<GLU, 10, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
     else
       mx_job<GLU, kMF, true>(a, first, nvalid, expert, ntile, lds_a0, lds_a1, lds_a2, lds_a3, lds_dummy);
     return;
