@@ -117,6 +117,9 @@ MFMA_CASES = [
                                     shared_inter=1024, routed_scaling_factor=2.446, zipf_s=1.1, zipf_c=0.05)),
     ("jobs_of_5_to_12_tiles", dict(T=512, hidden=512, latent=512, n_experts=8, topk=2, inter=512,
                                    shared_inter=512)),
+    # a Zipf-skewed router: jobs of 1, 2, 3, 4, 5, 7 and 12 row tiles (every row-tile kernel)
+    ("jobs_of_1_to_12_tiles_zipf", dict(T=224, hidden=512, latent=512, n_experts=20, topk=4, inter=512,
+                                        shared_inter=512, zipf_s=1.1, zipf_c=0.5)),
 ]
 
 
