@@ -167,7 +167,9 @@ Plan make_plan(const moe_latent_dims* d, int topk) {
     moe::gemm_split_plan(p.T, 1, n2, k2, kNumCu, sp);
     p.su = sp[0];
   } else {
-    p.sz = p.sr = p.su = 1;
+    p.sz = p.su = 1;
+    const int n1[2] = {p.L, p.E}, k1[2] = {p.H, 3 * p.H};
+    p.sr = moe::gemm_large_split(p.T, n1, k1, kNumCu);
   }
   size_t o = 0;
   auto take = [&](size_t bytes) {

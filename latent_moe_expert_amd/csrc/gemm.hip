@@ -23,7 +23,10 @@
 // into three bf16 planes hi + mid + lo (24 significand bits = 3 x 8) stored as
 // one [N, 3K] matrix; the contraction then runs over 3K with A's column k mod K,
 // which gives the fp32-weight product with fp32 accumulation.
+#include <algorithm>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -537,8 +540,9 @@ __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ W
 }  // namespace
 
 // The 256 x 224 tile for large batches, the 128 x 128 tile (split over K where its tiles
-// leave compute units idle) below: with splits the larger tile's partial planes cost more to
-// write than its lower load traffic per flop saves.
+// leave compute units idle) below: splitting every segment of the larger tile cost more in
+// partial planes than its lower load traffic per flop saved; it splits only the router
+// segment, where that balances the rounds (gemm_large_split).
 bool use_tile256(int M) { return M >= kLargeM; }
 
 void gemm_split_plan(int M, int nseg, const int* N, const int* K, int num_cu, int* splits) {
@@ -563,12 +567,50 @@ void gemm_split_plan(int M, int nseg, const int* N, const int* K, int num_cu, in
   }
 }
 
+// 256 x 224 tiles (2048+ rows): one block fills a compute unit, so the launch runs as list
+// scheduling of its tiles, in grid order, over the compute units. A router segment whose K is
+// three times the other's (its three bf16 planes) leaves the last round partly idle; cut into
+// two K slices (fp32 partial planes, summed before routing) its tiles balance the rounds. The
+// split is taken when the simulated schedule is at least 8% shorter: at 8192 tokens of the K3
+// layer 784 against 896 k-step units (the partial planes add ~60 MB of traffic).
+static long long schedule_steps(long long tiles_a, long long steps_a, long long tiles_b, long long steps_b, int num_cu) {
+  // tiles of the longer k-step count first, as gemm256_kernel orders its segments
+  if (steps_b > steps_a) {
+    std::swap(tiles_a, tiles_b);
+    std::swap(steps_a, steps_b);
+  }
+  std::priority_queue<long long, std::vector<long long>, std::greater<long long>> cu;
+  for (int i = 0; i < num_cu; ++i) cu.push(0);
+  long long end = 0;
+  auto run = [&](long long n, long long len) {
+    for (long long t = 0; t < n; ++t) {
+      const long long f = cu.top() + len;
+      cu.pop();
+      cu.push(f);
+      end = std::max(end, f);
+    }
+  };
+  run(tiles_a, steps_a);
+  run(tiles_b, steps_b);
+  return end;
+}
+
+int gemm_large_split(int M, const int* N, const int* K, int num_cu) {
+  if (!use_tile256(M)) return 1;
+  const long long tm = (M + kBM2 - 1) / kBM2;
+  const long long t0 = tm * ((N[0] + kBN2 - 1) / kBN2), t1 = tm * ((N[1] + kBN2 - 1) / kBN2);
+  const long long s0 = K[0] / kBK2, s1 = K[1] / kBK2;
+  if (s1 % 2 || t0 + 2 * t1 > 0x7fffff) return 1;
+  const long long whole = schedule_steps(t0, s0, t1, s1, num_cu);
+  const long long halves = schedule_steps(t0, s0, 2 * t1, s1 / 2, num_cu);
+  return halves * 100 <= whole * 92 ? 2 : 1;
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.nseg < 1 || a.nseg > 2 || a.M < 0 || a.lda % 8) return hipErrorInvalidValue;
   const bool big = use_tile256(a.M);
   const int bm = big ? kBM2 : kBM, bn = big ? kBN2 : kBN, bk = big ? kBK2 : kBK;
   long long blocks = 0;
-  bool split = false;
   const long long tm = (a.M + bm - 1) / bm;
   for (int i = 0; i < a.nseg; ++i) {
     const GemmSeg& g = a.seg[i];
@@ -577,12 +619,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
     if (g.w_f32 && (big || g.kwrap != g.K)) return hipErrorInvalidValue;  // fp32 weights: the 128 x 128 tile
     if (g.splits < 0 || g.splits > g.K / (g.w_f32 ? 32 : bk) || (g.mode == kPartF32) != (g.splits > 1))
       return hipErrorInvalidValue;
-    split |= g.splits > 1;
     blocks += tm * ((g.N + bn - 1) / bn) * (g.splits > 1 ? g.splits : 1);
   }
   if ((long long)a.M * a.lda * 2 >= (1ll << 31)) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
-  if (a.M >= kLargeM && split) return hipErrorInvalidValue;
   if (blocks > 0x7ffffff0ll) return hipErrorInvalidValue;
   if (big) {
     hipLaunchKernelGGL(gemm256_kernel, dim3((unsigned)blocks), dim3(512), 0, s, a);

@@ -65,6 +65,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 // K slices per segment (N[i] x K[i], nseg <= 2) for a split-K launch of M < 2048 rows that
 // puts one block on each of num_cu compute units
 void gemm_split_plan(int M, int nseg, const int* N, const int* K, int num_cu, int* splits);
+// 2048+ rows: K slices (1 or 2) for segment 1 of a two-segment launch (the router's planes)
+int gemm_large_split(int M, const int* N, const int* K, int num_cu);
 // fp32 [N, K] -> bf16 [N, 3K] rows hi | mid | lo with w = hi + mid + lo exactly
 hipError_t launch_split3(const float* W, int N, int K, uint16_t* out, hipStream_t s);
 

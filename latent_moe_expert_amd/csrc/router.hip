@@ -260,7 +260,9 @@ __global__ __launch_bounds__(256) void route_radix_kernel(RouteArgs a) {
 
 // One token per wave, four per block (E <= 64 * NPL <= kFastMaxE, k <= kFastMaxK): the waves
 // share nothing but the block's LDS arrays, each its own part, and need no block barrier.
-template <int NPL>
+// PLANES2: the logits arrive as two split-K partial planes [2][T][E]; the wave sums them in
+// slice order from zero (as reduce_planes_kernel does) and stores the sums in logits_out.
+template <int NPL, bool PLANES2>
 __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
   __shared__ float s_lds[4][64 * NPL];
   __shared__ RouteWaveSmem sm[4];
@@ -269,14 +271,26 @@ __global__ __launch_bounds__(256) void route_wave_kernel(RouteArgs a) {
   if (t >= a.T) return;  // wave-uniform
   const int E = a.E;
   // every load is issued before any is used; experts past E read as zeros
-  const __amdgpu_buffer_rsrc_t lg_rs = make_rsrc(a.logits + (size_t)t * E, (uint32_t)E * 4);
+  const float* src = PLANES2 ? a.r_part : a.logits;
+  const __amdgpu_buffer_rsrc_t lg_rs = make_rsrc(src + (size_t)t * E, (uint32_t)E * 4);
+  const __amdgpu_buffer_rsrc_t l2_rs =
+      make_rsrc(PLANES2 ? a.r_part + (size_t)a.T * E + (size_t)t * E : a.logits, PLANES2 ? (uint32_t)E * 4 : 0u);
   const __amdgpu_buffer_rsrc_t bs_rs = make_rsrc(a.bias, a.bias ? (uint32_t)E * 4 : 0u);
-  float lg[NPL], bs[NPL];
+  float lg[NPL], l2[NPL], bs[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const uint32_t off = (uint32_t)(lane + 64 * i) * 4;
     lg[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lg_rs, off, 0, 0));
+    if (PLANES2) l2[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l2_rs, off, 0, 0));
     bs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs_rs, off, 0, 0));
+  }
+  if constexpr (PLANES2) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      lg[i] = ((0.f + lg[i]) + l2[i]) + 0.f;
+      if (e < E) a.logits_out[(size_t)t * E + e] = lg[i];
+    }
   }
   unsigned long long c[NPL];
   float sc[NPL];
@@ -367,22 +381,33 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(route_fast_planes_kernel, dim3((unsigned)(a.T + (zb < 4096 ? zb : 4096))), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (a.r_part || a.z_part) {  // finish split-K sums first, in parallel over all elements
+  if (a.k > 64) return hipErrorInvalidValue;
+  const bool fast = a.E <= kFastMaxE && a.k <= kFastMaxK;
+  // two logit planes and no latent planes (the 2048+-row dense tile splits only the router):
+  // the routing waves sum them as they load them
+  const bool planes2 = fast && a.r_part && !a.z_part && a.sr == 2 && a.logits_out;
+  if ((a.r_part || a.z_part) && !planes2) {  // finish split-K sums first, in parallel over all elements
     const size_t n = (a.z_part ? (size_t)a.T * a.L / 4 : 0) + (a.r_part ? (size_t)a.T * a.E : 0);
     const size_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(reduce_planes_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, a);
   }
-  if (a.k > 64) return hipErrorInvalidValue;
-  if (a.E <= kFastMaxE && a.k <= kFastMaxK) {
+  if (fast) {
     const dim3 grid((unsigned)((a.T + 3) / 4));
-    if (a.E <= 128)
-      hipLaunchKernelGGL(route_wave_kernel<2>, grid, dim3(256), 0, s, a);
-    else if (a.E <= 256)
-      hipLaunchKernelGGL(route_wave_kernel<4>, grid, dim3(256), 0, s, a);
-    else if (a.E <= 512)
-      hipLaunchKernelGGL(route_wave_kernel<8>, grid, dim3(256), 0, s, a);
+    auto go = [&](auto k2, auto k4, auto k8, auto k16) {
+      if (a.E <= 128)
+        hipLaunchKernelGGL(k2, grid, dim3(256), 0, s, a);
+      else if (a.E <= 256)
+        hipLaunchKernelGGL(k4, grid, dim3(256), 0, s, a);
+      else if (a.E <= 512)
+        hipLaunchKernelGGL(k8, grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(k16, grid, dim3(256), 0, s, a);
+    };
+    if (planes2)
+      go(route_wave_kernel<2, true>, route_wave_kernel<4, true>, route_wave_kernel<8, true>, route_wave_kernel<16, true>);
     else
-      hipLaunchKernelGGL(route_wave_kernel<16>, grid, dim3(256), 0, s, a);
+      go(route_wave_kernel<2, false>, route_wave_kernel<4, false>, route_wave_kernel<8, false>,
+         route_wave_kernel<16, false>);
   }
   else if (a.E <= kMaxE)
     hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(256), 0, s, a);
