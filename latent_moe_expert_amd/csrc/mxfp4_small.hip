@@ -7,7 +7,8 @@
 //
 // Work unit: one 16-slot tile of the expert-sorted layout (or 16 rows of a
 // dense batch) x 64 weight rows per wave (GLU: 32 gate rows and the same 32 up
-// rows; plain: 64 rows), 4 waves per block, full K per wave. The block loads
+// rows; plain: 64 rows), 4 waves per block, full K per wave; the routed tiles
+// of a launch's last round take half the weight rows per wave. The block loads
 // the tile's activations once per step into a shared, swizzled LDS tile.
 //
 // Memory path. Decode streams each touched expert's bytes once, so the kernel
@@ -44,21 +45,14 @@ namespace moe {
 
 namespace {
 
-template <bool GLU>
-__global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0, int bands0, int bands1) {
-  // per wave: an 8 KB weight tile; per block: two 8 KB activation tiles (16 slots x 256 K bf16)
-  __shared__ __attribute__((aligned(16))) uint8_t lds_w[4][64 * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][16 * 512];
+// NTW: 16-row weight tiles per wave (GLU: NTW/2 gate tiles and the same up tiles). One block:
+// 4 waves, one 16-slot tile `blk` of problem `a` against the column band `band`.
+template <bool GLU, int NTW>
+__device__ __forceinline__ void mx_small_block(const MxProblem& a, int band, int blk, uint8_t (*lds_w)[4 * 16 * 128],
+                                               uint8_t (*lds_a)[16 * 512]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int nl = lane & 15, q = lane >> 4;
-  // block -> (problem, column band, 16-slot tile); problem 0 first
-  const bool second = (int)blockIdx.x >= blocks0;
-  const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
-  const int bands = second ? bands1 : bands0;
-  const MxProblem& a = args.p[second ? 1 : 0];
-  const int band = local % bands;
-  const int blk = local / bands;
   uint8_t* lds = lds_w[wave];
 
   // block-uniform exits only (the loop below has block barriers)
@@ -70,7 +64,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   } else if (blk * 16 >= a.M) {
     return;
   }
-  constexpr int kColsPerWave = GLU ? 32 : 64;
+  constexpr int kColsPerWave = GLU ? 8 * NTW : 16 * NTW;
   const int col0 = (band * 4 + wave) * kColsPerWave;  // N is a multiple of the block's columns
 
   const int K = a.K;
@@ -84,7 +78,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   // Wave tile t (16 rows) starts at row col0 + 16*tt(t) of its matrix, tt(t) = t&1 (GLU: t<2 gate,
   // t>=2 up) or t (plain). Load l (0..7) of a double step covers the wave's slots 8l..8l+7;
   // lane = (slot 8l + lane/8, 16-byte chunk lane%8). Row offsets are uniform per l.
-  auto tt = [](int t) { return GLU ? (t & 1) : t; };
+  auto tt = [](int t) { return GLU ? t % (NTW / 2) : t; };
   const uint32_t gbase = (uint32_t)(col0 + (lane >> 3)) * kb2 + (lane & 7) * 16;
   // LDS: slot j, chunk c lives at j*128 + ((c ^ (j & 7)) * 16); for load l, j & 7 = lane >> 3
   const uint32_t wbase = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) * 16);
@@ -117,13 +111,13 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   for (int j = 0; j < 4; ++j) aread[j] = nl * 512 + (((4 * q + j) ^ nl) * 16);
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(a.A, 0x7fffffffu);
 
-  f32x4_t acc[4];
+  f32x4_t acc[NTW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NTW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   struct Stage {
-    u32x4_t w[8];
-    uint2 sc[4];
+    u32x4_t w[2 * NTW];
+    uint2 sc[NTW];
   };
   u32x4_t anext[2];
   // A double step past the end loads from a zero-size resource (zeros, no memory traffic), so
@@ -139,17 +133,17 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     }
     const uint32_t vo = gbase + (uint32_t)d * 128;  // 256 weights of a row per double step
 #pragma unroll
-    for (int l = 0; l < 8; ++l) {
+    for (int l = 0; l < 2 * NTW; ++l) {
       const int t = l >> 1;
       const uint32_t so = (uint32_t)(16 * tt(t) + 8 * (l & 1)) * kb2;
       st.w[l] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                on ? ((GLU && t >= 2) ? w_hi : w_lo) : none, vo, so, kNonTemporal));
+                                                on ? ((GLU && t >= NTW / 2) ? w_hi : w_lo) : none, vo, so, kNonTemporal));
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NTW; ++t) {
       const uint32_t so = (uint32_t)(16 * tt(t)) * ks32 + (uint32_t)d * 8;
       st.sc[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               on ? ((GLU && t >= 2) ? s_hi : s_lo) : none, sbase, so, 0));
+                                               on ? ((GLU && t >= NTW / 2) ? s_hi : s_lo) : none, sbase, so, 0));
     }
   };
   auto fill_a = [&](int buf) {
@@ -158,7 +152,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   };
   auto consume = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int l = 0; l < 8; ++l) *(u32x4_t*)(lds + l * 1024 + wbase) = st.w[l];
+    for (int l = 0; l < 2 * NTW; ++l) *(u32x4_t*)(lds + l * 1024 + wbase) = st.w[l];
     const uint8_t* at = lds_a[buf];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -166,7 +160,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = *(const u32x4_t*)(at + h * 256 + aread[j]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < NTW; ++t) {
         const u32x4_t wf = *(const u32x4_t*)(lds + t * 2048 + (h ? rbase1 : rbase0));
         const uint32_t code = ((h ? st.sc[t].y : st.sc[t].x) >> (8 * q)) & 0xffu;
         const float sc = e8m0_as_f32_exponent(code);
@@ -213,13 +207,14 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
     valid[r] = a.routed ? (sid < a.pairs) : (pos < a.M);
   }
   if (GLU) {
-    // a wave's 32 columns of a row are one MXFP8 group: lanes 16q..16q+15 (tiles 0 and 1) of row 4q + r
-    float hv[2][4];
+    // with NTW == 4 a wave's 32 columns of a row are one MXFP8 group: lanes 16q..16q+15 (tiles 0
+    // and 1) of row 4q + r (the launcher runs MXFP8 outputs with NTW == 4 only)
+    float hv[NTW / 2][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NTW / 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hv[t][r] = glu_act(acc[t][r], acc[t + 2][r], a.act);
-    if (a.out_fp8) {
+      for (int r = 0; r < 4; ++r) hv[t][r] = glu_act(acc[t][r], acc[t + NTW / 2][r], a.act);
+    if (NTW == 4 && a.out_fp8) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float m = fmaxf(fabsf(hv[0][r]), fabsf(hv[1][r]));
@@ -227,22 +222,53 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
         for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
         const int sx = mxfp8_scale_exp(m);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) hv[t][r] = ldexpf(e4m3_round(ldexpf(hv[t][r], -sx)), sx);
+        for (int t = 0; t < NTW / 2; ++t) hv[t][r] = ldexpf(e4m3_round(ldexpf(hv[t][r], -sx)), sx);
       }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NTW / 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (valid[r])
           ((uint16_t*)a.out)[(size_t)opos[r] * a.ldo + col0 + t * 16 + nl] = (uint16_t)f32_to_bf16_bits(hv[t][r]);
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTW; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (valid[r]) ((float*)a.out)[(size_t)opos[r] * a.ldo + col0 + t * 16 + nl] = acc[t][r];
   }
+}
+
+// Block -> (problem, column band, 16-slot tile); problem 0 first. With half_tiles > 0 the last
+// min(half_tiles, V) valid tiles of problem 1 (V = its valid 16-slot tiles, known on the device)
+// run as blocks of half the columns (NTW = 2), placed after every full-width block, so the launch
+// ends on blocks half as long. Per-block timestamps at decode16: as the last full-width blocks
+// finish, the compute units go idle over about one block duration (30-38 us), which cost ~17 us
+// of the gate/up launch and ~13 us of the down launch against their steady 6.1 TB/s; with the
+// half-width tail the launches took 431 and 224 us against 435 and 226 (decode step 0.716
+// against 0.720 ms). All blocks half-width measured slower (0.729 ms): per weight byte a
+// half-width block reads its activation tile twice as often.
+template <bool GLU, bool HALF>
+__global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0, int bands0, int bands1, int full1,
+                                                       int half_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[4][4 * 16 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][16 * 512];
+  const bool second = (int)blockIdx.x >= blocks0;
+  const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
+  const MxProblem& a = args.p[second ? 1 : 0];
+  if (HALF && second) {
+    const int V = (*a.num_post + 15) >> 4, X = min(half_tiles, V);
+    if (local >= full1) {  // half-width blocks: tile V - X + h / (2 bands1)
+      const int h = local - full1, t = h / (2 * bands1);
+      if (t >= X) return;
+      mx_small_block<GLU, 2>(a, h % (2 * bands1), V - X + t, lds_w, lds_a);
+      return;
+    }
+    if (local / bands1 >= V - X) return;  // its tile runs as half-width blocks
+  }
+  const int bands = second ? bands1 : bands0;
+  mx_small_block<GLU, 4>(a, local % bands, local / bands, lds_w, lds_a);
 }
 
 }  // namespace
@@ -257,15 +283,32 @@ hipError_t launch_mx_small(const MxArgs& a, hipStream_t s) {
     bands[i] = a.p[i].N / cols_per_block;
     blocks[i] = a.p[i].max_blocks > 0 ? bands[i] * a.p[i].max_blocks : 0;
   }
-  const long long total = (long long)blocks[0] + blocks[1];
+  // The routed problem's last tiles as half-width blocks, about kTailBlocks full blocks' worth:
+  // one round of the launch (two blocks per compute unit are resident, measured with per-block
+  // timestamps; 256 and 1024 measured no better than 512). Not for MXFP8 outputs of h, whose
+  // groups are one full-width wave's 32 columns.
+  constexpr int kTailBlocks = 512;
+  const int r = a.nprob - 1;
+  const bool half = a.p[r].routed && !(glu && a.p[r].out_fp8) && bands[r] > 0;
+  const int half_tiles = half ? (kTailBlocks + bands[r] - 1) / bands[r] : 0;
+  const long long extra = half ? (long long)half_tiles * 2 * bands[r] : 0;
+  const long long total = (long long)blocks[0] + blocks[1] + extra;
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffffll) return hipErrorInvalidValue;
-  if (glu)
-    hipLaunchKernelGGL(mx_small_kernel<true>, dim3((unsigned)total), dim3(256), 0, s, a, blocks[0], bands[0],
-                       bands[1] ? bands[1] : 1);
-  else
-    hipLaunchKernelGGL(mx_small_kernel<false>, dim3((unsigned)total), dim3(256), 0, s, a, blocks[0], bands[0],
-                       bands[1] ? bands[1] : 1);
+  // with one problem it is problem "1" of the kernel's mapping (blocks0 = 0)
+  const int b0 = a.nprob > 1 ? blocks[0] : 0, bd0 = a.nprob > 1 ? bands[0] : 1, bd1 = bands[r], full1 = blocks[r];
+  MxArgs args = a;
+  if (a.nprob == 1) args.p[1] = a.p[0];
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(256), 0, s, args, b0, bd0, bd1, full1, half_tiles);
+  };
+  if (glu) {
+    if (half) go(mx_small_kernel<true, true>);
+    else go(mx_small_kernel<true, false>);
+  } else {
+    if (half) go(mx_small_kernel<false, true>);
+    else go(mx_small_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 
