@@ -243,8 +243,8 @@ __device__ __forceinline__ void mx_small_block(const MxProblem& a, int band, int
 // Block -> (problem, column band, 16-slot tile); problem 0 first. With half_tiles > 0 the last
 // min(half_tiles, V) valid tiles of problem 1 (V = its valid 16-slot tiles, known on the device)
 // run as blocks of half the columns (NTW = 2), placed after every full-width block, so the launch
-// ends on blocks half as long. Per-block timestamps at decode16: as the last full-width blocks
-// finish, the compute units go idle over about one block duration (30-38 us), which cost ~17 us
+// ends on blocks half as long. Per-block timestamps at decode16 (three blocks resident per compute
+// unit, 768 in all): as the last full-width blocks finish, the compute units go idle over about one block duration (30-38 us), which cost ~17 us
 // of the gate/up launch and ~13 us of the down launch against their steady 6.1 TB/s; with the
 // half-width tail the launches took 431 and 224 us against 435 and 226 (decode step 0.716
 // against 0.720 ms). All blocks half-width measured slower (0.729 ms): per weight byte a
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MxArgs args, int blocks0,
   const int local = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
   const MxProblem& a = args.p[second ? 1 : 0];
   if (HALF && second) {
-    const int V = (*a.num_post + 15) >> 4, X = min(half_tiles, V);
+    const int V = min((*a.num_post + 15) >> 4, a.max_blocks), X = min(half_tiles, V);
     if (local >= full1) {  // half-width blocks: tile V - X + h / (2 bands1)
       const int h = local - full1, t = h / (2 * bands1);
       if (t >= X) return;
@@ -283,10 +283,9 @@ hipError_t launch_mx_small(const MxArgs& a, hipStream_t s) {
     bands[i] = a.p[i].N / cols_per_block;
     blocks[i] = a.p[i].max_blocks > 0 ? bands[i] * a.p[i].max_blocks : 0;
   }
-  // The routed problem's last tiles as half-width blocks, about kTailBlocks full blocks' worth:
-  // one round of the launch (two blocks per compute unit are resident, measured with per-block
-  // timestamps; 256 and 1024 measured no better than 512). Not for MXFP8 outputs of h, whose
-  // groups are one full-width wave's 32 columns.
+  // The routed problem's last tiles as half-width blocks, about kTailBlocks full blocks' worth
+  // (decode16 step 0.720, 0.713, 0.716 and 0.717 ms with 0, 512, 768 and 1024; 256 no better than
+  // 512). Not for MXFP8 outputs of h, whose groups are one full-width wave's 32 columns.
   constexpr int kTailBlocks = 512;
   const int r = a.nprob - 1;
   const bool half = a.p[r].routed && !(glu && a.p[r].out_fp8) && bands[r] > 0;
