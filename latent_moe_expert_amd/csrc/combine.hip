@@ -21,7 +21,8 @@ constexpr int kMaxSlots = 64;
 
 // One block per token; thread owns float4 columns v = tid + 256*i (i < KV). Slots
 // are taken in groups of G = 32/KV with every load of a group issued before any
-// use, then added in slot order (a fixed rounding order).
+// use, then added in slot order (a fixed rounding order). Each row of O is read once,
+// with the read-once cache policy: at 8192 tokens (1.88 GB of O) 0.348 ms against 0.373.
 template <int KV>
 __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restrict__ O, int L,
                                                            const int32_t* __restrict__ inv_pos,
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const float* __restri
 #pragma unroll
       for (int i = 0; i < KV; ++i) {
         const int vi = threadIdx.x + 256 * i;
-        v[g][i] = (p >= 0 && vi < nvec) ? row[vi] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        v[g][i] = (p >= 0 && vi < nvec) ? __builtin_nontemporal_load(row + vi) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll

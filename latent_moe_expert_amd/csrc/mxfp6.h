@@ -65,6 +65,23 @@ __device__ __forceinline__ uint32_t fp6_scale_code(float amax) {
 }
 __device__ __forceinline__ float e8m0_value(uint32_t code) { return __uint_as_float(code << 23); }  // code >= 1
 
+// The two packing conversions, as inline asm with early-clobber outputs: no register of the
+// result may also hold an operand. The builtins leave that to the register allocator, which
+// may give the 6-dword result of the 2 x 16-value conversion registers inside a source operand.
+// Where they start at the same register the results were right, but a result placed four
+// registers into the second source (v[6:11] against v[2:17]) gave wrong codes: the
+// instruction writes its first result dwords before it has read the rest of that source.
+__device__ __forceinline__ fp6_u32x6_t fp6_cvt_2xpk16(fp6_f32x16_t even, fp6_f32x16_t odd, float scale) {
+  fp6_u32x6_t r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(even), "v"(odd), "v"(scale));
+  return r;
+}
+__device__ __forceinline__ fp6_f32x32_t fp6_cvt_pk32_to_f32(fp6_u32x6_t codes, float scale) {
+  fp6_f32x32_t r;
+  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(r) : "v"(codes), "v"(scale));
+  return r;
+}
+
 // Encode one group of 32 values into hi and lo planes (6 dwords each) and their scale
 // codes. v_cvt_scalef32_2xpk16_fp6_f32 rounds x / scale to E2M3 (nearest even, saturating
 // at 7.5) and packs src0[j] at code position 2j and src1[j] at 2j + 1;
@@ -82,8 +99,8 @@ __device__ __forceinline__ void fp6_encode_group(const float v[32], uint32_t hi[
   }
   s_hi = fp6_scale_code(amax);
   const float x_hi = e8m0_value(s_hi);
-  const fp6_u32x6_t h = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, x_hi);
-  const fp6_f32x32_t q = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(h, x_hi);
+  const fp6_u32x6_t h = fp6_cvt_2xpk16(ev, od, x_hi);
+  const fp6_f32x32_t q = fp6_cvt_pk32_to_f32(h, x_hi);
   float ramax = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -93,7 +110,7 @@ __device__ __forceinline__ void fp6_encode_group(const float v[32], uint32_t hi[
     ramax = fmaxf(ramax, fmaxf(fabsf(ev[i]), fabsf(od[i])));
   }
   s_lo = fp6_scale_code(ramax);
-  const fp6_u32x6_t l = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, e8m0_value(s_lo));
+  const fp6_u32x6_t l = fp6_cvt_2xpk16(ev, od, e8m0_value(s_lo));
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
     hi[j] = h[j];

@@ -8,18 +8,38 @@ namespace moe {
 
 namespace {
 
-// One thread per group of 32 values: 64 bytes in, 2 x 24 bytes and 2 scale bytes out.
+// One thread per group of 32 values: 64 bytes in, 2 x 24 bytes and 2 scale bytes out. The
+// block's 256 groups move through LDS: each load instruction reads 1 KB of contiguous rows
+// (16 groups x 64 bytes; part r of block group lg at LDS slot 4 lg + (r ^ (lg / 4 % 4)), so
+// that the per-group reads are conflict-free), and the 48 output bytes of each group, which
+// lie contiguous in the dense FP6 rows, leave as 16-byte stores of consecutive lanes. At 8192
+// tokens (z and x, 176 MB in, 132 MB out) 64.5 us against 89 us with one thread reading and
+// writing its own group (64-byte strided loads, 8-byte strided stores).
 __global__ __launch_bounds__(256) void quant_fp6_kernel(const uint16_t* __restrict__ A, int lda, int rows, int K,
                                                         uint8_t* __restrict__ data, uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[256 * 64];
   const int G = K >> 5;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)rows * G) return;
-  const int row = (int)(idx / G), g = (int)(idx % G);
-  const u32x4_t* src = (const u32x4_t*)(A + (size_t)row * lda + (size_t)g * 32);
+  const long long ng = (long long)rows * G;
+  const long long base = (long long)blockIdx.x * 256;
+  const int nv = (int)min(256ll, ng - base);  // valid groups of this block (>= 1)
+  const int tid = threadIdx.x;
+  const int base_row = (int)(base / G), base_g = (int)(base % G);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j, lg = c >> 2, r = c & 3;
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (lg < nv) {
+      const int gg = base_g + lg;
+      const int row = base_row + gg / G, g = gg % G;
+      x = __builtin_nontemporal_load((const u32x4_t*)(A + (size_t)row * lda + (size_t)g * 32 + r * 8));
+    }
+    *(u32x4_t*)(tile + (4 * lg + (r ^ ((lg >> 2) & 3))) * 16) = x;
+  }
+  __syncthreads();
   float v[32];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const u32x4_t x = src[j];
+    const u32x4_t x = *(const u32x4_t*)(tile + (4 * tid + (j ^ ((tid >> 2) & 3))) * 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[8 * j + 2 * e] = bf16_bits_to_f32(x[e] & 0xffffu);
@@ -28,17 +48,22 @@ __global__ __launch_bounds__(256) void quant_fp6_kernel(const uint16_t* __restri
   }
   uint32_t hi[6], lo[6], s_hi, s_lo;
   fp6_encode_group(v, hi, lo, s_hi, s_lo);
-  uint8_t* drow = data + (size_t)row * fp6_row_bytes(K);
-  uint2* dh = (uint2*)(drow + fp6_data_offset(g, 0));
-  uint2* dl = (uint2*)(drow + fp6_data_offset(g, 1));
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    dh[j] = make_uint2(hi[2 * j], hi[2 * j + 1]);
-    dl[j] = make_uint2(lo[2 * j], lo[2 * j + 1]);
+  __syncthreads();  // the tile now takes the outputs: group lg's 48 bytes at 48 lg
+  u32x4_t* o = (u32x4_t*)(tile + tid * 48);
+  o[0] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+  o[1] = u32x4_t{hi[4], hi[5], lo[0], lo[1]};
+  o[2] = u32x4_t{lo[2], lo[3], lo[4], lo[5]};
+  __syncthreads();
+  // FP6 rows are dense (fp6_row_bytes(K) = 48 G): group gi's bytes start at 48 gi
+  uint8_t* dst = data + (size_t)base * 48;
+  for (int b = tid * 16; b < nv * 48; b += 256 * 16) *(u32x4_t*)(dst + b) = *(const u32x4_t*)(tile + b);
+  if (tid < nv) {
+    const int gg = base_g + tid;
+    const int row = base_row + gg / G, g = gg % G;
+    uint8_t* srow = scales + (size_t)row * fp6_scale_row_bytes(K);
+    srow[fp6_scale_offset(g, 0)] = (uint8_t)s_hi;
+    srow[fp6_scale_offset(g, 1)] = (uint8_t)s_lo;
   }
-  uint8_t* srow = scales + (size_t)row * fp6_scale_row_bytes(K);
-  srow[fp6_scale_offset(g, 0)] = (uint8_t)s_hi;
-  srow[fp6_scale_offset(g, 1)] = (uint8_t)s_lo;
 }
 
 __device__ __forceinline__ void load_bf16x32(const uint16_t* p, float v[32]) {
