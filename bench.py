@@ -51,20 +51,39 @@ TRAFFIC_PROFILES = {"decode16": "mx_small_decode16_traffic.md", "prefill8192": "
                     "qb8192": "qb8192_traffic.md"}
 
 
+def kernel_source_hash(rel: str) -> str:
+    """sha256 (first 16 hex digits) of a kernel source file followed by the library headers it
+    includes, directly or through other headers, in name order: a profile record keyed by it
+    goes stale when the kernel or any header it compiles with changes."""
+    import hashlib
+    import re
+    csrc = os.path.dirname(os.path.join(ROOT, rel))
+    seen, todo = set(), [os.path.basename(rel)]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            continue
+        seen.add(name)
+        todo += re.findall(r'^#include "([^"]+)"', open(os.path.join(csrc, name)).read(), re.M)
+    h = hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read())
+    for name in sorted(seen - {os.path.basename(rel)}):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC summary,
     or None when that summary was taken on a different kernel source or workload."""
-    import hashlib
     if workload not in TRAFFIC_PROFILES:
         return None
     path = os.path.join(ROOT, "profiles", TRAFFIC_PROFILES[workload])
     try:
         line = next(l for l in open(path) if l.startswith("traffic_record:"))
         rec = json.loads(line.split(":", 1)[1])
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        key = kernel_source_hash(rec["source"])
     except (OSError, StopIteration, ValueError, KeyError):
         return None
-    if rec.get("workload") != workload or hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+    if rec.get("workload") != workload or key != rec["source_sha256_16"]:
         return None
     return rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
 
@@ -72,17 +91,16 @@ def measured_traffic(workload: str):
 def measured_mfma(workload: str):
     """MFMA busy fraction and engine clock of the prefill gate/up launch from the committed
     rocprofv3 counter summary, or None when it was taken on a different kernel source."""
-    import hashlib
     if workload != "prefill8192":
         return None
     path = os.path.join(ROOT, "profiles", "mx_mfma_prefill8192_mfma_util.md")
     try:
         line = next(l for l in open(path) if l.startswith("mfma_record:"))
         rec = json.loads(line.split(":", 1)[1])
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        key = kernel_source_hash(rec["source"])
     except (OSError, StopIteration, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+    if key != rec["source_sha256_16"]:
         return None
     return {"mfma_busy": rec["mfma_busy"], "clock_ghz": rec["clock_ghz"]}
 
