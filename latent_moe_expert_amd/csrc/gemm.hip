@@ -520,21 +520,24 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   }
 }
 
-// fp32 [N, K] -> bf16 [N, 3K]: row n = hi(k) | mid(k) | lo(k), w = hi + mid + lo exactly
+// fp32 [N, K] -> bf16 [N, 3K]: row n = hi(k) | mid(k) | lo(k), w = hi + mid + lo exactly.
+// Eight consecutive weights per thread (K % 8 == 0): two 16-byte read-once loads and one
+// 16-byte store per plane (at 8192 tokens of the K3 router, 25.7 MB in and 38.5 MB out, ~12 us
+// against 21 us with one weight and three 2-byte stores per thread).
 __global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ W, int N, int K,
                                                      uint16_t* __restrict__ out) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= (long long)N * K) return;
   const int n = (int)(i / K), k = (int)(i % K);
-  const float f = W[i];
-  const uint32_t h = __float_as_uint(f) & 0xffff0000u;
-  const float r = f - __uint_as_float(h);
-  const uint32_t m = __float_as_uint(r) & 0xffff0000u;
-  const float l = r - __uint_as_float(m);
+  const u32x4_t a = load_nt_u32x4(W + i), b = load_nt_u32x4(W + i + 4);
+  const uint32_t f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) split3x2(__uint_as_float(f[2 * j]), __uint_as_float(f[2 * j + 1]), hi[j], mid[j], lo[j]);
   uint16_t* row = out + (size_t)n * 3 * K;
-  row[k] = (uint16_t)(h >> 16);
-  row[K + k] = (uint16_t)(m >> 16);
-  row[2 * K + k] = (uint16_t)(__float_as_uint(l) >> 16);
+  *(u32x4_t*)(row + k) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+  *(u32x4_t*)(row + K + k) = u32x4_t{mid[0], mid[1], mid[2], mid[3]};
+  *(u32x4_t*)(row + 2 * K + k) = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
 }
 
 }  // namespace
@@ -636,7 +639,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_split3(const float* W, int N, int K, uint16_t* out, hipStream_t s) {
   const long long n = (long long)N * K;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(split3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, W, N, K, out);
+  if (K % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split3_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s, W, N, K, out);
   return hipGetLastError();
 }
 
