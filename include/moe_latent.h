@@ -146,7 +146,9 @@ typedef struct moe_latent_taps {
   float* y_routed;        /* fp32 [T, H]  up-projection output */
   float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none) */
   float* O;               /* fp32 [T*k, L] the routed expert's output of slot t*k+j (token t's
-                             j-th selected expert), before the routing weight */
+                             j-th selected expert), before the routing weight; on the MFMA path
+                             above 64 tokens the layer keeps O in bf16, and the tap holds those
+                             bf16 values widened to fp32 */
 } moe_latent_taps;
 
 int moe_latent_abi_version(void);

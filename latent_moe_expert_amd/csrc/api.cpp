@@ -580,7 +580,10 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
       g.s_stride = 3 * gu_scales;
       g.N = p.L;
       g.K = p.I;
-      g.outf = O;
+      if (p.small)
+        g.outf = O;
+      else  // bf16 rows: the combine reads half the bytes
+        g.outh = (uint16_t*)O;
       g.ldo = p.L;
       m.nprob = n;
       MOE_HIP(moe::launch_mx_mfma(m, s));
@@ -692,9 +695,12 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
   if (p.small)
     MOE_HIP(moe::launch_combine_cols(O, p.L, p.mfma ? inv_pos : nullptr, w, p.T, p.k, (const uint16_t*)norm, cf, cn,
                                      at<float>(ws, p.psq), s));
+  else if (p.mfma)
+    MOE_HIP(moe::launch_combine_norm_bf16((const uint16_t*)O, p.L, inv_pos, w, p.T, p.k, (const uint16_t*)norm,
+                                          d->rms_eps, taps ? taps->c : nullptr, cn, s));
   else
-    MOE_HIP(moe::launch_combine_norm(O, p.L, p.mfma ? inv_pos : nullptr, w, p.T, p.k, (const uint16_t*)norm,
-                                     d->rms_eps, taps ? taps->c : nullptr, cn, s));
+    MOE_HIP(moe::launch_combine_norm(O, p.L, nullptr, w, p.T, p.k, (const uint16_t*)norm, d->rms_eps,
+                                     taps ? taps->c : nullptr, cn, s));
   STAGE_MARK(7);
   // a9: up-projection, plus the shared output, rounded to bf16
   if (p.small) {
@@ -755,7 +761,9 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
       return r;
     }
     if (taps->O) {
-      if (p.mfma)
+      if (p.mfma && !p.small)
+        MOE_HIP(moe::launch_gather_rows_bf16((const uint16_t*)O, p.L, inv_pos, p.pairs, taps->O, s));
+      else if (p.mfma)
         MOE_HIP(moe::launch_gather_rows_f32(O, p.L, inv_pos, p.pairs, taps->O, s));
       else if ((r = copy_tap(taps->O, O, (size_t)p.pairs * p.L * 4, s)))
         return r;

@@ -210,6 +210,7 @@ struct MfmaProblem {
   uint8_t* outqs;
   float* outf;                // plain: fp32 [row, ldo] (routed: slot position, or with out_flat the
                               // flat slot index t * topk + j)
+  uint16_t* outh;             // plain, instead of outf when set: the same rows rounded to bf16
   int out_flat;
   GluAct act;                 // GLU: the activation
   int ldo;
@@ -225,6 +226,9 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s);
 // c_t = sum_j w[t][j] * O[row of slot t * k + j] in slot order: O fp32 by flat slot index
 // (inv_pos null) or by layout position (row = inv_pos[t * k + j])
 hipError_t launch_combine_norm(const float* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
+                               const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
+// the same with O in bf16 (the MFMA path's down output above 64 rows)
+hipError_t launch_combine_norm_bf16(const uint16_t* O, int L, const int32_t* inv_pos, const float* w, int T, int k,
                                const uint16_t* norm, float eps, float* c_tap, uint16_t* c_norm, hipStream_t s);
 
 // Decode batches: c [T, L] fp32 (required) and cg = bf16(c * g) (bf16(c) without a norm
@@ -258,6 +262,7 @@ hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, hi
 
 // out[i] = src[idx[i]] for rows of `cols` floats (cols % 4 == 0), i < n
 hipError_t launch_gather_rows_f32(const float* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s);
+hipError_t launch_gather_rows_bf16(const uint16_t* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s);
 
 // fill with a constant (a kernel, so that captured graphs hold no memset node)
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);

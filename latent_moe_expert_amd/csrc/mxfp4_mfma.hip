@@ -486,9 +486,16 @@ __device__ __forceinline__ void mx_job(const MfmaProblem& a, int first, int nval
       const int j = 16 * mf + nl;
       if (j < nvalid) {
         const int orow = a.routed && a.out_flat ? a.sorted_ids[first + j] : first + j;
-        float* o = a.outf + (size_t)orow * a.ldo + col0 + 4 * q;
+        const size_t ob = (size_t)orow * a.ldo + col0 + 4 * q;
+        if (a.outh) {  // bf16 rows: 8 bytes per lane and tile
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) *(f32x4_t*)(o + 16 * nf) = acc[mf][nf];
+          for (int nf = 0; nf < 2; ++nf)
+            *(uint2*)(a.outh + ob + 16 * nf) =
+                uint2{pack_bf16x2(acc[mf][nf][0], acc[mf][nf][1]), pack_bf16x2(acc[mf][nf][2], acc[mf][nf][3])};
+        } else {
+#pragma unroll
+          for (int nf = 0; nf < 2; ++nf) *(f32x4_t*)(a.outf + ob + 16 * nf) = acc[mf][nf];
+        }
       }
     }
   } else {
@@ -638,6 +645,8 @@ hipError_t launch_mx_mfma(const MfmaArgs& a, hipStream_t s) {
   for (int i = 0; i < a.nprob; ++i) {
     const MfmaProblem& p = a.p[i];
     if ((p.W2 != nullptr) != glu || p.K % 512 || p.K <= 0) return hipErrorInvalidValue;
+    // plain problems write fp32 or bf16 rows (bf16: 8-byte stores, so ldo % 4 == 0)
+    if (!glu && (!p.outf == !p.outh || (p.outh && p.ldo % 4))) return hipErrorInvalidValue;
     // GLU blocks cover 128 h columns and write whole FP6 windows of h; plain blocks cover 256 columns
     if (glu ? (p.N % 512) : (p.N % 256)) return hipErrorInvalidValue;
     // 32-bit byte offsets: activations, weights of one matrix, outputs
