@@ -95,6 +95,78 @@ __device__ __forceinline__ GemmSeg pick_seg(const GemmArgs& a, bool second) {
   return r;
 }
 
+// Epilogue of both tiles, the weights having been the MFMA's A operand: acc[i][j][r] is
+// D[row0 + 16 i][col0 + 16 j + r]. One loop per output form (a branch on the form inside the
+// tile loops made the 256 x 224 tile spill its accumulators), each storing a lane's four
+// columns as one 8- or 16-byte store (with one 16-byte addend load) when the row strides and N
+// allow it, else element by element.
+template <int MI, int NJ, typename F>
+__device__ __forceinline__ void gemm_tiles(const f32x4_t (&acc)[MI][NJ], int M, int N, int row0, int col0, F f) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = row0 + 16 * i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = col0 + 16 * j;
+      if (col < N) f(row, col, acc[i][j]);
+    }
+  }
+}
+
+template <int MI, int NJ>
+__device__ __forceinline__ void gemm_epilogue_rows(const f32x4_t (&acc)[MI][NJ], const GemmSeg& sg, int M, int row0,
+                                                   int col0, int slice) {
+  const int N = sg.N;
+  const bool add = sg.mode == kAddStoreBf16;
+  const bool vec = sg.ldo % 4 == 0 && N % 4 == 0 && (!add || !sg.addend || sg.ld_add % 4 == 0) &&
+                   (!add || !sg.tap || sg.ld_tap % 4 == 0);
+  uint16_t* outh = (uint16_t*)sg.out;
+  if (add) {
+    const float* ad = sg.addend;
+    float* tap = sg.tap;
+    if (vec)
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+        const f32x4_t a = ad ? *(const f32x4_t*)(ad + (size_t)row * sg.ld_add + col) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const f32x4_t y = v + a;
+        *(uint2*)(outh + (size_t)row * sg.ldo + col) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        if (tap) *(f32x4_t*)(tap + (size_t)row * sg.ld_tap + col) = v;
+      });
+    else
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (col + e >= N) continue;
+          const float a = ad ? ad[(size_t)row * sg.ld_add + col + e] : 0.f;
+          outh[(size_t)row * sg.ldo + col + e] = (uint16_t)f32_to_bf16_bits(v[e] + a);
+          if (tap) tap[(size_t)row * sg.ld_tap + col + e] = v[e];
+        }
+      });
+  } else if (sg.mode == kStoreF32 || sg.mode == kPartF32) {
+    float* outf = (float*)sg.out + (sg.mode == kPartF32 ? (size_t)slice * M * sg.ldo : 0);
+    if (vec)
+      gemm_tiles(acc, M, N, row0, col0,
+                 [&](int row, int col, const f32x4_t& v) { *(f32x4_t*)(outf + (size_t)row * sg.ldo + col) = v; });
+    else
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < N) outf[(size_t)row * sg.ldo + col + e] = v[e];
+      });
+  } else {
+    if (vec)
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+        *(uint2*)(outh + (size_t)row * sg.ldo + col) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      });
+    else
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < N) outh[(size_t)row * sg.ldo + col + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+      });
+  }
+}
+
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[2 * kTile];
   __shared__ __attribute__((aligned(16))) uint8_t st1[2 * kTile];
@@ -211,8 +283,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[i][j] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+              acc[i][j] =  // weights as the MFMA's A operand: acc[i][j] holds the tile transposed
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[j]), as_bf16x8(av[i]), acc[i][j], 0, 0, 0);
         }
       } else {
         // A: row 64 wm + 16 mi + nl of 64-byte rows, chunk q (K 8q .. 8q + 7); W: the same K of
@@ -237,9 +309,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
           const u32x4_t lo = {l4[0], l4[1], l4[2], l4[3]};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(hi), acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(mi), acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(lo), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(hi), as_bf16x8(av[i]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(mi), as_bf16x8(av[i]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lo), as_bf16x8(av[i]), acc[i][j], 0, 0, 0);
           }
         }
       }
@@ -274,61 +346,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
   else
     core(std::false_type{});
 
-  // epilogue: lane holds D[m = 4q + r][n = nl] of each 16 x 16 tile. Rows past M and
-  // columns past N are skipped; all addend loads are issued before any store.
-  int rows[4][4];
-  bool colok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rows[i][r] = m0 + wm * 64 + 16 * i + 4 * q + r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) colok[j] = n0 + wn * 64 + 16 * j + nl < sg.N;
-  const int colb = n0 + wn * 64 + nl;
-  if (sg.mode == kAddStoreBf16) {
-    float add[4][4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          add[i][r][j] = (sg.addend && rows[i][r] < args.M && colok[j])
-                             ? sg.addend[(size_t)rows[i][r] * sg.ld_add + colb + 16 * j]
-                             : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (rows[i][r] >= args.M) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!colok[j]) continue;
-          const float v = acc[i][j][r];
-          ((uint16_t*)sg.out)[(size_t)rows[i][r] * sg.ldo + colb + 16 * j] =
-              (uint16_t)f32_to_bf16_bits(v + add[i][r][j]);
-          if (sg.tap) sg.tap[(size_t)rows[i][r] * sg.ld_tap + colb + 16 * j] = v;
-        }
-      }
-  } else {
-    const bool f32 = sg.mode == kStoreF32 || sg.mode == kPartF32;
-    float* outf = (float*)sg.out + (sg.mode == kPartF32 ? (size_t)slice * args.M * sg.ldo : 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (rows[i][r] >= args.M) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!colok[j]) continue;
-          const size_t o = (size_t)rows[i][r] * sg.ldo + colb + 16 * j;
-          if (f32)
-            outf[o] = acc[i][j][r];
-          else
-            ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
-        }
-      }
-  }
+  // epilogue: lane (nl, q) holds D[m = 16 i + nl][n = 16 j + 4 q + r], r = 0..3, of tile (i, j)
+  gemm_epilogue_rows<4, 4>(acc, sg, args.M, m0 + wm * 64 + nl, n0 + wn * 64 + 4 * q, slice);
 }
 
 // ---- Large batches: 256 x 224 outputs per block, 8 waves (2 per SIMD) in 4 x 2, each
@@ -446,8 +465,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
     for (int i = 0; i < kMI; ++i) {
       const u32x4_t av = *(const u32x4_t*)(st + ard + i * 16 * 64);
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[j]), acc[i][j], 0, 0, 0);
+      for (int j = 0; j < kNJ; ++j)  // weights as the MFMA's A operand: acc[i][j] holds the tile transposed
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(bv[j]), as_bf16x8(av), acc[i][j], 0, 0, 0);
     }
   };
 
@@ -478,46 +497,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(GemmArgs args) {
   // block ends and its LDS goes to another block
   MOE_GEMM_WAIT_VM_LGKM0(0);
 
-  // epilogue: lane holds D[m = 4q + r][n = nl] of each 16 x 16 tile; rows past M and
-  // columns past N are skipped
-  bool colok[kNJ];
-#pragma unroll
-  for (int j = 0; j < kNJ; ++j) colok[j] = n0 + wn * 112 + 16 * j + nl < sg.N;
-  const int colb = n0 + wn * 112 + nl;
-  const bool f32 = sg.mode == kStoreF32 || sg.mode == kPartF32;
-  float* outf = (float*)sg.out + (sg.mode == kPartF32 ? (size_t)slice * args.M * sg.ldo : 0);
-#pragma unroll
-  for (int i = 0; i < kMI; ++i) {
-    float add[4][kNJ];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 64 + 16 * i + 4 * q + r;
-#pragma unroll
-      for (int j = 0; j < kNJ; ++j)
-        add[r][j] = (sg.mode == kAddStoreBf16 && sg.addend && row < args.M && colok[j])
-                        ? sg.addend[(size_t)row * sg.ld_add + colb + 16 * j]
-                        : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm * 64 + 16 * i + 4 * q + r;
-      if (row >= args.M) continue;
-#pragma unroll
-      for (int j = 0; j < kNJ; ++j) {
-        if (!colok[j]) continue;
-        const float v = acc[i][j][r];
-        const size_t o = (size_t)row * sg.ldo + colb + 16 * j;
-        if (sg.mode == kAddStoreBf16) {
-          ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(v + add[r][j]);
-          if (sg.tap) sg.tap[(size_t)row * sg.ld_tap + colb + 16 * j] = v;
-        } else if (f32) {
-          outf[o] = v;
-        } else {
-          ((uint16_t*)sg.out)[o] = (uint16_t)f32_to_bf16_bits(v);
-        }
-      }
-    }
-  }
+  // epilogue: lane (nl, q) holds D[m = 16 i + nl][n = 16 j + 4 q + r], r = 0..3, of tile (i, j):
+  // four consecutive columns of one row, stored (and the addend loaded) 8 or 16 bytes at a time
+  // when the row strides allow it. Rows past M and columns past N are skipped.
+  gemm_epilogue_rows<kMI, kNJ>(acc, sg, args.M, m0 + wm * 64 + nl, n0 + wn * 112 + 4 * q, slice);
 }
 
 // fp32 [N, K] -> bf16 [N, 3K]: row n = hi(k) | mid(k) | lo(k), w = hi + mid + lo exactly.
