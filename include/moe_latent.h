@@ -144,7 +144,9 @@ typedef struct moe_latent_taps {
                                            up-projection reads bf16(g * c) and its output
                                            is scaled by 1 / rms(c), the same function) */
   float* y_routed;        /* fp32 [T, H]  up-projection output */
-  float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none) */
+  float* y_shared;        /* fp32 [T, H]  shared experts' output (zeros if none); on the MFMA path
+                             above 64 tokens whose up-projection is not split over K, the layer
+                             keeps it in bf16 and the tap holds those values widened to fp32 */
   float* O;               /* fp32 [T*k, L] the routed expert's output of slot t*k+j (token t's
                              j-th selected expert), before the routing weight; on the MFMA path
                              above 64 tokens the layer keeps O in bf16, and the tap holds those

@@ -387,6 +387,9 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
   uint16_t* cn = at<uint16_t>(ws, p.cn);
   uint16_t* hs = at<uint16_t>(ws, p.hs);
   float* ys = at<float>(ws, p.ys);
+  // the shared experts' output in bf16 where its one consumer is the up-projection's 256 x 224
+  // tile (MFMA path, no K split of the up-projection): half the bytes written and read again
+  const bool ys16 = shared && p.mfma && !p.small && p.su == 1;
 
   // Stage events: the record is claimed here and marked complete after the last stage
   // event; a forward that fails on the way leaves an incomplete record, which
@@ -558,7 +561,7 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
         dn.S = shared->scales + 2 * sgs;
         dn.N = p.H;
         dn.K = p.Is;
-        dn.outf = ys;
+        if (ys16) dn.outh = (uint16_t*)ys; else dn.outf = ys;
         dn.ldo = p.H;
       }
       moe::MfmaProblem& g = m.p[n++];
@@ -732,8 +735,9 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     a.lda = p.L;
     a.M = p.T;
     a.nseg = 1;
-    a.seg[0] = {(const uint16_t*)up, p.H, p.L, p.L, moe::kAddStoreBf16, y, p.H, shared ? ys : nullptr, p.H,
+    a.seg[0] = {(const uint16_t*)up, p.H, p.L, p.L, moe::kAddStoreBf16, y, p.H, shared && !ys16 ? ys : nullptr, p.H,
                 taps ? taps->y_routed : nullptr, p.H};
+    if (shared && ys16) a.seg[0].addend16 = (const uint16_t*)ys;
     MOE_HIP(moe::launch_gemm_bf16(a, s));
   }
   STAGE_MARK(8);
@@ -770,7 +774,10 @@ int forward_impl(const moe_latent_dims* d, const void* x, const void* down, cons
     }
     if (taps->y_shared) {
       if (shared) {
-        if ((r = copy_tap(taps->y_shared, ys, (size_t)p.T * p.H * 4, s))) return r;
+        if (ys16)
+          MOE_HIP(moe::launch_widen_bf16((const uint16_t*)ys, (size_t)p.T * p.H, taps->y_shared, s));
+        else if ((r = copy_tap(taps->y_shared, ys, (size_t)p.T * p.H * 4, s)))
+          return r;
       } else {
         MOE_HIP(moe::launch_fill_f32(taps->y_shared, (size_t)p.T * p.H, 0.f, s));
       }

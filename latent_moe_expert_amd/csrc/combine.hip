@@ -307,6 +307,16 @@ __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const uint16_t* _
   }
 }
 
+// bf16 -> fp32, four values per thread (the shared experts' output tap when it is held in bf16)
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src, size_t n4,
+                                                         float* __restrict__ out) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const uint2 b = *(const uint2*)(src + 4 * i);
+    *(f32x4_t*)(out + 4 * i) = f32x4_t{bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
+                                       bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16)};
+  }
+}
+
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -323,6 +333,14 @@ hipError_t launch_rmsnorm(const uint16_t* x, int rows, int cols, const uint16_t*
 hipError_t launch_gather_rows_f32(const float* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, s, src, cols, idx, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen_bf16(const uint16_t* src, size_t n, float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  const size_t blocks = (n / 4 + 255) / 256;
+  hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, src, n / 4, out);
   return hipGetLastError();
 }
 

@@ -75,10 +75,11 @@ __host__ __device__ constexpr int g_pos2(int c, int r) { return c ^ ((r >> 2) & 
 
 // One of the two segments as a value, chosen field by field (a select between references to
 // the kernel argument makes the compiler copy the arguments to scratch and index them there).
+// Every field of GemmSeg is copied; r starts zeroed so that a field left out reads as zero.
 __device__ __forceinline__ GemmSeg pick_seg(const GemmArgs& a, bool second) {
   const GemmSeg& x = a.seg[0];
   const GemmSeg& y = a.seg[1];
-  GemmSeg r;
+  GemmSeg r{};
   r.W = second ? y.W : x.W;
   r.N = second ? y.N : x.N;
   r.K = second ? y.K : x.K;
@@ -92,6 +93,7 @@ __device__ __forceinline__ GemmSeg pick_seg(const GemmArgs& a, bool second) {
   r.ld_tap = second ? y.ld_tap : x.ld_tap;
   r.splits = second ? y.splits : x.splits;
   r.w_f32 = second ? y.w_f32 : x.w_f32;
+  r.addend16 = second ? y.addend16 : x.addend16;
   return r;
 }
 
@@ -119,10 +121,31 @@ __device__ __forceinline__ void gemm_epilogue_rows(const f32x4_t (&acc)[MI][NJ],
                                                    int col0, int slice) {
   const int N = sg.N;
   const bool add = sg.mode == kAddStoreBf16;
-  const bool vec = sg.ldo % 4 == 0 && N % 4 == 0 && (!add || !sg.addend || sg.ld_add % 4 == 0) &&
+  const bool vec = sg.ldo % 4 == 0 && N % 4 == 0 && (!add || !(sg.addend || sg.addend16) || sg.ld_add % 4 == 0) &&
                    (!add || !sg.tap || sg.ld_tap % 4 == 0);
   uint16_t* outh = (uint16_t*)sg.out;
-  if (add) {
+  if (add && sg.addend16) {  // bf16 addend
+    const uint16_t* ad = sg.addend16;
+    float* tap = sg.tap;
+    if (vec)
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+        const uint2 b = *(const uint2*)(ad + (size_t)row * sg.ld_add + col);
+        const f32x4_t y = v + f32x4_t{bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
+                                      bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16)};
+        *(uint2*)(outh + (size_t)row * sg.ldo + col) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        if (tap) *(f32x4_t*)(tap + (size_t)row * sg.ld_tap + col) = v;
+      });
+    else
+      gemm_tiles(acc, M, N, row0, col0, [&](int row, int col, const f32x4_t& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (col + e >= N) continue;
+          const float a = bf16_bits_to_f32(ad[(size_t)row * sg.ld_add + col + e]);
+          outh[(size_t)row * sg.ldo + col + e] = (uint16_t)f32_to_bf16_bits(v[e] + a);
+          if (tap) tap[(size_t)row * sg.ld_tap + col + e] = v[e];
+        }
+      });
+  } else if (add) {
     const float* ad = sg.addend;
     float* tap = sg.tap;
     if (vec)

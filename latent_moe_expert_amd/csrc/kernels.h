@@ -54,6 +54,7 @@ struct GemmSeg {
   int ld_tap;
   int splits;           // kPartF32: K slices (M below the 256 x 224 tile's threshold); else 0 or 1
   int w_f32;            // 1: W is fp32 [N, K], split into three bf16 planes as it is staged (M < 2048)
+  const uint16_t* addend16;  // kAddStoreBf16: a bf16 addend [m][n] (stride ld_add) instead of addend
 };
 struct GemmArgs {
   const uint16_t* A;
@@ -263,6 +264,7 @@ hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* checksum, hi
 // out[i] = src[idx[i]] for rows of `cols` floats (cols % 4 == 0), i < n
 hipError_t launch_gather_rows_f32(const float* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s);
 hipError_t launch_gather_rows_bf16(const uint16_t* src, int cols, const int32_t* idx, int n, float* out, hipStream_t s);
+hipError_t launch_widen_bf16(const uint16_t* src, size_t n, float* out, hipStream_t s);  // n % 4 == 0
 
 // fill with a constant (a kernel, so that captured graphs hold no memset node)
 hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t s);
