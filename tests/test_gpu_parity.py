@@ -157,13 +157,15 @@ def test_align_block_multiple_of_16(B):
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
 
 
-def test_dense_projections_256_tiles_all_rows():
+@pytest.mark.parametrize("n_experts", [40, 37])
+def test_dense_projections_256_tiles_all_rows(n_experts):
     """T = 2100 tokens take the 256 x 224 dense-projection tiles (M >= 2048): a ragged last
-    M tile (52 rows), partial N tiles (z: 768 = 3 x 224 + 96 columns; the router's 40 of 224
-    rows, K = 3 x hidden; the up-projection's 1024 = 4 x 224 + 128 with the shared addend);
-    every token compared."""
+    M tile (52 rows), partial N tiles (z: 768 = 3 x 224 + 96 columns; the router's 40 or 37 of
+    224 rows, K = 3 x hidden; the up-projection's 1024 = 4 x 224 + 128 with the shared addend);
+    every token compared. With 37 experts the router's output rows are 37 floats apart, so its
+    tiles take the element-by-element epilogue instead of the 16-byte stores."""
     H = _harness()
-    c = li.small_config(T=2100, hidden=1024, latent=768, n_experts=40, topk=3, inter=256, shared_inter=256)
+    c = li.small_config(T=2100, hidden=1024, latent=768, n_experts=n_experts, topk=3, inter=256, shared_inter=256)
     out, ref, _ = _run_small(c)
     H.compare_layer(out, ref, c.T, c.topk, c.n_experts)
 
