@@ -89,6 +89,8 @@ MFMA_SMALL = [
     # 12-tile kernels each run jobs with fewer valid tiles than they cover
     ("jobs_of_1_to_12_tiles_zipf", dict(T=224, hidden=512, latent=512, n_experts=20, topk=4, inter=512,
                                         shared_inter=512, zipf_s=1.1, zipf_c=0.5)),
+    # a latent above 4096: the bf16-O combine's threads take four 8-column vectors of the row
+    ("latent_4608", dict(T=96, hidden=512, latent=4608, n_experts=8, topk=4, inter=512, shared_inter=512)),
 ]
 
 
