@@ -91,6 +91,10 @@ MFMA_SMALL = [
                                         shared_inter=512, zipf_s=1.1, zipf_c=0.5)),
     # a latent above 4096: the bf16-O combine's threads take four 8-column vectors of the row
     ("latent_4608", dict(T=96, hidden=512, latent=4608, n_experts=8, topk=4, inter=512, shared_inter=512)),
+    # 128 x 128 dense tiles with more tiles than compute units (9 x 32 for the up-projection), so
+    # the up-projection is not split over K and adds the shared output in bf16
+    ("mid_rows_unsplit_up_projection", dict(T=1100, hidden=4096, latent=512, n_experts=16, topk=4, inter=512,
+                                            shared_inter=512)),
 ]
 
 
